@@ -1,0 +1,232 @@
+/*
+ * zi.h -- memory-centric tiling of a large linear operator on one AMD MI355X.
+ *
+ * The method (ZeRO-Infinity transformer-math page, section "Memory-centric
+ * tiling: operators bigger than the device"; pwwt.cn ZeRO-Infinity article,
+ * section "关键技术一：Memory-centric tiling for working memory"): a linear
+ * operator Y = X W whose weight W[K x M] does not fit the device is split
+ * along its output dimension into N tiles W_1..W_N of n = M/N columns.  The
+ * tiles stay in pinned host memory and are brought into device memory one at
+ * a time; each produces its slice Y_i = X W_i of the output with no
+ * communication between tiles, and its buffer is released before the next
+ * tile needs it.  Here the tiles flow through a d-slot ring of device buffers
+ * fed by host-to-device copies on a dedicated copy stream, so that the copy of
+ * tile i+d overlaps the products of tile i (the prefetch of the same page's
+ * section "Prefetch depth: how far ahead the pipeline must run").  The
+ * backward pass stages every tile again (the FLOPs-per-byte section counts the
+ * parameters climbing twice per step), forms dX += dY_i W_i^T and
+ * dW_i = X^T dY_i, and writes each dW_i back to pinned host memory on a second
+ * copy stream.
+ *
+ * Data layout (all row-major, element = 16-bit input format unless stated):
+ *   X   [T x K]   device, activations                       (caller owned)
+ *   W^t [M x K]   pinned host, "out-major": row m of W^t is column m of W,
+ *                 so tile i is the contiguous rows [i*n, (i+1)*n) of W^t,
+ *                 at byte offset i*K*n*2                     (caller owned)
+ *   Y   [T x M]   device, output of the forward             (caller owned)
+ *   dY  [T x M]   device, upstream gradient                 (caller owned)
+ *   dX  [T x K]   device, fp32, accumulated over the tiles  (caller owned)
+ *   dW^t[M x K]   pinned host, same layout as W^t           (caller owned)
+ *
+ * Conventions shared by every call:
+ *   - Every call returns a zi_status and never throws.  On an error nothing
+ *     has been enqueued; zi_last_error() returns a text for the calling
+ *     thread's most recent error.
+ *   - Forward/backward calls only enqueue work on the context's streams and
+ *     return at once.  Inputs must stay valid, and outputs (device or host)
+ *     must not be read, until zi_sync() on that context returns ZI_OK.
+ *   - An asynchronous HIP failure makes the context's error sticky
+ *     (ZI_ERR_HIP): zi_sync() and every later call on it return it.
+ *   - Streams are hipStream_t values passed as void*; they must be streams of
+ *     the current device with default priority.  The library creates only
+ *     hipEvents; it never allocates device memory inside a call, so the ring
+ *     lives in the caller's workspace and the device budget holds by
+ *     construction.
+ *   - One host thread at a time per context.
+ */
+#ifndef ZI_H
+#define ZI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ZI_OK = 0,
+    ZI_ERR_ARG = 1,        /* NULL where a pointer is required, bad enum, bad size */
+    ZI_ERR_SHAPE = 2,      /* N does not divide M, K or n not a multiple of 8, ... */
+    ZI_ERR_BUDGET = 3,     /* ring does not fit the device budget or the workspace */
+    ZI_ERR_NOT_PINNED = 4, /* host weight or gradient buffer is not page-locked */
+    ZI_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned */
+    ZI_ERR_HIP = 6,        /* a HIP runtime call failed (sticky on the context) */
+    ZI_ERR_STATE = 7       /* plan and context disagree, or the context is unusable */
+} zi_status;
+
+typedef enum { ZI_F16 = 1, ZI_BF16 = 2 } zi_dtype;
+
+/* zi_problem.flags */
+#define ZI_FLAG_F32_OUT 0x1u /* Y and dW^t are written in fp32 instead of the input
+                                format (same kernels, fp32 epilogue): the form in
+                                which rounding-free results can be compared.  The
+                                caller sizes Y and dW_host for 4-byte elements. */
+
+/* The problem, as the pages state it: X, W, the number of tiles, the prefetch
+ * depth and the device memory the tiles may occupy. */
+typedef struct {
+    int64_t T;            /* tokens: rows of X, Y, dY, dX                      (>= 1) */
+    int64_t K;            /* in_features: columns of X; multiple of 8          (>= 8) */
+    int64_t M;            /* out_features: columns of Y; N must divide it       (>= 8) */
+    int32_t N;            /* number of weight tiles along M; n = M/N multiple of 8 */
+    int32_t d;            /* ring depth: device slots for weight tiles          (>= 1) */
+    int32_t dtype;        /* zi_dtype of X, W, dY, Y and dW */
+    uint32_t flags;       /* ZI_FLAG_* */
+    uint64_t device_budget_bytes; /* device bytes the tile buffers may use; 0 = no cap */
+    const void *W_host;   /* pinned W^t [M x K]; may be NULL for a planning-only call */
+    void *dW_host;        /* pinned dW^t [M x K]; NULL if no backward will be run */
+} zi_problem;
+
+/* What a plan decided and what one pass costs (closed forms of the method). */
+typedef struct {
+    int64_t n;                 /* tile width M / N */
+    uint64_t tile_bytes;       /* K * n * 2: one weight tile, one host-to-device copy */
+    uint64_t dw_tile_bytes;    /* K * n * 2 (or * 4 with ZI_FLAG_F32_OUT) */
+    int32_t d;                 /* weight-tile slots in the ring */
+    int32_t dw_slots;          /* separate gradient slots; 0 = dW_i written into W_i's slot */
+    uint64_t ring_bytes;       /* device bytes the ring uses = workspace the context needs */
+    double flops_fwd;          /* 2 T K M */
+    double flops_bwd;          /* 4 T K M */
+    double h2d_bytes_pass;     /* K * M * 2: every tile staged once per pass */
+    double d2h_bytes_bwd;      /* dW write-back bytes of one backward */
+    double ait_fwd;            /* flops_fwd / h2d bytes  (= T)  */
+    double ait_bwd;            /* flops_bwd / h2d bytes  (= 2T) */
+    double working_bytes_one;  /* layer bytes / N: one tile resident */
+    double working_bytes_two;  /* twice that: one tile computing, one in flight */
+} zi_plan_info;
+
+typedef struct zi_plan zi_plan; /* library-owned, immutable after creation */
+typedef struct zi_ctx zi_ctx;   /* library-owned: ring over caller workspace, events */
+
+/* Plan the tiling of one linear operator.
+ * Validates the shapes (N | M, K % 8 == 0, n % 8 == 0, T >= 1), the dtype,
+ * and the budget: the forward needs d weight slots; the backward additionally
+ * needs somewhere to form dW_i -- up to two separate gradient slots if the
+ * budget allows, otherwise dW_i is formed in W_i's own slot after the dX
+ * product has consumed it.  ZI_ERR_BUDGET if even d weight slots do not fit.
+ * W_host/dW_host are not dereferenced here (checked when a pass is enqueued).
+ * out may be NULL (planning only); info may be NULL. */
+zi_status zi_plan_tiles(const zi_problem *problem, zi_plan **out, zi_plan_info *info);
+zi_status zi_plan_destroy(zi_plan *plan);
+
+/* Smallest integer depth d >= t_fetch / t_layer, at least 1 (transformer-math
+ * page, section "Prefetch depth": d >= t_fetch / t_layer, buffers d * layer). */
+int32_t zi_prefetch_depth(double t_fetch_s, double t_layer_s);
+
+/* Predicted timing of one pass from the ring's event recurrence: tile i's copy
+ * starts when the link is free and its slot has been released by tile i-d;
+ * its products start when the compute stream is free and the copy has landed
+ * (pwwt.cn article, section "关键技术三：Overlap-Centric Design": the pipeline
+ * runs at the pace of its slowest stage).  backward: 0 = forward pass,
+ * 1 = backward pass, 2 = backward with the forward product recomputed per
+ * tile.  Rates: flop_rate in FLOP/s (products), link rates in bytes/s. */
+typedef struct {
+    double t_pass_s;        /* first copy issued -> last product (and write-back) done */
+    double t_compute_s;     /* sum of product times */
+    double t_link_s;        /* sum of host-to-device copy times */
+    double stall_frac;      /* 1 - t_compute / t_pass: compute-stream idle share */
+    int32_t d_pages;        /* ceil(t_fetch(tile) / t_compute(tile)) */
+} zi_prediction;
+zi_status zi_plan_predict(const zi_plan *plan, int32_t backward, double flop_rate,
+                          double h2d_bytes_per_s, double d2h_bytes_per_s, zi_prediction *out);
+
+/* A context: the tile ring over caller-owned device workspace and three
+ * caller-owned streams (products, host-to-device, device-to-host).  The ring
+ * geometry (slot sizes, d, gradient slots) is taken from `plan`; any plan with
+ * the same d whose tiles fit the slots may then run on this context, and
+ * consecutive calls share the ring, so the copies of the next call's first
+ * tiles overlap the previous call's last products.
+ * workspace_dev: 256-byte aligned device memory of at least info.ring_bytes.
+ * The context keeps no reference to the plan. */
+zi_status zi_ctx_create(const zi_plan *plan, void *workspace_dev, uint64_t workspace_bytes,
+                        void *compute_stream, void *h2d_stream, void *d2h_stream,
+                        zi_ctx **out);
+/* Waits for outstanding work, then frees the context's events. */
+zi_status zi_ctx_destroy(zi_ctx *ctx);
+
+/* Forward: Y[:, i*n:(i+1)*n] = RNE(X W_i) for i = 0..N-1, tiles in ascending
+ * order, fp32 accumulation, one rounding into the input format (or fp32 with
+ * ZI_FLAG_F32_OUT).  X [T x K] and Y [T x M] (ldc = M) are device pointers,
+ * 16-byte aligned. */
+zi_status zi_tiled_linear_fwd(zi_ctx *ctx, const zi_plan *plan, const void *X_dev, void *Y_dev);
+
+/* Forward with the GeLU of the feed-forward block fused into the epilogue
+ * (the 1T model's FFN, transformer-math page, section "Memory-centric
+ * tiling"): A = RNE(X W) and H = RNE(GeLU(A)), GeLU in the exact erf form
+ * evaluated in fp32 on the stored (rounded) A.  A and H are [T x M] device
+ * buffers in the input format.  Not available with ZI_FLAG_F32_OUT. */
+zi_status zi_tiled_linear_fwd_gelu(zi_ctx *ctx, const zi_plan *plan, const void *X_dev,
+                                   void *A_dev, void *H_dev);
+
+/* Backward: for each tile i in ascending order,
+ *   dX (+)= dY[:, i*n:(i+1)*n] W_i^T   (fp32; the first tile overwrites dX),
+ *   dW_i  = X^T dY[:, i*n:(i+1)*n]     (fp32 accumulation, one rounding into the
+ *                                        input format, or fp32 with ZI_FLAG_F32_OUT),
+ * and dW_i is copied to dW_host rows [i*n, (i+1)*n) on the write-back stream.
+ * dX_dev: fp32 [T x K].  Requires a plan with dW_host.  dW_host must not be
+ * read before zi_sync(). */
+zi_status zi_tiled_linear_bwd(zi_ctx *ctx, const zi_plan *plan, const void *X_dev,
+                              const void *dY_dev, float *dX_dev);
+
+/* Backward with the forward product recomputed from the same staged tile
+ * (activation checkpointing: forward, recomputed forward and backward,
+ * transformer-math page, section "The FLOPs-per-byte test every tier must
+ * pass"): per tile, Yr[:, i*n:(i+1)*n] = RNE(X W_i) first, then the two
+ * backward products as in zi_tiled_linear_bwd.  Yr_dev: [T x M] device. */
+zi_status zi_tiled_linear_bwd_recompute(zi_ctx *ctx, const zi_plan *plan, const void *X_dev,
+                                        const void *dY_dev, float *dX_dev, void *Yr_dev);
+
+/* dA = RNE(dH * GeLU'(A)) elementwise on the compute stream, GeLU'(a) =
+ * Phi(a) + a phi(a) evaluated in fp32 on the stored A.  dH: fp32 device,
+ * A and dA: device, input format `dtype`; `count` elements each. */
+zi_status zi_gelu_bwd(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const void *A_dev,
+                      void *dA_dev, int64_t count);
+
+/* Wait for everything enqueued on the context's three streams; return the
+ * first error (sticky). */
+zi_status zi_sync(zi_ctx *ctx);
+
+/* Per-context timing (off by default).  When on, every kernel launch and
+ * every copy is bracketed by timing events; zi_ctx_stats() (after zi_sync)
+ * reports the totals since the last reset. */
+typedef struct {
+    int32_t kind_count;          /* number of valid entries below */
+    char kind_name[8][24];       /* "gemm_fwd", "gemm_fwd_gelu", "gemm_dx", "gemm_dw", ... */
+    int64_t launches[8];
+    double kernel_ms[8];         /* sum of event-measured durations */
+    double flops[8];             /* algorithmic FLOPs of those launches */
+    int64_t h2d_copies, d2h_copies;
+    double h2d_ms, d2h_ms;       /* sums of event-measured copy durations */
+    double h2d_bytes, d2h_bytes;
+    double span_ms;              /* first timed event -> last timed event */
+    double compute_busy_ms;      /* sum of all kernel durations */
+} zi_stats;
+zi_status zi_ctx_set_timing(zi_ctx *ctx, int32_t enable);
+zi_status zi_ctx_reset_stats(zi_ctx *ctx);
+zi_status zi_ctx_stats(zi_ctx *ctx, zi_stats *out);
+
+/* Page-locked host memory (hipHostMalloc) for W^t / dW^t; 4096-byte aligned. */
+zi_status zi_host_alloc(uint64_t bytes, void **out);
+zi_status zi_host_free(void *ptr);
+
+/* Text of the calling thread's most recent error ("" if none). */
+const char *zi_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t zi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZI_H */

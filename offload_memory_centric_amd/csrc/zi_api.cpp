@@ -1,0 +1,597 @@
+// zi_api.cpp -- the C ABI: contexts, the tile ring (stager), passes, timing.
+//
+// The stager follows the pages' description of memory-centric tiling (ZeRO-
+// Infinity transformer-math page, section "Memory-centric tiling: operators
+// bigger than the device"; pwwt.cn article, section "关键技术一：Memory-centric
+// tiling", worked example: load W_i, compute Y_i, release W_i and its
+// gradient, load W_{i+1}, ...) with the copy of later tiles overlapping the
+// products of the current one (pwwt.cn article, section "关键技术三：Overlap-
+// Centric Design": CPU-to-GPU copies run ahead of compute; in the backward
+// the gradient write-back to host overlaps the next tiles' products).
+//
+// Ring: d weight slots over the caller's workspace.  Global tile number g
+// (counted across calls on one context) uses slot g mod d.  Per slot:
+//   w_ready[s]  recorded on the copy-in stream after the tile landed,
+//   w_free[s]   recorded after the last reader of the slot (compute stream,
+//               or the write-back stream when dW_i is formed in the slot).
+// The copy of tile g waits on w_free of its slot, whose latest record is
+// tile g - d's release; the products of tile g wait on w_ready.  Because the
+// numbering continues across calls, the first copies of a call overlap the
+// last products of the previous call.  Gradient slots (dw_slots of them) work
+// the same way with dw_ready (compute) and dw_free (write-back stream).
+#include <hip/hip_runtime_api.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/zi.h"
+#include "zi_host.h"
+#include "zi_internal.h"
+
+namespace zi {
+
+static thread_local char g_err[512];
+
+zi_status fail(zi_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+enum Kind { K_FWD = 0, K_FWD_GELU, K_DX, K_DW, K_FWD_RECOMPUTE, K_GELU_BWD, K_COUNT };
+static const char *kKindNames[K_COUNT] = {"gemm_fwd", "gemm_fwd_gelu", "gemm_dx",
+                                          "gemm_dw",  "gemm_fwd_recompute", "gelu_bwd"};
+
+struct KernelRec {
+    int kind;
+    double flops;
+    hipEvent_t a, b;
+};
+struct CopyRec {
+    int d2h;
+    double bytes;
+    hipEvent_t a, b;
+};
+
+}  // namespace zi
+
+using namespace zi;
+
+struct zi_ctx {
+    int device = 0;
+    hipStream_t comp = nullptr, h2d = nullptr, d2h = nullptr;
+    char *ws = nullptr;
+    uint64_t ws_bytes = 0;
+    int d = 1, dw_slots = 0;
+    uint64_t slot_bytes = 0, dw_slot_bytes = 0;
+    std::vector<hipEvent_t> w_ready, w_free, dw_ready, dw_free;
+    std::vector<char> w_free_rec, dw_free_rec;
+    int64_t seq = 0, dw_seq = 0;
+    zi_status sticky = ZI_OK;
+    std::string sticky_msg;
+    bool timing = false;
+    std::vector<hipEvent_t> pool;
+    size_t pool_used = 0;
+    std::vector<KernelRec> krec;
+    std::vector<CopyRec> crec;
+
+    char *wslot(int s) const { return ws + (uint64_t)s * slot_bytes; }
+    char *dwslot(int s) const { return ws + (uint64_t)d * slot_bytes + (uint64_t)s * dw_slot_bytes; }
+};
+
+namespace {
+
+uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+zi_status hip_fail(zi_ctx *c, hipError_t e, const char *what) {
+    char buf[400];
+    snprintf(buf, sizeof(buf), "%s failed: %s (%d)", what, hipGetErrorString(e), (int)e);
+    if (c && c->sticky == ZI_OK) {
+        c->sticky = ZI_ERR_HIP;
+        c->sticky_msg = buf;
+    }
+    return fail(ZI_ERR_HIP, "%s", buf);
+}
+
+#define HIPCHK(c, call)                                     \
+    do {                                                    \
+        hipError_t e_ = (call);                             \
+        if (e_ != hipSuccess) return hip_fail((c), e_, #call); \
+    } while (0)
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool pinned_range(const void *p, uint64_t bytes) {
+    if (!p || !bytes) return false;
+    const char *q[2] = {static_cast<const char *>(p), static_cast<const char *>(p) + bytes - 1};
+    for (const char *x : q) {
+        hipPointerAttribute_t a;
+        hipError_t e = hipPointerGetAttributes(&a, x);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return false;
+        }
+        if (a.type != hipMemoryTypeHost) return false;
+    }
+    return true;
+}
+
+zi_status ev_timed(zi_ctx *c, hipEvent_t *out) {
+    if (c->pool_used == c->pool.size()) {
+        hipEvent_t e;
+        HIPCHK(c, hipEventCreate(&e));
+        c->pool.push_back(e);
+    }
+    *out = c->pool[c->pool_used++];
+    return ZI_OK;
+}
+
+zi_status check_ctx(zi_ctx *c) {
+    if (!c) return fail(ZI_ERR_ARG, "context is NULL");
+    if (c->sticky != ZI_OK) return fail(c->sticky, "context has a sticky error: %s", c->sticky_msg.c_str());
+    int dev = -1;
+    HIPCHK(nullptr, hipGetDevice(&dev));
+    if (dev != c->device)
+        return fail(ZI_ERR_STATE, "current device %d is not the context's device %d", dev, c->device);
+    return ZI_OK;
+}
+
+zi_status check_pass(zi_ctx *c, const zi_plan *p, bool backward) {
+    zi_status st = check_ctx(c);
+    if (st != ZI_OK) return st;
+    if (!p) return fail(ZI_ERR_ARG, "plan is NULL");
+    const zi_problem &pr = p->prob;
+    const zi_plan_info &in = p->info;
+    if (pr.d != c->d) return fail(ZI_ERR_STATE, "plan depth d=%d differs from the context's %d", pr.d, c->d);
+    if (in.tile_bytes > c->slot_bytes)
+        return fail(ZI_ERR_STATE, "plan tile of %llu B does not fit the context's %llu B slots",
+                    (unsigned long long)in.tile_bytes, (unsigned long long)c->slot_bytes);
+    const uint64_t wbytes = (uint64_t)pr.M * (uint64_t)pr.K * 2u;
+    if (!pr.W_host) return fail(ZI_ERR_ARG, "plan has no W_host");
+    if (!pinned_range(pr.W_host, wbytes))
+        return fail(ZI_ERR_NOT_PINNED, "W_host is not page-locked host memory over its %llu bytes",
+                    (unsigned long long)wbytes);
+    if (backward) {
+        if (!pr.dW_host) return fail(ZI_ERR_ARG, "a backward needs a plan with dW_host");
+        const uint64_t dwbytes = (uint64_t)pr.M * (uint64_t)pr.K * ((pr.flags & ZI_FLAG_F32_OUT) ? 4u : 2u);
+        if (!pinned_range(pr.dW_host, dwbytes))
+            return fail(ZI_ERR_NOT_PINNED, "dW_host is not page-locked host memory over its %llu bytes",
+                        (unsigned long long)dwbytes);
+        const uint64_t room = c->dw_slots > 0 ? c->dw_slot_bytes : c->slot_bytes;
+        if (in.dw_tile_bytes > room)
+            return fail(ZI_ERR_STATE, "gradient tile of %llu B does not fit the context's %llu B slot",
+                        (unsigned long long)in.dw_tile_bytes, (unsigned long long)room);
+    }
+    return ZI_OK;
+}
+
+zi_status check_dev_ptr(const void *p, const char *name) {
+    if (!p) return fail(ZI_ERR_ARG, "%s is NULL", name);
+    if (!aligned16(p)) return fail(ZI_ERR_ALIGN, "%s is not 16-byte aligned", name);
+    return ZI_OK;
+}
+
+// Copy global tile g (tile index `tile` of plan p) into its slot.
+zi_status stage(zi_ctx *c, const zi_plan *p, int64_t g, int64_t tile) {
+    const int s = (int)(g % c->d);
+    if (c->w_free_rec[s]) HIPCHK(c, hipStreamWaitEvent(c->h2d, c->w_free[s], 0));
+    const uint64_t bytes = p->info.tile_bytes;
+    const char *src = static_cast<const char *>(p->prob.W_host) + (uint64_t)tile * bytes;
+    hipEvent_t ea = nullptr, eb = nullptr;
+    if (c->timing) {
+        zi_status st = ev_timed(c, &ea);
+        if (st != ZI_OK) return st;
+        HIPCHK(c, hipEventRecord(ea, c->h2d));
+    }
+    HIPCHK(c, hipMemcpyAsync(c->wslot(s), src, bytes, hipMemcpyHostToDevice, c->h2d));
+    if (c->timing) {
+        zi_status st = ev_timed(c, &eb);
+        if (st != ZI_OK) return st;
+        HIPCHK(c, hipEventRecord(eb, c->h2d));
+        c->crec.push_back(CopyRec{0, (double)bytes, ea, eb});
+    }
+    HIPCHK(c, hipEventRecord(c->w_ready[s], c->h2d));
+    return ZI_OK;
+}
+
+zi_status write_back(zi_ctx *c, const zi_plan *p, int64_t tile, const void *src, hipEvent_t ready,
+                     hipEvent_t done) {
+    HIPCHK(c, hipStreamWaitEvent(c->d2h, ready, 0));
+    const uint64_t bytes = p->info.dw_tile_bytes;
+    char *dst = static_cast<char *>(p->prob.dW_host) + (uint64_t)tile * bytes;
+    hipEvent_t ea = nullptr, eb = nullptr;
+    if (c->timing) {
+        zi_status st = ev_timed(c, &ea);
+        if (st != ZI_OK) return st;
+        HIPCHK(c, hipEventRecord(ea, c->d2h));
+    }
+    HIPCHK(c, hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, c->d2h));
+    if (c->timing) {
+        zi_status st = ev_timed(c, &eb);
+        if (st != ZI_OK) return st;
+        HIPCHK(c, hipEventRecord(eb, c->d2h));
+        c->crec.push_back(CopyRec{1, (double)bytes, ea, eb});
+    }
+    HIPCHK(c, hipEventRecord(done, c->d2h));
+    return ZI_OK;
+}
+
+zi_status gemm(zi_ctx *c, int kind, GemmOp op, int dtype, const GemmArgs &a, double flops) {
+    hipEvent_t ea = nullptr, eb = nullptr;
+    if (c->timing) {
+        zi_status st = ev_timed(c, &ea);
+        if (st != ZI_OK) return st;
+        HIPCHK(c, hipEventRecord(ea, c->comp));
+    }
+    hipError_t e = launch_gemm(op, dtype, a, c->comp);
+    if (e != hipSuccess) return hip_fail(c, e, kKindNames[kind]);
+    if (c->timing) {
+        zi_status st = ev_timed(c, &eb);
+        if (st != ZI_OK) return st;
+        HIPCHK(c, hipEventRecord(eb, c->comp));
+        c->krec.push_back(KernelRec{kind, flops, ea, eb});
+    }
+    return ZI_OK;
+}
+
+zi_status run_fwd(zi_ctx *c, const zi_plan *p, const void *X, void *Y, void *H) {
+    const zi_problem &pr = p->prob;
+    const zi_plan_info &in = p->info;
+    const bool f32 = (pr.flags & ZI_FLAG_F32_OUT) != 0;
+    const int64_t N = pr.N, n = in.n;
+    const int d = c->d;
+    const int64_t base = c->seq;
+    const double tile_flops = 2.0 * (double)pr.T * (double)pr.K * (double)n;
+    zi_status st;
+    for (int64_t j = 0; j < std::min<int64_t>(d, N); ++j)
+        if ((st = stage(c, p, base + j, j)) != ZI_OK) return st;
+    for (int64_t i = 0; i < N; ++i) {
+        const int s = (int)((base + i) % d);
+        HIPCHK(c, hipStreamWaitEvent(c->comp, c->w_ready[s], 0));
+        GemmArgs a{};
+        a.Q = c->wslot(s);
+        a.ldq = pr.K;
+        a.P = X;
+        a.ldp = pr.K;
+        a.C = static_cast<char *>(Y) + i * n * (f32 ? 4 : 2);
+        a.ldc = pr.M;
+        a.C2 = H ? static_cast<char *>(H) + i * n * 2 : nullptr;
+        a.rows = pr.T;
+        a.cols = n;
+        a.red = pr.K;
+        a.out_f32 = f32 ? 1 : 0;
+        st = gemm(c, H ? K_FWD_GELU : K_FWD, H ? GemmOp::FwdGelu : GemmOp::Fwd, pr.dtype, a, tile_flops);
+        if (st != ZI_OK) return st;
+        HIPCHK(c, hipEventRecord(c->w_free[s], c->comp));
+        c->w_free_rec[s] = 1;
+        if (i + d < N && (st = stage(c, p, base + i + d, i + d)) != ZI_OK) return st;
+    }
+    c->seq += N;
+    return ZI_OK;
+}
+
+zi_status run_bwd(zi_ctx *c, const zi_plan *p, const void *X, const void *dY, float *dX, void *Yr) {
+    const zi_problem &pr = p->prob;
+    const zi_plan_info &in = p->info;
+    const bool f32 = (pr.flags & ZI_FLAG_F32_OUT) != 0;
+    const int64_t N = pr.N, n = in.n;
+    const int d = c->d;
+    const int64_t base = c->seq, dbase = c->dw_seq;
+    const double tile_flops = 2.0 * (double)pr.T * (double)pr.K * (double)n;
+    zi_status st;
+    for (int64_t j = 0; j < std::min<int64_t>(d, N); ++j)
+        if ((st = stage(c, p, base + j, j)) != ZI_OK) return st;
+    for (int64_t i = 0; i < N; ++i) {
+        const int s = (int)((base + i) % d);
+        HIPCHK(c, hipStreamWaitEvent(c->comp, c->w_ready[s], 0));
+        const uint16_t *dYi = static_cast<const uint16_t *>(dY) + i * n;
+        if (Yr) {  // recomputed forward slice from the same staged tile
+            GemmArgs a{};
+            a.Q = c->wslot(s);
+            a.ldq = pr.K;
+            a.P = X;
+            a.ldp = pr.K;
+            a.C = static_cast<char *>(Yr) + i * n * (f32 ? 4 : 2);
+            a.ldc = pr.M;
+            a.rows = pr.T;
+            a.cols = n;
+            a.red = pr.K;
+            a.out_f32 = f32 ? 1 : 0;
+            if ((st = gemm(c, K_FWD_RECOMPUTE, GemmOp::Fwd, pr.dtype, a, tile_flops)) != ZI_OK) return st;
+        }
+        {  // dX (+)= dY_i W_i^T: W_i^t[r][k] read across its rows
+            GemmArgs a{};
+            a.Q = c->wslot(s);
+            a.ldq = pr.K;
+            a.P = dYi;
+            a.ldp = pr.M;
+            a.C = dX;
+            a.ldc = pr.K;
+            a.rows = pr.T;
+            a.cols = pr.K;
+            a.red = n;
+            a.accumulate = i > 0 ? 1 : 0;
+            if ((st = gemm(c, K_DX, GemmOp::Dx, pr.dtype, a, tile_flops)) != ZI_OK) return st;
+        }
+        char *dst;
+        hipEvent_t ready, done;
+        int ds = -1;
+        if (c->dw_slots > 0) {
+            HIPCHK(c, hipEventRecord(c->w_free[s], c->comp));
+            c->w_free_rec[s] = 1;
+            ds = (int)((dbase + i) % c->dw_slots);
+            if (c->dw_free_rec[ds]) HIPCHK(c, hipStreamWaitEvent(c->comp, c->dw_free[ds], 0));
+            dst = c->dwslot(ds);
+            ready = c->dw_ready[ds];
+            done = c->dw_free[ds];
+        } else {
+            dst = c->wslot(s);  // the weight tile is consumed; its slot takes dW_i
+            ready = c->dw_ready[s];
+            done = c->w_free[s];
+        }
+        {  // dW_i^t[m][k] = sum_t dY[t][i n + m] X[t][k]
+            GemmArgs a{};
+            a.Q = X;
+            a.ldq = pr.K;
+            a.P = dYi;
+            a.ldp = pr.M;
+            a.C = dst;
+            a.ldc = pr.K;
+            a.rows = n;
+            a.cols = pr.K;
+            a.red = pr.T;
+            a.out_f32 = f32 ? 1 : 0;
+            if ((st = gemm(c, K_DW, GemmOp::Dw, pr.dtype, a, tile_flops)) != ZI_OK) return st;
+        }
+        HIPCHK(c, hipEventRecord(ready, c->comp));
+        if ((st = write_back(c, p, i, dst, ready, done)) != ZI_OK) return st;
+        if (ds >= 0)
+            c->dw_free_rec[ds] = 1;
+        else
+            c->w_free_rec[s] = 1;
+        if (i + d < N && (st = stage(c, p, base + i + d, i + d)) != ZI_OK) return st;
+    }
+    c->seq += N;
+    c->dw_seq += N;
+    return ZI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *zi_last_error(void) { return g_err; }
+
+int32_t zi_version(void) { return 100; }
+
+zi_status zi_host_alloc(uint64_t bytes, void **out) {
+    clear_error();
+    if (!out || !bytes) return fail(ZI_ERR_ARG, "zi_host_alloc needs bytes > 0 and an out pointer");
+    *out = nullptr;
+    HIPCHK(nullptr, hipHostMalloc(out, bytes, hipHostMallocDefault));
+    return ZI_OK;
+}
+
+zi_status zi_host_free(void *ptr) {
+    clear_error();
+    if (!ptr) return ZI_OK;
+    HIPCHK(nullptr, hipHostFree(ptr));
+    return ZI_OK;
+}
+
+zi_status zi_ctx_create(const zi_plan *plan, void *workspace_dev, uint64_t workspace_bytes,
+                        void *compute_stream, void *h2d_stream, void *d2h_stream, zi_ctx **out) {
+    clear_error();
+    if (!plan || !out) return fail(ZI_ERR_ARG, "plan and out are required");
+    *out = nullptr;
+    if (!workspace_dev) return fail(ZI_ERR_ARG, "workspace is NULL");
+    if ((uintptr_t)workspace_dev & 255u) return fail(ZI_ERR_ALIGN, "workspace is not 256-byte aligned");
+    const zi_plan_info &in = plan->info;
+    if (workspace_bytes < in.ring_bytes)
+        return fail(ZI_ERR_BUDGET, "workspace of %llu B is smaller than the ring's %llu B",
+                    (unsigned long long)workspace_bytes, (unsigned long long)in.ring_bytes);
+    zi_ctx *c = new (std::nothrow) zi_ctx;
+    if (!c) return fail(ZI_ERR_ARG, "out of host memory");
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        delete c;
+        return fail(ZI_ERR_HIP, "hipGetDevice failed");
+    }
+    c->device = dev;
+    c->comp = static_cast<hipStream_t>(compute_stream);
+    c->h2d = static_cast<hipStream_t>(h2d_stream);
+    c->d2h = static_cast<hipStream_t>(d2h_stream);
+    c->ws = static_cast<char *>(workspace_dev);
+    c->ws_bytes = workspace_bytes;
+    c->d = in.d;
+    c->dw_slots = in.dw_slots;
+    c->slot_bytes = round_up(in.tile_bytes, 256);
+    c->dw_slot_bytes = in.dw_slots ? round_up(in.dw_tile_bytes, 256) : 0;
+    const int nd = std::max(c->d, std::max(c->dw_slots, 1));
+    auto mk = [&](std::vector<hipEvent_t> &v, int count) -> bool {
+        v.assign(count, nullptr);
+        for (int i = 0; i < count; ++i)
+            if (hipEventCreateWithFlags(&v[i], hipEventDisableTiming) != hipSuccess) return false;
+        return true;
+    };
+    if (!mk(c->w_ready, c->d) || !mk(c->w_free, c->d) || !mk(c->dw_ready, nd) ||
+        !mk(c->dw_free, std::max(c->dw_slots, 1))) {
+        zi_ctx_destroy(c);
+        return fail(ZI_ERR_HIP, "hipEventCreateWithFlags failed");
+    }
+    c->w_free_rec.assign(c->d, 0);
+    c->dw_free_rec.assign(std::max(c->dw_slots, 1), 0);
+    *out = c;
+    return ZI_OK;
+}
+
+zi_status zi_ctx_destroy(zi_ctx *c) {
+    clear_error();
+    if (!c) return ZI_OK;
+    if (c->comp || c->h2d || c->d2h) {
+        (void)hipStreamSynchronize(c->comp);
+        (void)hipStreamSynchronize(c->h2d);
+        (void)hipStreamSynchronize(c->d2h);
+    }
+    for (auto *v : {&c->w_ready, &c->w_free, &c->dw_ready, &c->dw_free, &c->pool})
+        for (hipEvent_t e : *v)
+            if (e) (void)hipEventDestroy(e);
+    delete c;
+    return ZI_OK;
+}
+
+zi_status zi_tiled_linear_fwd(zi_ctx *ctx, const zi_plan *plan, const void *X_dev, void *Y_dev) {
+    clear_error();
+    zi_status st = check_pass(ctx, plan, false);
+    if (st != ZI_OK) return st;
+    if ((st = check_dev_ptr(X_dev, "X")) != ZI_OK || (st = check_dev_ptr(Y_dev, "Y")) != ZI_OK) return st;
+    return run_fwd(ctx, plan, X_dev, Y_dev, nullptr);
+}
+
+zi_status zi_tiled_linear_fwd_gelu(zi_ctx *ctx, const zi_plan *plan, const void *X_dev, void *A_dev,
+                                   void *H_dev) {
+    clear_error();
+    zi_status st = check_pass(ctx, plan, false);
+    if (st != ZI_OK) return st;
+    if (plan->prob.flags & ZI_FLAG_F32_OUT)
+        return fail(ZI_ERR_ARG, "the GeLU forward stores A and H in the input format only");
+    if ((st = check_dev_ptr(X_dev, "X")) != ZI_OK || (st = check_dev_ptr(A_dev, "A")) != ZI_OK ||
+        (st = check_dev_ptr(H_dev, "H")) != ZI_OK)
+        return st;
+    return run_fwd(ctx, plan, X_dev, A_dev, H_dev);
+}
+
+zi_status zi_tiled_linear_bwd(zi_ctx *ctx, const zi_plan *plan, const void *X_dev, const void *dY_dev,
+                              float *dX_dev) {
+    clear_error();
+    zi_status st = check_pass(ctx, plan, true);
+    if (st != ZI_OK) return st;
+    if ((st = check_dev_ptr(X_dev, "X")) != ZI_OK || (st = check_dev_ptr(dY_dev, "dY")) != ZI_OK ||
+        (st = check_dev_ptr(dX_dev, "dX")) != ZI_OK)
+        return st;
+    return run_bwd(ctx, plan, X_dev, dY_dev, dX_dev, nullptr);
+}
+
+zi_status zi_tiled_linear_bwd_recompute(zi_ctx *ctx, const zi_plan *plan, const void *X_dev,
+                                        const void *dY_dev, float *dX_dev, void *Yr_dev) {
+    clear_error();
+    zi_status st = check_pass(ctx, plan, true);
+    if (st != ZI_OK) return st;
+    if ((st = check_dev_ptr(X_dev, "X")) != ZI_OK || (st = check_dev_ptr(dY_dev, "dY")) != ZI_OK ||
+        (st = check_dev_ptr(dX_dev, "dX")) != ZI_OK || (st = check_dev_ptr(Yr_dev, "Yr")) != ZI_OK)
+        return st;
+    return run_bwd(ctx, plan, X_dev, dY_dev, dX_dev, Yr_dev);
+}
+
+zi_status zi_gelu_bwd(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const void *A_dev, void *dA_dev,
+                      int64_t count) {
+    clear_error();
+    zi_status st = check_ctx(ctx);
+    if (st != ZI_OK) return st;
+    if (dtype != ZI_F16 && dtype != ZI_BF16) return fail(ZI_ERR_ARG, "bad dtype %d", dtype);
+    if (count < 0) return fail(ZI_ERR_ARG, "count < 0");
+    if ((st = check_dev_ptr(dH_dev, "dH")) != ZI_OK || (st = check_dev_ptr(A_dev, "A")) != ZI_OK ||
+        (st = check_dev_ptr(dA_dev, "dA")) != ZI_OK)
+        return st;
+    hipEvent_t ea = nullptr, eb = nullptr;
+    if (ctx->timing) {
+        if ((st = ev_timed(ctx, &ea)) != ZI_OK) return st;
+        HIPCHK(ctx, hipEventRecord(ea, ctx->comp));
+    }
+    hipError_t e = launch_gelu_bwd(dtype, dH_dev, A_dev, dA_dev, count, ctx->comp);
+    if (e != hipSuccess) return hip_fail(ctx, e, "gelu_bwd");
+    if (ctx->timing) {
+        if ((st = ev_timed(ctx, &eb)) != ZI_OK) return st;
+        HIPCHK(ctx, hipEventRecord(eb, ctx->comp));
+        ctx->krec.push_back(KernelRec{K_GELU_BWD, (double)count, ea, eb});
+    }
+    return ZI_OK;
+}
+
+zi_status zi_sync(zi_ctx *ctx) {
+    clear_error();
+    if (!ctx) return fail(ZI_ERR_ARG, "context is NULL");
+    hipError_t e1 = hipStreamSynchronize(ctx->comp);
+    hipError_t e2 = hipStreamSynchronize(ctx->h2d);
+    hipError_t e3 = hipStreamSynchronize(ctx->d2h);
+    if (e1 != hipSuccess) return hip_fail(ctx, e1, "hipStreamSynchronize(compute)");
+    if (e2 != hipSuccess) return hip_fail(ctx, e2, "hipStreamSynchronize(h2d)");
+    if (e3 != hipSuccess) return hip_fail(ctx, e3, "hipStreamSynchronize(d2h)");
+    if (ctx->sticky != ZI_OK) return fail(ctx->sticky, "%s", ctx->sticky_msg.c_str());
+    return ZI_OK;
+}
+
+zi_status zi_ctx_set_timing(zi_ctx *ctx, int32_t enable) {
+    clear_error();
+    if (!ctx) return fail(ZI_ERR_ARG, "context is NULL");
+    ctx->timing = enable != 0;
+    return ZI_OK;
+}
+
+zi_status zi_ctx_reset_stats(zi_ctx *ctx) {
+    zi_status st = zi_sync(ctx);
+    if (st != ZI_OK) return st;
+    ctx->krec.clear();
+    ctx->crec.clear();
+    ctx->pool_used = 0;
+    return ZI_OK;
+}
+
+zi_status zi_ctx_stats(zi_ctx *ctx, zi_stats *out) {
+    zi_status st = zi_sync(ctx);
+    if (st != ZI_OK) return st;
+    if (!out) return fail(ZI_ERR_ARG, "out is NULL");
+    memset(out, 0, sizeof(*out));
+    out->kind_count = K_COUNT;
+    for (int k = 0; k < K_COUNT; ++k) snprintf(out->kind_name[k], sizeof(out->kind_name[k]), "%s", kKindNames[k]);
+    hipEvent_t ref = nullptr;
+    if (!ctx->krec.empty()) ref = ctx->krec.front().a;
+    if (!ctx->crec.empty() && !ref) ref = ctx->crec.front().a;
+    double lo = 0, hi = 0;
+    bool any = false;
+    auto span = [&](hipEvent_t a, hipEvent_t b) -> zi_status {
+        float t0 = 0, t1 = 0;
+        HIPCHK(ctx, hipEventElapsedTime(&t0, ref, a));
+        HIPCHK(ctx, hipEventElapsedTime(&t1, ref, b));
+        if (!any || t0 < lo) lo = t0;
+        if (!any || t1 > hi) hi = t1;
+        any = true;
+        return ZI_OK;
+    };
+    for (const KernelRec &r : ctx->krec) {
+        float ms = 0;
+        HIPCHK(ctx, hipEventElapsedTime(&ms, r.a, r.b));
+        out->launches[r.kind] += 1;
+        out->kernel_ms[r.kind] += ms;
+        out->flops[r.kind] += r.flops;
+        out->compute_busy_ms += ms;
+        if ((st = span(r.a, r.b)) != ZI_OK) return st;
+    }
+    for (const CopyRec &r : ctx->crec) {
+        float ms = 0;
+        HIPCHK(ctx, hipEventElapsedTime(&ms, r.a, r.b));
+        if (r.d2h) {
+            out->d2h_copies += 1;
+            out->d2h_ms += ms;
+            out->d2h_bytes += r.bytes;
+        } else {
+            out->h2d_copies += 1;
+            out->h2d_ms += ms;
+            out->h2d_bytes += r.bytes;
+        }
+        if ((st = span(r.a, r.b)) != ZI_OK) return st;
+    }
+    out->span_ms = any ? hi - lo : 0.0;
+    return ZI_OK;
+}
+
+}  // extern "C"

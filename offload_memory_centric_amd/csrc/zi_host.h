@@ -1,0 +1,33 @@
+// zi_host.h -- host-side internals shared by zi_plan.cpp and zi_api.cpp.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/zi.h"
+
+struct zi_plan {
+    zi_problem prob;
+    zi_plan_info info;
+};
+
+namespace zi {
+
+// Record an error for zi_last_error() and return its status.
+zi_status fail(zi_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+zi_status plan_validate_and_fill(const zi_problem *p, zi_plan_info *info);
+
+// One pass over the ring, times in seconds per tile.
+struct PassModel {
+    int N = 1, d = 1, dw_slots = 0;
+    bool backward = false;
+    double t_h2d = 0, t_d2h = 0;
+    double t_fwd = 0, t_recompute = 0, t_dx = 0, t_dw = 0;
+};
+struct Prediction {
+    double t_pass = 0, t_compute = 0, t_link = 0, stall = 0;
+};
+Prediction simulate_pass(const PassModel &m);
+
+}  // namespace zi

@@ -1,0 +1,45 @@
+// zi_internal.h -- declarations shared by the library's own translation units
+// (host API, ring model, kernels).  Not installed; the public ABI is zi.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace zi {
+
+// Which product a GEMM launch forms.  The output C[p][q] is row-major with q
+// contiguous; "Q" is the operand indexed by q, "P" the operand indexed by p.
+enum class GemmOp : int {
+    Fwd = 0,      // Y_i[t][m]  = sum_k X[t][k] W^t_i[m][k]      (Q = W slot, P = X)
+    FwdGelu = 1,  // same product; stores A = RNE(acc) and H = RNE(GeLU(A))
+    Dx = 2,       // dX[t][k]  (+)= sum_r dY[t][i*n+r] W^t_i[r][k] (Q = W slot^T, P = dY)
+    Dw = 3,       // dW^t_i[m][k] = sum_t dY[t][i*n+m] X[t][k]    (Q = X^T,      P = dY^T)
+};
+
+struct GemmArgs {
+    const void *Q;  // 16-bit elements
+    int64_t ldq;
+    const void *P;  // 16-bit elements
+    int64_t ldp;
+    void *C;        // output: 16-bit, or fp32 when out_f32 / Dx
+    int64_t ldc;
+    void *C2;       // FwdGelu: H output (same layout as C)
+    int64_t rows;   // extent of p
+    int64_t cols;   // extent of q (multiple of 8)
+    int64_t red;    // reduction length
+    int accumulate; // Dx only: 0 = overwrite, 1 = add into C
+    int out_f32;    // Fwd / Dw: write fp32 instead of the 16-bit format
+};
+
+// dtype: 1 = fp16, 2 = bf16.  Returns the launch status (hipGetLastError).
+hipError_t launch_gemm(GemmOp op, int dtype, const GemmArgs &a, hipStream_t stream);
+
+// dA[i] = RNE(dH[i] * GeLU'(A[i])), i < count.
+hipError_t launch_gelu_bwd(int dtype, const float *dH, const void *A, void *dA, int64_t count,
+                           hipStream_t stream);
+
+// Macro-tile of the GEMM kernels (rows of p, columns of q per workgroup).
+constexpr int kTileP = 256;
+constexpr int kTileQ = 256;
+
+}  // namespace zi

@@ -1,0 +1,203 @@
+// zi_plan.cpp -- planning of a tiled linear operator and the ring's timing model.
+//
+// Host-only code: nothing here touches the GPU, so all of it runs (and is
+// tested) without one.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "../../include/zi.h"
+#include "zi_host.h"
+
+namespace zi {
+
+static uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+zi_status plan_validate_and_fill(const zi_problem *p, zi_plan_info *info) {
+    if (!p) return fail(ZI_ERR_ARG, "problem is NULL");
+    if (p->dtype != ZI_F16 && p->dtype != ZI_BF16)
+        return fail(ZI_ERR_ARG, "dtype must be ZI_F16 (1) or ZI_BF16 (2), got %d", p->dtype);
+    if (p->flags & ~ZI_FLAG_F32_OUT) return fail(ZI_ERR_ARG, "unknown flags 0x%x", p->flags);
+    if (p->T < 1 || p->K < 1 || p->M < 1)
+        return fail(ZI_ERR_SHAPE, "T, K, M must be >= 1 (got %lld, %lld, %lld)", (long long)p->T,
+                    (long long)p->K, (long long)p->M);
+    if (p->N < 1) return fail(ZI_ERR_SHAPE, "N must be >= 1 (got %d)", p->N);
+    if (p->d < 1) return fail(ZI_ERR_ARG, "prefetch depth d must be >= 1 (got %d)", p->d);
+    if (p->M % p->N)
+        return fail(ZI_ERR_SHAPE, "N = %d does not divide M = %lld", p->N, (long long)p->M);
+    if (p->K % 8) return fail(ZI_ERR_SHAPE, "K = %lld is not a multiple of 8", (long long)p->K);
+    const int64_t n = p->M / p->N;
+    if (n % 8) return fail(ZI_ERR_SHAPE, "tile width n = M/N = %lld is not a multiple of 8", (long long)n);
+    // 32-bit tile indices inside the kernels: keep every extent well inside int
+    if (p->T > (int64_t)1 << 30 || p->K > (int64_t)1 << 30 || p->M > (int64_t)1 << 34)
+        return fail(ZI_ERR_SHAPE, "extent too large");
+
+    const bool f32 = (p->flags & ZI_FLAG_F32_OUT) != 0;
+    const uint64_t tile = (uint64_t)p->K * (uint64_t)n * 2u;
+    const uint64_t dw_tile = (uint64_t)p->K * (uint64_t)n * (f32 ? 4u : 2u);
+    const uint64_t slot = round_up(tile, 256);
+    const uint64_t dw_slot = round_up(dw_tile, 256);
+    const uint64_t budget = p->device_budget_bytes;
+
+    const uint64_t w_ring = (uint64_t)p->d * slot;
+    if (budget && w_ring > budget)
+        return fail(ZI_ERR_BUDGET, "%d weight slots of %llu B need %llu B > budget %llu B", p->d,
+                    (unsigned long long)slot, (unsigned long long)w_ring, (unsigned long long)budget);
+    // Gradient slots: two for full-duplex write-back when the budget allows,
+    // else one, else form dW_i inside W_i's slot (only if it fits there).
+    int dw_slots = 2;
+    if (budget) {
+        const uint64_t left = budget - w_ring;
+        dw_slots = (int)std::min<uint64_t>(2, left / dw_slot);
+    }
+    if (dw_slots == 0 && dw_tile > slot) {
+        if (p->dW_host)
+            return fail(ZI_ERR_BUDGET,
+                        "no room for a gradient slot and an fp32 gradient tile does not fit a weight slot");
+    }
+    // A forward-only plan (no dW_host) needs no gradient slot at all.
+    if (!p->dW_host) dw_slots = 0;
+
+    zi_plan_info o;
+    memset(&o, 0, sizeof(o));
+    o.n = n;
+    o.tile_bytes = tile;
+    o.dw_tile_bytes = dw_tile;
+    o.d = p->d;
+    o.dw_slots = dw_slots;
+    o.ring_bytes = w_ring + (uint64_t)dw_slots * dw_slot;
+    const double T = (double)p->T, K = (double)p->K, M = (double)p->M;
+    o.flops_fwd = 2.0 * T * K * M;
+    o.flops_bwd = 4.0 * T * K * M;
+    o.h2d_bytes_pass = K * M * 2.0;
+    o.d2h_bytes_bwd = K * M * (f32 ? 4.0 : 2.0);
+    o.ait_fwd = o.flops_fwd / o.h2d_bytes_pass;
+    o.ait_bwd = o.flops_bwd / o.h2d_bytes_pass;
+    o.working_bytes_one = o.h2d_bytes_pass / (double)p->N;
+    o.working_bytes_two = 2.0 * o.working_bytes_one;
+    *info = o;
+    return ZI_OK;
+}
+
+// ---- timing model -----------------------------------------------------------------
+
+// Event recurrence of one pass over the ring, mirroring the enqueue order of
+// the stager: copy j waits for the link and for the release of its slot by
+// tile j - d; the products of tile j wait for the compute stream and the copy.
+Prediction simulate_pass(const PassModel &m) {
+    Prediction r;
+    const int N = m.N, d = m.d;
+    std::vector<double> wfree(d, 0.0);
+    std::vector<double> dwfree(m.dw_slots > 0 ? m.dw_slots : 1, 0.0);
+    double link = 0.0, comp = 0.0, back = 0.0;
+    double busy = 0.0, linkbusy = 0.0;
+    for (int i = 0; i < N; ++i) {
+        const int s = i % d;
+        const double cs = std::max(link, wfree[s]);
+        const double ready = cs + m.t_h2d;
+        link = ready;
+        linkbusy += m.t_h2d;
+        double start = std::max(comp, ready);
+        if (!m.backward) {
+            comp = start + m.t_fwd;
+            busy += m.t_fwd;
+            wfree[s] = comp;
+            continue;
+        }
+        // recompute (optional) and dX read the weight slot
+        const double t_w = m.t_recompute + m.t_dx;
+        const double after_w = start + t_w;
+        busy += t_w + m.t_dw;
+        if (m.dw_slots > 0) {
+            wfree[s] = after_w;
+            const int ds = i % m.dw_slots;
+            const double dw_start = std::max(after_w, dwfree[ds]);
+            comp = dw_start + m.t_dw;
+            const double wb = std::max(back, comp) + m.t_d2h;
+            back = wb;
+            dwfree[ds] = wb;
+        } else {
+            comp = after_w + m.t_dw;
+            const double wb = std::max(back, comp) + m.t_d2h;
+            back = wb;
+            wfree[s] = wb;  // dW_i lives in W_i's slot until written back
+        }
+    }
+    r.t_pass = std::max(comp, back);
+    r.t_compute = busy;
+    r.t_link = linkbusy;
+    r.stall = r.t_pass > 0 ? 1.0 - busy / r.t_pass : 0.0;
+    return r;
+}
+
+}  // namespace zi
+
+using namespace zi;
+
+extern "C" int32_t zi_prefetch_depth(double t_fetch_s, double t_layer_s) {
+    if (!(t_layer_s > 0.0) || !(t_fetch_s >= 0.0)) return 1;
+    const double r = t_fetch_s / t_layer_s;
+    const double c = ceil(r);
+    if (c < 1.0) return 1;
+    if (c > 1e9) return 1000000000;
+    return (int32_t)c;
+}
+
+extern "C" zi_status zi_plan_tiles(const zi_problem *problem, zi_plan **out, zi_plan_info *info) {
+    clear_error();
+    zi_plan_info tmp;
+    zi_status st = plan_validate_and_fill(problem, &tmp);
+    if (st != ZI_OK) return st;
+    if (info) *info = tmp;
+    if (out) {
+        zi_plan *p = new (std::nothrow) zi_plan;
+        if (!p) return fail(ZI_ERR_ARG, "out of host memory");
+        p->prob = *problem;
+        p->info = tmp;
+        *out = p;
+    }
+    return ZI_OK;
+}
+
+extern "C" zi_status zi_plan_destroy(zi_plan *plan) {
+    clear_error();
+    delete plan;
+    return ZI_OK;
+}
+
+extern "C" zi_status zi_plan_predict(const zi_plan *plan, int32_t backward, double flop_rate,
+                                     double h2d_bps, double d2h_bps, zi_prediction *out) {
+    clear_error();
+    if (!plan || !out) return fail(ZI_ERR_ARG, "plan and out are required");
+    if (!(flop_rate > 0) || !(h2d_bps > 0) || (backward && !(d2h_bps > 0)))
+        return fail(ZI_ERR_ARG, "rates must be positive");
+    if (backward < 0 || backward > 2) return fail(ZI_ERR_ARG, "backward must be 0, 1 or 2");
+    if (backward && !plan->prob.dW_host)
+        return fail(ZI_ERR_STATE, "a backward needs a plan with dW_host");
+    const zi_problem &p = plan->prob;
+    const zi_plan_info &i = plan->info;
+    PassModel m;
+    m.N = p.N;
+    m.d = p.d;
+    m.backward = backward != 0;
+    m.dw_slots = i.dw_slots;
+    const double tile_flops = 2.0 * (double)p.T * (double)p.K * (double)i.n;
+    m.t_h2d = (double)i.tile_bytes / h2d_bps;
+    m.t_fwd = tile_flops / flop_rate;
+    m.t_dx = tile_flops / flop_rate;
+    m.t_dw = tile_flops / flop_rate;
+    m.t_recompute = backward == 2 ? tile_flops / flop_rate : 0.0;
+    m.t_d2h = backward ? (double)i.dw_tile_bytes / d2h_bps : 0.0;
+    Prediction r = simulate_pass(m);
+    out->t_pass_s = r.t_pass;
+    out->t_compute_s = r.t_compute;
+    out->t_link_s = r.t_link;
+    out->stall_frac = r.stall;
+    const double t_tile = backward ? (m.t_recompute + m.t_dx + m.t_dw) : m.t_fwd;
+    out->d_pages = zi_prefetch_depth(m.t_h2d, t_tile);
+    return ZI_OK;
+}

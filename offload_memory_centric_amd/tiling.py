@@ -1,0 +1,175 @@
+"""Convenience layer over the binding: plans, contexts and pinned buffers.
+
+torch is used here only for plumbing: device memory (workspace, activations)
+and streams.  Every step of the tiled operator runs in libzi.so.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import weakref
+from typing import Optional
+
+import torch
+
+from . import zi
+
+def inputs_dtype(dtype: str) -> torch.dtype:
+    return torch.float16 if dtype == "f16" else torch.bfloat16
+
+
+_ELEM = {torch.float16: 2, torch.bfloat16: 2, torch.float32: 4, torch.uint8: 1, torch.int16: 2}
+
+
+def host_tensor(shape, dtype: torch.dtype) -> torch.Tensor:
+    """Page-locked host tensor of exactly this size (hipHostMalloc through
+    zi_host_alloc); freed when the tensor is garbage-collected."""
+    nbytes = int(math.prod(shape)) * _ELEM[dtype]
+    ptr = zi.zi_host_alloc(nbytes)
+    buf = (ctypes.c_uint8 * nbytes).from_address(ptr)
+    weakref.finalize(buf, zi.zi_host_free, ptr)
+    return torch.frombuffer(buf, dtype=torch.uint8).view(dtype).view(tuple(shape))
+
+
+class Plan:
+    """One tiled linear operator Y[T x M] = X[T x K] W[K x M] with W^t in pinned host memory."""
+
+    def __init__(self, T: int, K: int, M: int, N: int, d: int, dtype: str, W_host: Optional[torch.Tensor],
+                 dW_host: Optional[torch.Tensor] = None, budget: int = 0, f32_out: bool = False):
+        self.problem = zi.zi_problem(T=T, K=K, M=M, N=N, d=d, dtype=zi.DTYPE_CODES[dtype],
+                                     flags=zi.ZI_FLAG_F32_OUT if f32_out else 0,
+                                     device_budget_bytes=budget,
+                                     W_host=None if W_host is None else W_host.data_ptr(),
+                                     dW_host=None if dW_host is None else dW_host.data_ptr())
+        if W_host is not None:
+            _need(W_host, M * K, (inputs_dtype(dtype),), "W_host", device=False)
+        self._keep = (W_host, dW_host)
+        self.handle, self.info = zi.zi_plan_tiles(self.problem)
+        self.T, self.K, self.M, self.N, self.d, self.dtype = T, K, M, N, d, dtype
+        self.f32_out = f32_out
+
+    @property
+    def n(self) -> int:
+        return self.info.n
+
+    def predict(self, backward: int, flop_rate: float, h2d: float, d2h: float = 0.0):
+        return zi.zi_plan_predict(self.handle, backward, flop_rate, h2d, d2h)
+
+    def close(self):
+        if self.handle:
+            zi.zi_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _need(t, elems: int, dtypes, name: str, device: bool = True):
+    """Host-side check that a tensor can hold what a pass will read or write."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if dtypes and t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if device and t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.numel() < elems:
+        raise ValueError("%s holds %d elements, the pass needs %d" % (name, t.numel(), elems))
+
+
+def _lp(plan) -> tuple:
+    return (torch.float16,) if plan.dtype == "f16" else (torch.bfloat16,)
+
+
+def _out(plan) -> tuple:
+    return (torch.float32,) if plan.f32_out else _lp(plan)
+
+
+class Context:
+    """The ring over a torch-allocated workspace and three torch streams."""
+
+    def __init__(self, plan: Plan, device: str = "cuda", workspace_bytes: Optional[int] = None,
+                 streams=None):
+        nbytes = int(workspace_bytes if workspace_bytes is not None else plan.info.ring_bytes)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        if streams is None:
+            streams = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device),
+                       torch.cuda.Stream(device=device))
+        self.streams = streams
+        self.handle = zi.zi_ctx_create(plan.handle, self.workspace, nbytes, *streams)
+
+    def fwd(self, plan: Plan, X, Y):
+        _need(X, plan.T * plan.K, _lp(plan), "X")
+        _need(Y, plan.T * plan.M, _out(plan), "Y")
+        zi.zi_tiled_linear_fwd(self.handle, plan.handle, X, Y)
+
+    def fwd_gelu(self, plan: Plan, X, A, H):
+        _need(X, plan.T * plan.K, _lp(plan), "X")
+        _need(A, plan.T * plan.M, _lp(plan), "A")
+        _need(H, plan.T * plan.M, _lp(plan), "H")
+        zi.zi_tiled_linear_fwd_gelu(self.handle, plan.handle, X, A, H)
+
+    def _bwd_args(self, plan: Plan, X, dY, dX):
+        _need(X, plan.T * plan.K, _lp(plan), "X")
+        _need(dY, plan.T * plan.M, _lp(plan), "dY")
+        _need(dX, plan.T * plan.K, (torch.float32,), "dX")
+        dW = plan._keep[1]
+        if dW is None:
+            raise ValueError("plan has no dW_host")
+        _need(dW, plan.M * plan.K, _out(plan), "dW_host", device=False)
+
+    def bwd(self, plan: Plan, X, dY, dX):
+        self._bwd_args(plan, X, dY, dX)
+        zi.zi_tiled_linear_bwd(self.handle, plan.handle, X, dY, dX)
+
+    def bwd_recompute(self, plan: Plan, X, dY, dX, Yr):
+        self._bwd_args(plan, X, dY, dX)
+        _need(Yr, plan.T * plan.M, _out(plan), "Yr")
+        zi.zi_tiled_linear_bwd_recompute(self.handle, plan.handle, X, dY, dX, Yr)
+
+    def gelu_bwd(self, dtype: str, dH, A, dA, count: int):
+        lp = (torch.float16,) if dtype == "f16" else (torch.bfloat16,)
+        _need(dH, count, (torch.float32,), "dH")
+        _need(A, count, lp, "A")
+        _need(dA, count, lp, "dA")
+        zi.zi_gelu_bwd(self.handle, zi.DTYPE_CODES[dtype], dH, A, dA, count)
+
+    def sync(self):
+        zi.zi_sync(self.handle)
+
+    def set_timing(self, on: bool):
+        zi.zi_ctx_set_timing(self.handle, on)
+
+    def reset_stats(self):
+        zi.zi_ctx_reset_stats(self.handle)
+
+    def stats(self) -> dict:
+        return zi.zi_ctx_stats(self.handle).as_dict()
+
+    def close(self):
+        if self.handle:
+            zi.zi_ctx_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def ffn_block_step(ctx: Context, p1: Plan, p2: Plan, X, A, H, Y, dY, dH, dA, dX, Yr) -> None:
+    """The feed-forward block with activation checkpointing, enqueued without
+    host synchronisation (the ring carries prefetch across the calls):
+    forward W1 (+GeLU), forward W2, recomputed forward W1 (+GeLU), backward W2
+    with the recomputed W2 product, dA = dH * GeLU'(A), backward W1."""
+    ctx.fwd_gelu(p1, X, A, H)
+    ctx.fwd(p2, H, Y)
+    ctx.fwd_gelu(p1, X, A, H)
+    ctx.bwd_recompute(p2, H, dY, dH, Yr)
+    ctx.gelu_bwd(p1.dtype, dH, A, dA, A.numel())
+    ctx.bwd(p1, X, dA, dX)

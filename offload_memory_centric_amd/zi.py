@@ -1,0 +1,225 @@
+"""ctypes binding of libzi.so, one Python function per entry point of include/zi.h.
+
+Argument marshalling only: every step of the tiled operator runs inside the
+library.  Pointer arguments accept an int address or a torch tensor (its
+``data_ptr()``); stream arguments accept an int handle or a ``torch.cuda.Stream``.
+A non-OK status raises :class:`ZiError` carrying the status and the library's
+error text.  Importing this module loads the library and fails loudly if it
+has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzi.so")
+
+ZI_OK, ZI_ERR_ARG, ZI_ERR_SHAPE, ZI_ERR_BUDGET, ZI_ERR_NOT_PINNED, ZI_ERR_ALIGN, ZI_ERR_HIP, ZI_ERR_STATE = range(8)
+STATUS_NAMES = ["ZI_OK", "ZI_ERR_ARG", "ZI_ERR_SHAPE", "ZI_ERR_BUDGET", "ZI_ERR_NOT_PINNED",
+                "ZI_ERR_ALIGN", "ZI_ERR_HIP", "ZI_ERR_STATE"]
+ZI_F16, ZI_BF16 = 1, 2
+ZI_FLAG_F32_OUT = 0x1
+DTYPE_CODES = {"f16": ZI_F16, "bf16": ZI_BF16}
+
+
+class ZiError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__("%s: %s" % (name, message))
+
+
+class zi_problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("K", ctypes.c_int64), ("M", ctypes.c_int64),
+                ("N", ctypes.c_int32), ("d", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("device_budget_bytes", ctypes.c_uint64),
+                ("W_host", ctypes.c_void_p), ("dW_host", ctypes.c_void_p)]
+
+
+class zi_plan_info(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("tile_bytes", ctypes.c_uint64),
+                ("dw_tile_bytes", ctypes.c_uint64), ("d", ctypes.c_int32),
+                ("dw_slots", ctypes.c_int32), ("ring_bytes", ctypes.c_uint64),
+                ("flops_fwd", ctypes.c_double), ("flops_bwd", ctypes.c_double),
+                ("h2d_bytes_pass", ctypes.c_double), ("d2h_bytes_bwd", ctypes.c_double),
+                ("ait_fwd", ctypes.c_double), ("ait_bwd", ctypes.c_double),
+                ("working_bytes_one", ctypes.c_double), ("working_bytes_two", ctypes.c_double)]
+
+
+class zi_prediction(ctypes.Structure):
+    _fields_ = [("t_pass_s", ctypes.c_double), ("t_compute_s", ctypes.c_double),
+                ("t_link_s", ctypes.c_double), ("stall_frac", ctypes.c_double),
+                ("d_pages", ctypes.c_int32)]
+
+
+class zi_stats(ctypes.Structure):
+    _fields_ = [("kind_count", ctypes.c_int32), ("kind_name", (ctypes.c_char * 24) * 8),
+                ("launches", ctypes.c_int64 * 8), ("kernel_ms", ctypes.c_double * 8),
+                ("flops", ctypes.c_double * 8), ("h2d_copies", ctypes.c_int64),
+                ("d2h_copies", ctypes.c_int64), ("h2d_ms", ctypes.c_double),
+                ("d2h_ms", ctypes.c_double), ("h2d_bytes", ctypes.c_double),
+                ("d2h_bytes", ctypes.c_double), ("span_ms", ctypes.c_double),
+                ("compute_busy_ms", ctypes.c_double)]
+
+    def as_dict(self):
+        kinds = {}
+        for k in range(self.kind_count):
+            name = bytes(self.kind_name[k]).split(b"\0", 1)[0].decode()
+            kinds[name] = {"launches": self.launches[k], "ms": self.kernel_ms[k], "flops": self.flops[k]}
+        return {"kinds": kinds, "h2d_copies": self.h2d_copies, "d2h_copies": self.d2h_copies,
+                "h2d_ms": self.h2d_ms, "d2h_ms": self.d2h_ms, "h2d_bytes": self.h2d_bytes,
+                "d2h_bytes": self.d2h_bytes, "span_ms": self.span_ms,
+                "compute_busy_ms": self.compute_busy_ms}
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libzi.so is not built (expected at %s); run "
+                      "`python -m offload_memory_centric_amd.build`" % LIB_PATH)
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_S = ctypes.c_int  # zi_status
+_sigs = {
+    "zi_plan_tiles": (_S, [ctypes.POINTER(zi_problem), ctypes.POINTER(_P), ctypes.POINTER(zi_plan_info)]),
+    "zi_plan_destroy": (_S, [_P]),
+    "zi_prefetch_depth": (ctypes.c_int32, [ctypes.c_double, ctypes.c_double]),
+    "zi_plan_predict": (_S, [_P, ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                             ctypes.POINTER(zi_prediction)]),
+    "zi_ctx_create": (_S, [_P, _P, ctypes.c_uint64, _P, _P, _P, ctypes.POINTER(_P)]),
+    "zi_ctx_destroy": (_S, [_P]),
+    "zi_tiled_linear_fwd": (_S, [_P, _P, _P, _P]),
+    "zi_tiled_linear_fwd_gelu": (_S, [_P, _P, _P, _P, _P]),
+    "zi_tiled_linear_bwd": (_S, [_P, _P, _P, _P, _P]),
+    "zi_tiled_linear_bwd_recompute": (_S, [_P, _P, _P, _P, _P, _P]),
+    "zi_gelu_bwd": (_S, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_int64]),
+    "zi_sync": (_S, [_P]),
+    "zi_ctx_set_timing": (_S, [_P, ctypes.c_int32]),
+    "zi_ctx_reset_stats": (_S, [_P]),
+    "zi_ctx_stats": (_S, [_P, ctypes.POINTER(zi_stats)]),
+    "zi_host_alloc": (_S, [ctypes.c_uint64, ctypes.POINTER(_P)]),
+    "zi_host_free": (_S, [_P]),
+    "zi_last_error": (ctypes.c_char_p, []),
+    "zi_version": (ctypes.c_int32, []),
+}
+for _name, (_res, _args) in _sigs.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_sigs)
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(s) -> int:
+    if s is None:
+        return None
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    return int(s)
+
+
+def _check(status: int):
+    if status != ZI_OK:
+        raise ZiError(status, zi_last_error())
+
+
+# ---- entry points ----------------------------------------------------------------
+
+def zi_last_error() -> str:
+    return (_lib.zi_last_error() or b"").decode(errors="replace")
+
+
+def zi_version() -> int:
+    return _lib.zi_version()
+
+
+def zi_plan_tiles(problem: zi_problem, make_plan: bool = True):
+    """Returns (plan handle or None, zi_plan_info)."""
+    info = zi_plan_info()
+    h = _P()
+    _check(_lib.zi_plan_tiles(ctypes.byref(problem), ctypes.byref(h) if make_plan else None,
+                              ctypes.byref(info)))
+    return (h.value if make_plan else None), info
+
+
+def zi_plan_destroy(plan) -> None:
+    _check(_lib.zi_plan_destroy(plan))
+
+
+def zi_prefetch_depth(t_fetch_s: float, t_layer_s: float) -> int:
+    return _lib.zi_prefetch_depth(t_fetch_s, t_layer_s)
+
+
+def zi_plan_predict(plan, backward: int, flop_rate: float, h2d_bytes_per_s: float,
+                    d2h_bytes_per_s: float = 0.0) -> zi_prediction:
+    out = zi_prediction()
+    _check(_lib.zi_plan_predict(plan, int(backward), flop_rate, h2d_bytes_per_s, d2h_bytes_per_s,
+                                ctypes.byref(out)))
+    return out
+
+
+def zi_ctx_create(plan, workspace, workspace_bytes: int, compute_stream, h2d_stream, d2h_stream):
+    h = _P()
+    _check(_lib.zi_ctx_create(plan, _ptr(workspace), int(workspace_bytes), _stream(compute_stream),
+                              _stream(h2d_stream), _stream(d2h_stream), ctypes.byref(h)))
+    return h.value
+
+
+def zi_ctx_destroy(ctx) -> None:
+    _check(_lib.zi_ctx_destroy(ctx))
+
+
+def zi_tiled_linear_fwd(ctx, plan, X, Y) -> None:
+    _check(_lib.zi_tiled_linear_fwd(ctx, plan, _ptr(X), _ptr(Y)))
+
+
+def zi_tiled_linear_fwd_gelu(ctx, plan, X, A, H) -> None:
+    _check(_lib.zi_tiled_linear_fwd_gelu(ctx, plan, _ptr(X), _ptr(A), _ptr(H)))
+
+
+def zi_tiled_linear_bwd(ctx, plan, X, dY, dX) -> None:
+    _check(_lib.zi_tiled_linear_bwd(ctx, plan, _ptr(X), _ptr(dY), _ptr(dX)))
+
+
+def zi_tiled_linear_bwd_recompute(ctx, plan, X, dY, dX, Yr) -> None:
+    _check(_lib.zi_tiled_linear_bwd_recompute(ctx, plan, _ptr(X), _ptr(dY), _ptr(dX), _ptr(Yr)))
+
+
+def zi_gelu_bwd(ctx, dtype: int, dH, A, dA, count: int) -> None:
+    _check(_lib.zi_gelu_bwd(ctx, int(dtype), _ptr(dH), _ptr(A), _ptr(dA), int(count)))
+
+
+def zi_sync(ctx) -> None:
+    _check(_lib.zi_sync(ctx))
+
+
+def zi_ctx_set_timing(ctx, enable: bool) -> None:
+    _check(_lib.zi_ctx_set_timing(ctx, 1 if enable else 0))
+
+
+def zi_ctx_reset_stats(ctx) -> None:
+    _check(_lib.zi_ctx_reset_stats(ctx))
+
+
+def zi_ctx_stats(ctx) -> zi_stats:
+    out = zi_stats()
+    _check(_lib.zi_ctx_stats(ctx, ctypes.byref(out)))
+    return out
+
+
+def zi_host_alloc(nbytes: int) -> int:
+    h = _P()
+    _check(_lib.zi_host_alloc(int(nbytes), ctypes.byref(h)))
+    return h.value
+
+
+def zi_host_free(ptr) -> None:
+    _check(_lib.zi_host_free(_ptr(ptr)))
