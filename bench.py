@@ -1,0 +1,317 @@
+"""Benchmark of the tiled linear hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input.  The
+default workload is the feed-forward block of the 1T-parameter model that the
+ZeRO-Infinity transformer-math page tiles in its section "Memory-centric
+tiling: operators bigger than the device": up-projection W1[25600 x 102400],
+GeLU, down-projection W2[102400 x 25600], both fp16 in pinned host memory and
+split into 16 output-dimension tiles each, T = 32768 tokens (the batch that
+the tier table's section shows clearing the slow-tier bar), prefetch depth 2.
+One step = forward W1 (+GeLU), forward W2, recomputed forward W1 (+GeLU),
+backward W2 with the recomputed W2 product, dA = dH * GeLU'(A), backward W1:
+forward 2P + recompute 2P + backward 4P = 8PT FLOPs (the page's
+FLOPs-per-byte section), every tile staged over the host link per pass and
+every weight gradient written back to pinned host memory.
+
+Prints one JSON line (rank 0, N = 1).  ``--workload linear`` times a single
+tiled linear fwd+bwd instead (the mid FFN up-projection shape by default).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tiled-linear fwd+bwd TFLOP/s, % MFMA peak, exposed host-transfer stall %"
+PEAK_MFMA_F16 = 2.5e15   # dense fp16/bf16 MFMA, MI355X published figure (FLOP/s)
+PEAK_HBM = 8.0e12        # bytes/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", choices=["ffn", "linear"], default="ffn")
+    ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--d", type=int, default=2)
+    ap.add_argument("--dtype", choices=["f16", "bf16"], default=None)
+    ap.add_argument("--K", type=int, default=None)
+    ap.add_argument("--M", type=int, default=None)
+    ap.add_argument("--N", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-link-peak", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def link_peak(torch, tiling, nbytes=1 << 30, reps=5):
+    """hipMemcpyAsync peak from pinned memory: H2D alone, D2H alone, both at once."""
+    host = tiling.host_tensor((nbytes,), torch.uint8)
+    host2 = tiling.host_tensor((nbytes,), torch.uint8)
+    dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dev2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def timed(fn):
+        out = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            out.append(time.perf_counter() - t0)
+        return statistics.median(out)
+
+    def h2d():
+        with torch.cuda.stream(s1):
+            dev.copy_(host, non_blocking=True)
+
+    def d2h():
+        with torch.cuda.stream(s2):
+            host2.copy_(dev2, non_blocking=True)
+
+    def both():
+        h2d()
+        d2h()
+
+    h2d()
+    d2h()
+    t_h2d, t_d2h, t_both = timed(h2d), timed(d2h), timed(both)
+    del host, host2, dev, dev2
+    return {"h2d_GBps": nbytes / t_h2d / 1e9, "d2h_GBps": nbytes / t_d2h / 1e9,
+            "duplex_h2d_plus_d2h_GBps": 2 * nbytes / t_both / 1e9, "bytes": nbytes, "reps": reps}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from offload_memory_centric_amd import inputs, tiling
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    dtype = args.dtype or ("f16" if args.workload == "ffn" else "bf16")
+    tdt = inputs.torch_dtype(dtype)
+    d = args.d
+    seed = 0
+
+    link = None if args.no_link_peak else link_peak(torch, tiling)
+    if link:
+        log("link peak", link)
+
+    # ---------------- workload ----------------
+    if args.workload == "ffn":
+        T = args.T or 32768
+        D, F = args.K or 25600, args.M or 102400
+        N1 = N2 = args.N or 16
+        log("allocating FFN block T=%d D=%d F=%d" % (T, D, F))
+        X = inputs.new((T, D), dtype, "gaussian", seed, "X", device="cuda")
+        dY = inputs.new((T, D), dtype, "gaussian", seed, "dY", device="cuda")
+        W1t = tiling.host_tensor((F, D), tdt)
+        W2t = tiling.host_tensor((D, F), tdt)
+        inputs.fill_(W1t, "gaussian", seed, "W1", std=0.02, device="cuda", chunk_rows=4096)
+        inputs.fill_(W2t, "gaussian", seed, "W2", std=0.02, device="cuda", chunk_rows=1024)
+        dW1t = tiling.host_tensor((F, D), tdt)
+        dW2t = tiling.host_tensor((D, F), tdt)
+        p1 = tiling.Plan(T, D, F, N1, d, dtype, W1t, dW1t)
+        p2 = tiling.Plan(T, F, D, N2, d, dtype, W2t, dW2t)
+        ctx = tiling.Context(p1 if p1.info.ring_bytes >= p2.info.ring_bytes else p2)
+        A = torch.empty((T, F), dtype=tdt, device="cuda")
+        H = torch.empty_like(A)
+        dA = torch.empty_like(A)
+        dH = torch.empty((T, F), dtype=torch.float32, device="cuda")
+        Y = torch.empty((T, D), dtype=tdt, device="cuda")
+        Yr = torch.empty_like(Y)
+        dX = torch.empty((T, D), dtype=torch.float32, device="cuda")
+        P = D * F * 2  # parameters of the block
+        flops_step = 8.0 * P * T
+        h2d_bytes_step = 2.0 * (3 * D * F + 2 * D * F)
+
+        def step():
+            tiling.ffn_block_step(ctx, p1, p2, X, A, H, Y, dY, dH, dA, dX, Yr)
+
+        config = {"workload": "ffn_block_fwd_recompute_bwd", "T": T, "d_model": D, "d_ff": F,
+                  "N_up": N1, "N_down": N2, "n_up": F // N1, "n_down": D // N2, "d": d,
+                  "weights": "pinned host", "dtype": dtype}
+        plans = (p1, p2)
+    else:
+        T = args.T or 4096
+        K, M = args.K or 8192, args.M or 32768
+        N = args.N or 8
+        log("allocating linear T=%d K=%d M=%d N=%d" % (T, K, M, N))
+        X = inputs.new((T, K), dtype, "gaussian", seed, "X", device="cuda")
+        dY = inputs.new((T, M), dtype, "gaussian", seed, "dY", device="cuda")
+        Wt = tiling.host_tensor((M, K), tdt)
+        inputs.fill_(Wt, "gaussian", seed, "W", std=0.02, device="cuda", chunk_rows=4096)
+        dWt = tiling.host_tensor((M, K), tdt)
+        p = tiling.Plan(T, K, M, N, d, dtype, Wt, dWt)
+        ctx = tiling.Context(p)
+        Y = torch.empty((T, M), dtype=tdt, device="cuda")
+        dX = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        flops_step = 6.0 * T * K * M
+        h2d_bytes_step = 2.0 * K * M * 2
+
+        def step():
+            ctx.fwd(p, X, Y)
+            ctx.bwd(p, X, dY, dX)
+
+        config = {"workload": "tiled_linear_fwd_bwd", "T": T, "K": K, "M": M, "N": N, "n": M // N,
+                  "d": d, "weights": "pinned host", "dtype": dtype}
+        plans = (p,)
+    torch.cuda.synchronize()
+
+    # ---------------- warmup ----------------
+    for _ in range(args.warmup):
+        step()
+    ctx.sync()
+    torch.cuda.synchronize()
+
+    # ---------------- timed steps ----------------
+    ctx.set_timing(True)
+    ctx.reset_stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    ctx.sync()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = ctx.stats()
+    ctx.set_timing(False)
+
+    ms_step = wall / args.steps * 1e3
+    tflops = flops_step * args.steps / wall / 1e12
+    busy_ms = st["compute_busy_ms"]
+    stall = max(0.0, 1.0 - busy_ms / (wall * 1e3))
+    h2d_rate = st["h2d_bytes"] / (st["h2d_ms"] * 1e-3) if st["h2d_ms"] > 0 else 0.0
+    d2h_rate = st["d2h_bytes"] / (st["d2h_ms"] * 1e-3) if st["d2h_ms"] > 0 else 0.0
+
+    kinds = {k: v for k, v in st["kinds"].items() if v["launches"]}
+    dom = max(kinds.items(), key=lambda kv: kv[1]["ms"])
+    dom_name, dom_v = dom
+    avg_ms = dom_v["ms"] / dom_v["launches"]
+    flops_launch = dom_v["flops"] / dom_v["launches"]
+    achieved = flops_launch / (avg_ms * 1e-3) / 1e12
+    kernel_table = {k: {"launches": v["launches"], "avg_ms": v["ms"] / v["launches"],
+                        "total_ms_per_step": v["ms"] / args.steps,
+                        "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if k != "gelu_bwd" else None}
+                    for k, v in kinds.items()}
+
+    # model prediction of the stall with the measured rates
+    pred = None
+    if link:
+        try:
+            R = sum(v["flops"] for k, v in kinds.items() if k != "gelu_bwd") / (
+                sum(v["ms"] for k, v in kinds.items() if k != "gelu_bwd") * 1e-3)
+            pred = {"kernel_flop_rate_TFLOPs": R / 1e12,
+                    "link_h2d_GBps": link["h2d_GBps"],
+                    "balance_flop_per_byte": R / (link["h2d_GBps"] * 1e9),
+                    "ait_step_flop_per_h2d_byte": flops_step / h2d_bytes_step}
+        except ZeroDivisionError:
+            pred = None
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded Gaussian: X, dY ~ N(0,1), W ~ N(0, 0.02^2))",
+        "config": config,
+        "pct_mfma_peak": round(100.0 * tflops * 1e12 / PEAK_MFMA_F16, 2),
+        "exposed_stall_pct": round(100.0 * stall, 2),
+        "h2d_GBps_achieved": round(h2d_rate / 1e9, 2),
+        "d2h_GBps_achieved": round(d2h_rate / 1e9, 2),
+        "link_peak": link,
+        "kernels": kernel_table,
+        "model": pred,
+        "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_MFMA_F16 / 1e12, "unit": "TFLOP/s",
+                     "frac": round(achieved * 1e12 / PEAK_MFMA_F16, 4),
+                     "flops_per_launch": flops_launch, "avg_launch_ms": round(avg_ms, 4),
+                     "traffic": None},
+    }
+
+    # ---------------- CPU baseline (oracle, after the GPU timing) ----------------
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, np, torch, config, locals())
+    print(json.dumps(result), flush=True)
+    ctx.close()
+
+
+def _bits(torch, np, t):
+    if t.device.type != "cpu":
+        t = t.cpu()
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def cpu_baseline(args, np, torch, config, env):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+
+    oracle.set_threads(0)
+    cores = oracle.get_threads()
+    dtype = config["dtype"]
+    t_start = time.perf_counter()
+    if config["workload"] == "ffn_block_fwd_recompute_bwd":
+        X, dY, W1t, W2t = (_bits(torch, np, env[k]) for k in ("X", "dY", "W1t", "W2t"))
+        T, D, F = config["T"], config["d_model"], config["d_ff"]
+        rng = np.random.default_rng(0)
+        nt = 1
+        nf = 2
+        t_rows = np.sort(rng.choice(T, nt, replace=False))
+        f_cols = np.sort(rng.choice(F, nf, replace=False))
+        d2 = np.sort(rng.choice(D, 2, replace=False))
+        dc = np.sort(rng.choice(D, 2, replace=False))
+        t0 = time.perf_counter()
+        oracle.ffn_sample(X, W1t, W2t, dY, dtype, t_rows, f_cols, d2, dc, chunk=4096)
+        secs = time.perf_counter() - t0
+        # multiply-adds the sample performs (2 FLOPs each): token rows over the whole
+        # hidden dimension, hidden columns over all tokens
+        flops = 2.0 * (nt * F * D * 2 + nt * F * (len(d2) + len(dc)) + nf * T * D * 2 +
+                       nf * T * (len(d2) + len(dc)))
+        sample = ("oracle.ffn_sample: %d token row(s) through the whole block and %d hidden "
+                  "column(s) over all %d tokens (%.3g FLOPs)" % (nt, nf, T, flops))
+    else:
+        X, dY, Wt = (_bits(torch, np, env[k]) for k in ("X", "dY", "Wt"))
+        T, K, M = config["T"], config["K"], config["M"]
+        rows = np.arange(0, T, max(1, T // 32))[:32]
+        t0 = time.perf_counter()
+        oracle.linear_fwd_sample(X, Wt, rows, np.arange(M), dtype)
+        secs = time.perf_counter() - t0
+        flops = 2.0 * len(rows) * K * M
+        sample = "oracle.linear_fwd_sample: %d rows x all %d columns (%.3g FLOPs)" % (len(rows), M, flops)
+    log("cpu baseline: %.1f s sample, %.1f s total" % (secs, time.perf_counter() - t_start))
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds": round(secs, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -14,24 +14,34 @@
 // Workgroup: 256 threads = 4 wave64s in a 2 x 2 arrangement over a
 // 256 (p) x 256 (q) macro-tile; each wave owns 128 x 128 = 4 x 4 MFMA blocks
 // of 32 x 32 (v_mfma_f32_32x32x16_{f16,bf16}, fp32 accumulators: 256 per lane,
-// which is why the kernel runs one wave per SIMD).  The reduction advances 64
-// at a time through two LDS stages (2 x 64 KiB): global loads of step k+1 are
-// issued before the MFMAs of step k and written to the other stage after
-// them, one barrier per step.
+// so the kernel runs one wave per SIMD).
 //
-// LDS rows hold 64 reduction elements (128 B = 8 chunks of 16 B).  Chunk c of
-// row r sits at physical chunk c ^ ((r ^ (r >> 3)) & 7): the MFMA fragment
-// reads (32 consecutive rows, same chunk), the row-contiguous writes (one row,
-// 8 chunks) and the transposed writes (rows 8 apart, same chunk) each touch 8
-// distinct chunk positions per 8 lanes.
-//
-// An operand whose reduction index is strided in memory is loaded as 8 x 8
-// blocks of 16-bit values (8 reduction rows of 8 contiguous elements, one
-// 16-byte load each, coalesced along the contiguous dimension) and transposed
-// in registers before it is written to LDS in the same reduction-contiguous
-// layout, so the MFMA side never sees the difference.
+// Memory pipeline.  With one wave per SIMD nothing hides a wait except work
+// already queued, so global reads must be issued far ahead of their use.  Every
+// operand is copied global -> LDS by the buffer unit (buffer_load ... lds,
+// 16 bytes per lane), which needs no registers, into a ring of kStages LDS
+// stages of BK = 32 reduction elements; the copy of step k + kStages is issued
+// as soon as every wave has finished reading step k, so kStages steps are in
+// flight.  Each step the waves wait only for the step they need next
+// (s_waitcnt vmcnt(N) with N = the copies still allowed in flight), meet at one
+// barrier, and read MFMA fragments from LDS:
+//   * reduction-contiguous operand: rows of 32 reduction values (64 B, four
+//     16-byte chunks); chunk c of row r sits at c ^ ((r >> 2) & 3); a fragment
+//     is one ds_read_b128 per lane;
+//   * reduction-strided operand: kept in its natural layout, rows of 256
+//     elements (512 B, sixteen 32-byte segments) per reduction index k;
+//     segment s of row k sits at s ^ 2 (k & 3); a fragment is two
+//     ds_read_b64_tr_b16 per lane.  That instruction, per 16 lanes, hands lane
+//     j the (j % 4)-th element read by lanes 4e + j / 4 (e = 0..3); pointing
+//     those 16 lanes at 4 consecutive rows x 4 four-element column groups gives
+//     each lane 4 consecutive reduction values of one column: the MFMA layout.
+// The LDS serves 256 bytes per clock (64 banks of 4 bytes): both layouts let
+// every 16 lanes of a 16-byte read, and every 32 lanes of an 8-byte transposing
+// read, fall on distinct banks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "zi_internal.h"
 
@@ -40,95 +50,176 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
-constexpr int BK = 64;                        // reduction elements per main-loop step
-constexpr int kRowBytes = BK * 2;             // one LDS row: 8 chunks of 16 B
-constexpr int kOperandBytes = 256 * kRowBytes;  // 32 KiB: one operand, one stage
+constexpr int BK = 32;                          // reduction elements per step
+constexpr int kOperandBytes = 256 * BK * 2;     // 16 KiB: one operand, one step
 constexpr int kStageBytes = 2 * kOperandBytes;  // Q and P
-constexpr int kLdsBytes = 2 * kStageBytes;      // two stages: 128 KiB
+constexpr int kStages = 5;                      // 160 KiB of LDS
+constexpr int kLdsBytes = kStages * kStageBytes;
+constexpr int kCopiesPerStep = 8;               // buffer->LDS copies per wave per step
 
 enum Epi { EPI_LP = 0, EPI_F32 = 1, EPI_GELU = 2, EPI_ACC = 3 };
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-// ---- global -> registers ----------------------------------------------------
+__device__ __forceinline__ uint32_t lds_addr(const char *p) { return (uint32_t)(uintptr_t)p; }
 
-// Reduction-contiguous operand: element (r, k) at M[r * ld + k].  Thread t
-// loads chunk (t & 7) of rows (t >> 3) + 32 j, j < 8.  red % 8 == 0, so a
-// 16-byte chunk is entirely inside or entirely outside the reduction range.
-__device__ __forceinline__ void load_rc(const uint16_t *__restrict__ M, int64_t ld, int64_t r0,
-                                        int64_t rext, int64_t k0, int64_t red, int tid,
-                                        u32x4 (&v)[8]) {
-    const int c = tid & 7;
-    const int rb = tid >> 3;
-    const int64_t k = k0 + c * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int64_t r = r0 + rb + 32 * j;
-        if (r < rext && k < red)
-            v[j] = *reinterpret_cast<const u32x4 *>(M + r * ld + k);
-        else
-            v[j] = u32x4{0u, 0u, 0u, 0u};
-    }
+// ---- global -> LDS copies -------------------------------------------------------
+//
+// Reads go through raw buffer descriptors.  A lane whose element lies outside
+// the operand gets the offset kOOB, past the descriptor's range; the buffer
+// unit returns zeros for it, so ragged edges need no branches.
+
+constexpr uint32_t kNumRecords = 0x40000000u;  // bytes covered by a descriptor
+constexpr uint32_t kOOB = 0x40000000u;         // lane offset outside that range
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw 32-bit buffer, gfx9 layout
+
+typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor: 48-bit base, stride 0, kNumRecords bytes.
+__device__ __forceinline__ rsrc_t make_rsrc(const char *base) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    return rsrc_t{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, kNumRecords, kRsrcWord3};
 }
 
-// Reduction-strided operand: element (r, k) at M[k * ld + r].  Thread t loads
-// the 8 x 8 block of reduction rows 8 (t >> 5) .. +7 and elements
-// r0 + 8 (t & 31) .. +7; rext % 8 == 0.
-__device__ __forceinline__ void load_rs(const uint16_t *__restrict__ M, int64_t ld, int64_t r0,
-                                        int64_t rext, int64_t k0, int64_t red, int tid,
-                                        u32x4 (&v)[8]) {
-    const int rg = tid & 31;
-    const int kg = tid >> 5;
-    const int64_t r = r0 + rg * 8;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int64_t k = k0 + kg * 8 + q;
-        if (r < rext && k < red)
-            v[q] = *reinterpret_cast<const u32x4 *>(M + k * ld + r);
-        else
-            v[q] = u32x4{0u, 0u, 0u, 0u};
-    }
+// One 16-byte-per-lane copy global -> LDS at lds_block + 16 * lane.  Written as
+// inline assembly so that the compiler's wait-count pass, which cannot tell
+// LDS stages apart, does not drain every copy in flight before each LDS read;
+// completion is awaited explicitly (wait_and_barrier) before a stage is read.
+__device__ __forceinline__ void copy16(rsrc_t rs, char *lds_block, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_block));
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(m0), "v"(voff), "s"(rs)
+        : "memory", "m0");
 }
 
-// ---- registers -> LDS --------------------------------------------------------
+// Copy j (0..3) of wave w fills bytes [(4 w + j) * 1 KiB, +1 KiB) of an
+// operand's stage; lane l writes the 16 bytes at offset 16 l of that block.
 
-__device__ __forceinline__ void store_rc(char *lds, int tid, const u32x4 (&v)[8]) {
-    const int c = tid & 7;
-    const int rb = tid >> 3;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int row = rb + 32 * j;
-        *reinterpret_cast<u32x4 *>(lds + row * kRowBytes + ((c ^ swz(row)) << 4)) = v[j];
-    }
-}
+// Reduction-contiguous operand, element (r, k) at M[r * ld + k].
+struct RcOperand {
+    const char *base;  // &M[r0 * ld]
+    uint32_t voff[4];  // per-lane byte offsets of the 4 copies (kOOB past the row extent)
 
-// Transpose the thread's 8 x 8 block (v[q] = reduction row q, 8 elements) into
-// 8 rows of 8 reduction values and write each as chunk (t >> 5) of its row.
-__device__ __forceinline__ void store_rs(char *lds, int tid, const u32x4 (&v)[8]) {
-    const int rg = tid & 31;
-    const int kg = tid >> 5;
+    __device__ __forceinline__ static int chunk_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+    __device__ __forceinline__ void init(const uint16_t *M, int64_t ld, int64_t r0, int64_t rext,
+                                         int wave, int lane) {
+        base = reinterpret_cast<const char *>(M + r0 * ld);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        u32x4 u;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t lo = v[2 * p][c >> 1];
-            const uint32_t hi = v[2 * p + 1][c >> 1];
-            u[p] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        for (int j = 0; j < 4; ++j) {
+            const int pos = (wave * 4 + j) * 1024 + lane * 16;
+            const int r = pos >> 6;                     // 64 B per LDS row
+            const int c = chunk_pos(r, (pos >> 4) & 3);  // logical chunk (the map is an involution)
+            voff[j] = (r0 + r < rext) ? (uint32_t)((r * ld + c * 8) * 2) : kOOB;
         }
-        const int row = rg * 8 + c;
-        *reinterpret_cast<u32x4 *>(lds + row * kRowBytes + ((kg ^ swz(row)) << 4)) = u;
     }
-}
 
-__device__ __forceinline__ u32x4 lds_frag(const char *lds, int row, int chunk) {
-    return *reinterpret_cast<const u32x4 *>(lds + row * kRowBytes + ((chunk ^ swz(row)) << 4));
+    __device__ __forceinline__ void issue(char *stage, int64_t k0, int64_t red, int wave, int lane) {
+        const rsrc_t rs = make_rsrc(base + k0 * 2);
+        if (k0 + BK <= red) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) copy16(rs, stage + (wave * 4 + j) * 1024, voff[j]);
+        } else {  // last, ragged step: chunks past the reduction length read as zero
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int pos = (wave * 4 + j) * 1024 + lane * 16;
+                const int c = chunk_pos(pos >> 6, (pos >> 4) & 3);
+                copy16(rs, stage + (wave * 4 + j) * 1024, (k0 + c * 8 < red) ? voff[j] : kOOB);
+            }
+        }
+    }
+
+    // Fragment of rows rbase .. rbase+31, reduction values 16 ks + 8 (lane >> 5) .. +7.
+    __device__ __forceinline__ static u32x4 frag(const char *stage, int rbase, int ks, int lane) {
+        const int r = rbase + (lane & 31);
+        const int c = ks * 2 + (lane >> 5);
+        return *reinterpret_cast<const u32x4 *>(stage + r * 64 + (chunk_pos(r, c) << 4));
+    }
+};
+
+// Reduction-strided operand, element (r, k) at M[k * ld + r].
+struct RsOperand {
+    const char *base;  // &M[r0]
+    int64_t ldb;       // ld in bytes
+    uint32_t voff[4];
+
+    __device__ __forceinline__ static int seg_pos(int k, int s) { return s ^ ((k & 3) << 1); }
+
+    __device__ __forceinline__ void init(const uint16_t *M, int64_t ld, int64_t r0, int64_t rext,
+                                         int wave, int lane) {
+        base = reinterpret_cast<const char *>(M + r0);
+        ldb = ld * 2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int pos = (wave * 4 + j) * 1024 + lane * 16;
+            const int k = pos >> 9;                          // 512 B per LDS row
+            const int s = seg_pos(k, (pos >> 5) & 15);       // logical 32-byte segment
+            const int r = s * 16 + ((pos >> 4) & 1) * 8;     // first of 8 elements
+            voff[j] = (r0 + r < rext) ? (uint32_t)(k * ldb + r * 2) : kOOB;  // rext % 8 == 0
+        }
+    }
+
+    __device__ __forceinline__ void issue(char *stage, int64_t k0, int64_t red, int wave, int lane) {
+        const rsrc_t rs = make_rsrc(base + k0 * ldb);
+        if (k0 + BK <= red) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) copy16(rs, stage + (wave * 4 + j) * 1024, voff[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int k = ((wave * 4 + j) * 1024 + lane * 16) >> 9;
+                copy16(rs, stage + (wave * 4 + j) * 1024, (k0 + k < red) ? voff[j] : kOOB);
+            }
+        }
+    }
+
+    // Fragment of columns rbase .. rbase+31 (rbase % 32 == 0), reduction values
+    // 16 ks + 8 (lane >> 5) .. +7: two transposing reads of 4 values each.
+    __device__ __forceinline__ static u32x4 frag(const char *stage, int rbase, int ks, int lane) {
+        const int h = lane >> 4;
+        const int s = lane & 15;
+        const int r = rbase + 16 * (h & 1) + 4 * (s & 3);
+        u32x4 out;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int k = 16 * ks + 8 * (h >> 1) + 4 * t + (s >> 2);
+            const char *p = stage + k * 512 + (seg_pos(k, r >> 4) << 5) + (r & 15) * 2;
+            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(uintptr_t)lds_addr(p));
+            const u32x2 w = __builtin_bit_cast(u32x2, v);
+            out[2 * t] = w[0];
+            out[2 * t + 1] = w[1];
+        }
+        return out;
+    }
+};
+
+// Wait until at most `n` buffer->LDS copies of this wave are in flight and all
+// its LDS reads have returned, then meet the other waves.
+template <int n>
+__device__ __forceinline__ void wait_and_barrier() {
+    if constexpr (n == 0)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (n == kCopiesPerStep)
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (n == 2 * kCopiesPerStep)
+        asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (n == 3 * kCopiesPerStep)
+        asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (n == 4 * kCopiesPerStep)
+        asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        static_assert(n == 0, "unsupported in-flight count");
 }
 
 // ---- MFMA ------------------------------------------------------------------------
@@ -196,14 +287,17 @@ __device__ __forceinline__ void tile_coords(int w, int tiles_p, int tiles_q, int
 
 // ---- the GEMM ---------------------------------------------------------------------
 
+template <bool RS>
+using OperandT = typename std::conditional<RS, RsOperand, RcOperand>::type;
+
 template <typename T, bool Q_RS, bool P_RS, int EPI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
-    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wq = wave & 1;
     const int wp = wave >> 1;
 
@@ -212,8 +306,30 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     const int64_t p0 = (int64_t)tp * 256;
     const int64_t q0 = (int64_t)tq * 256;
 
-    const uint16_t *__restrict__ Q = static_cast<const uint16_t *>(a.Q);
-    const uint16_t *__restrict__ P = static_cast<const uint16_t *>(a.P);
+    OperandT<Q_RS> qo;
+    OperandT<P_RS> po;
+    qo.init(static_cast<const uint16_t *>(a.Q), a.ldq, q0, a.cols, wave, lane);
+    po.init(static_cast<const uint16_t *>(a.P), a.ldp, p0, a.rows, wave, lane);
+
+    const int64_t ksteps = (a.red + BK - 1) / BK;
+    auto stage_of = [&](int64_t kt) -> char * { return lds + (int)(kt % kStages) * kStageBytes; };
+    auto issue = [&](int64_t kt) {
+        char *st = stage_of(kt);
+        qo.issue(st, kt * BK, a.red, wave, lane);
+        po.issue(st + kOperandBytes, kt * BK, a.red, wave, lane);
+    };
+
+    // Fragments of substep ks (16 reduction values) of a stage: the wave's
+    // 4 q-blocks and 4 p-blocks.
+    u32x4 fa[2][4], fb[2][4];
+    auto frags = [&](const char *st, int ks, u32x4 (&xa)[4], u32x4 (&xb)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xa[i] = OperandT<Q_RS>::frag(st, wq * 128 + i * 32, ks, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            xb[j] = OperandT<P_RS>::frag(st + kOperandBytes, wp * 128 + j * 32, ks, lane);
+    };
+    constexpr int kReads = (Q_RS ? 8 : 4) + (P_RS ? 8 : 4);  // LDS read instructions per substep
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -221,62 +337,62 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-    u32x4 vq[8], vp[8];
-    const int64_t ksteps = (a.red + BK - 1) / BK;
-
-    auto load = [&](int64_t k0) {
-        if constexpr (Q_RS)
-            load_rs(Q, a.ldq, q0, a.cols, k0, a.red, tid, vq);
-        else
-            load_rc(Q, a.ldq, q0, a.cols, k0, a.red, tid, vq);
-        if constexpr (P_RS)
-            load_rs(P, a.ldp, p0, a.rows, k0, a.red, tid, vp);
-        else
-            load_rc(P, a.ldp, p0, a.rows, k0, a.red, tid, vp);
+    auto mma = [&](const u32x4 (&xa)[4], const u32x4 (&xb)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32<T>(xa[i], xb[j], acc[i][j]);
     };
-    auto store = [&](char *stage) {
-        if constexpr (Q_RS)
-            store_rs(stage, tid, vq);
-        else
-            store_rc(stage, tid, vq);
-        if constexpr (P_RS)
-            store_rs(stage + kOperandBytes, tid, vp);
-        else
-            store_rc(stage + kOperandBytes, tid, vp);
-    };
-
-    load(0);
-    store(lds);
-    __syncthreads();
-
-    const int frow = lane & 31;
-    const int fhalf = lane >> 5;
-    for (int64_t kt = 0; kt < ksteps; ++kt) {
-        const char *cur = lds + (kt & 1) * kStageBytes;
-        const bool more = kt + 1 < ksteps;
-        if (more) load((kt + 1) * BK);
+    // one LDS read, then one MFMA, for the first kReads MFMAs of a substep
+    auto interleave = [&]() {
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int chunk = ks * 2 + fhalf;
-            u32x4 fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) fa[i] = lds_frag(cur, wq * 128 + i * 32 + frow, chunk);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                fb[j] = lds_frag(cur + kOperandBytes, wp * 128 + j * 32 + frow, chunk);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32<T>(fa[i], fb[j], acc[i][j]);
+        for (int g = 0; g < kReads; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        if (more) store(lds + ((kt + 1) & 1) * kStageBytes);
-        __syncthreads();
+        __builtin_amdgcn_sched_group_barrier(0x008, 16 - kReads, 0);
+    };
+
+    // prologue: kStages steps in flight, wait for the first
+#pragma unroll
+    for (int s = 0; s < kStages; ++s)
+        if (s < ksteps) issue(s);
+    if (ksteps >= kStages)
+        wait_and_barrier<(kStages - 1) * kCopiesPerStep>();
+    else
+        wait_and_barrier<0>();
+    frags(stage_of(0), 0, fa[0], fb[0]);
+
+    for (int64_t kt = 0; kt + 1 < ksteps; ++kt) {
+        // substep 0 of step kt; the fragments of substep 1 are read under it
+        frags(stage_of(kt), 1, fa[1], fb[1]);
+        mma(fa[0], fb[0]);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        // every wave has read all of step kt: once step kt + 1 has landed,
+        // recycle step kt's stage for step kt + kStages
+        if (ksteps - 2 - kt >= kStages - 2)
+            wait_and_barrier<(kStages - 2) * kCopiesPerStep>();
+        else
+            wait_and_barrier<0>();
+        if (kt + kStages < ksteps) issue(kt + kStages);
+        __builtin_amdgcn_sched_barrier(0);
+        // substep 1 of step kt; substep 0 of step kt + 1 is read under it
+        frags(stage_of(kt + 1), 0, fa[0], fb[0]);
+        mma(fa[1], fb[1]);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
     }
+    // last step: nothing left to copy
+    frags(stage_of(ksteps - 1), 1, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    interleave();
+    mma(fa[1], fb[1]);
 
     // Epilogue.  Accumulator register 4g + e of block (i, j) holds
     // C[p][q] with p = j-block row (lane & 31) and q = 8 g + 4 (lane >> 5) + e.
-    const int64_t pb = p0 + wp * 128 + frow;
-    const int64_t qb = q0 + wq * 128 + 4 * fhalf;
+    const int64_t pb = p0 + wp * 128 + (lane & 31);
+    const int64_t qb = q0 + wq * 128 + 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll

@@ -32,9 +32,10 @@ zi_status plan_validate_and_fill(const zi_problem *p, zi_plan_info *info) {
     if (p->K % 8) return fail(ZI_ERR_SHAPE, "K = %lld is not a multiple of 8", (long long)p->K);
     const int64_t n = p->M / p->N;
     if (n % 8) return fail(ZI_ERR_SHAPE, "tile width n = M/N = %lld is not a multiple of 8", (long long)n);
-    // 32-bit tile indices inside the kernels: keep every extent well inside int
-    if (p->T > (int64_t)1 << 30 || p->K > (int64_t)1 << 30 || p->M > (int64_t)1 << 34)
-        return fail(ZI_ERR_SHAPE, "extent too large");
+    // The kernels address a 256-row panel of any operand with 32-bit offsets
+    // below 1 GiB (256 rows x ld x 2 B), and count tiles in int.
+    if (p->T > (int64_t)1 << 30 || p->K > (int64_t)1 << 21 || p->M > (int64_t)1 << 21)
+        return fail(ZI_ERR_SHAPE, "extent too large (T <= 2^30, K and M <= 2^21)");
 
     const bool f32 = (p->flags & ZI_FLAG_F32_OUT) != 0;
     const uint64_t tile = (uint64_t)p->K * (uint64_t)n * 2u;
