@@ -1,0 +1,201 @@
+"""GPU parity at the workloads' full sizes, on sampled outputs.
+
+Each case runs the whole tiled pass through the C ABI at its real shape and
+launch configuration, then compares sampled entries (random rows and columns
+plus every tile-boundary column and the first and last row) with the oracle,
+which computes each sampled entry as a full-length dot product.  Tolerance:
+max |gpu - ref| <= 2e-3 * max |ref| over the sample; bf16 is compared on the
+kernels' fp32 epilogue and its 16-bit results must be one RNE rounding of it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from offload_memory_centric_amd import inputs
+from zi_testlib import TOL, assert_close, host_bits, lib, sample_indices, say, tile_edges
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def release_pinned():
+    """Free the pinned buffers of earlier cases before a large allocation."""
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def big_linear(T, K, M, N, d, dtype, seed, f32_out=False, budget=0, chunk_rows=4096):
+    tiling = lib()
+    X = inputs.new((T, K), dtype, "gaussian", seed, "X", device="cuda")
+    dY = inputs.new((T, M), dtype, "gaussian", seed, "dY", device="cuda")
+    Wt = tiling.host_tensor((M, K), inputs.torch_dtype(dtype))
+    inputs.fill_(Wt, "gaussian", seed, "W", std=0.02, device="cuda", chunk_rows=chunk_rows)
+    return X, Wt, dY
+
+
+def run_pass(T, K, M, N, d, dtype, X, Wt, dY, f32_out=False, budget=0):
+    tiling = lib()
+    elem = torch.float32 if f32_out else inputs.torch_dtype(dtype)
+    dWt = tiling.host_tensor((M, K), elem)
+    plan = tiling.Plan(T, K, M, N, d, dtype, Wt, dWt, budget=budget, f32_out=f32_out)
+    ctx = tiling.Context(plan)
+    Y = torch.empty((T, M), dtype=elem, device="cuda")
+    dX = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    ctx.fwd(plan, X, Y)
+    ctx.bwd(plan, X, dY, dX)
+    ctx.sync()
+    info = plan.info
+    ctx.close()
+    plan.close()
+    return Y, dX, dWt, info
+
+
+def sampled_parity(T, K, M, N, dtype, X, Wt, dY, Y, dX, dWt, seed, tol=TOL):
+    n = M // N
+    rows = sample_indices(T, 64, seed)
+    cols = sample_indices(M, 64, seed + 1, must=tile_edges(M, n))
+    kcols = sample_indices(K, 64, seed + 2)
+    Xb, Wb, dYb = host_bits(X), host_bits(Wt), host_bits(dY)
+    ref_y = oracle.linear_fwd_sample(Xb, Wb, rows, cols, dtype)
+    ref_dx = oracle.linear_dx_sample(Wb, dYb, rows, kcols, dtype)
+    ref_dw = oracle.linear_dw_sample(Xb, dYb, cols, kcols, dtype)
+    rt, ct, kt = (torch.as_tensor(v, device=Y.device) for v in (rows, cols, kcols))
+    gy = Y[rt][:, ct]
+    gdx = dX[rt][:, kt]
+    gdw = dWt[torch.as_tensor(cols)][:, torch.as_tensor(kcols)]
+
+    def vals(t):
+        t = t.float().cpu() if t.dtype != torch.float32 else t.cpu()
+        return t.numpy().astype(np.float64)
+
+    assert_close(vals(gy), ref_y, "Y", tol)
+    assert_close(vals(gdx), ref_dx, "dX", tol)
+    assert_close(vals(gdw), ref_dw, "dW", tol)
+
+
+def test_extreme_width_layer():
+    # hd = 65536 -> 262144: W and dW 32 GiB each in pinned host memory,
+    # N = 16 tiles of 2 GiB, T = 2048, d = 2
+    T, K, M, N, d = 2048, 65536, 262144, 16, 2
+    say("case extreme width: allocating 64 GiB pinned")
+    release_pinned()
+    from offload_memory_centric_amd import zi
+    try:
+        X, Wt, dY = big_linear(T, K, M, N, d, "f16", seed=2, chunk_rows=8192)
+        Y, dX, dWt, info = run_pass(T, K, M, N, d, "f16", X, Wt, dY)
+    except zi.ZiError as e:
+        if "out of memory" in str(e):
+            pytest.skip("the host could not pin 64 GiB for W and dW (%s)" % e)
+        raise
+    assert info.tile_bytes == 2 ** 31
+    say("case extreme width: sampled parity")
+    sampled_parity(T, K, M, N, "f16", X, Wt, dY, Y, dX, dWt, seed=300)
+
+
+def test_mid_ffn_up_projection_bf16():
+    # X[4096x8192], W[8192x32768] bf16 (0.5 GB) pinned, N = 8 tiles of 4096, d = 2
+    T, K, M, N, d = 4096, 8192, 32768, 8, 2
+    say("case mid-ffn bf16 fp32-epilogue")
+    release_pinned()
+    X, Wt, dY = big_linear(T, K, M, N, d, "bf16", seed=0)
+    Y32, dX32, dW32, _ = run_pass(T, K, M, N, d, "bf16", X, Wt, dY, f32_out=True)
+    sampled_parity(T, K, M, N, "bf16", X, Wt, dY, Y32, dX32, dW32, seed=100)
+    say("case mid-ffn bf16 16-bit outputs")
+    Y16, dX16, dW16, _ = run_pass(T, K, M, N, d, "bf16", X, Wt, dY)
+    assert torch.equal(Y16, Y32.to(torch.bfloat16)), "Y16 is not RNE(Y32)"
+    assert torch.equal(dX16, dX32)
+    assert torch.equal(dW16, dW32.to(torch.bfloat16)), "dW16 is not RNE(dW32)"
+
+
+def test_ffn_first_matrix_two_tile_budget():
+    # W[25600x102400] fp16 (5.2 GB) pinned, N = 16 tiles of 6400 columns,
+    # T = 4096; device tile budget = two tiles; d in {1, 2, 3}
+    T, K, M, N = 4096, 25600, 102400, 16
+    tile = K * (M // N) * 2
+    from offload_memory_centric_amd import zi
+    tiling = lib()
+    say("case 1T-ffn budget: d=3 rejected")
+    release_pinned()
+    X, Wt, dY = big_linear(T, K, M, N, 2, "f16", seed=1)
+    with pytest.raises(zi.ZiError) as e:
+        tiling.Plan(T, K, M, N, 3, "f16", Wt, tiling.host_tensor((8, 8), torch.float16), budget=2 * tile)
+    assert e.value.status == zi.ZI_ERR_BUDGET
+    say("case 1T-ffn budget d=2")
+    Y2, dX2, dW2, info2 = run_pass(T, K, M, N, 2, "f16", X, Wt, dY, budget=2 * tile)
+    assert info2.ring_bytes == 2 * tile and info2.dw_slots == 0
+    sampled_parity(T, K, M, N, "f16", X, Wt, dY, Y2, dX2, dW2, seed=200)
+    say("case 1T-ffn budget d=1")
+    Y1, dX1, dW1, info1 = run_pass(T, K, M, N, 1, "f16", X, Wt, dY, budget=2 * tile)
+    assert info1.ring_bytes <= 2 * tile
+    # same kernels, same tile order: the depth changes only the overlap
+    assert torch.equal(Y1, Y2) and torch.equal(dX1, dX2) and torch.equal(dW1, dW2)
+
+
+def ffn_case(T, seed, nt=8, nf=16):
+    D, F, N1, N2, d = 25600, 102400, 16, 16, 2
+    release_pinned()
+    tiling = lib()
+    tdt = torch.float16
+    X = inputs.new((T, D), "f16", "gaussian", seed, "X", device="cuda")
+    dY = inputs.new((T, D), "f16", "gaussian", seed, "dY", device="cuda")
+    W1t = tiling.host_tensor((F, D), tdt)
+    W2t = tiling.host_tensor((D, F), tdt)
+    inputs.fill_(W1t, "gaussian", seed, "W1", std=0.02, device="cuda", chunk_rows=4096)
+    inputs.fill_(W2t, "gaussian", seed, "W2", std=0.02, device="cuda", chunk_rows=1024)
+    dW1t = tiling.host_tensor((F, D), tdt)
+    dW2t = tiling.host_tensor((D, F), tdt)
+    p1 = tiling.Plan(T, D, F, N1, d, "f16", W1t, dW1t)
+    p2 = tiling.Plan(T, F, D, N2, d, "f16", W2t, dW2t)
+    ctx = tiling.Context(p1 if p1.info.ring_bytes >= p2.info.ring_bytes else p2)
+    A = torch.empty((T, F), dtype=tdt, device="cuda")
+    H = torch.empty_like(A)
+    dA = torch.empty_like(A)
+    dH = torch.empty((T, F), dtype=torch.float32, device="cuda")
+    Y = torch.empty((T, D), dtype=tdt, device="cuda")
+    Yr = torch.empty_like(Y)
+    dX = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    say("  forward W1+GeLU (kept for the recompute check)")
+    ctx.fwd_gelu(p1, X, A, H)
+    ctx.sync()
+    A0, H0 = A.clone(), H.clone()
+    say("  full block step")
+    tiling.ffn_block_step(ctx, p1, p2, X, A, H, Y, dY, dH, dA, dX, Yr)
+    ctx.sync()
+    assert torch.equal(A, A0) and torch.equal(H, H0), "recomputed activations differ"
+    assert torch.equal(Y, Yr), "recomputed W2 product differs"
+    say("  oracle on samples")
+    t_rows = sample_indices(T, nt - 2, seed + 10)
+    f_cols = sample_indices(F, nf - 2, seed + 11, must=[6400 - 1, 6400, F - 6400])
+    d2_cols = sample_indices(D, nf - 2, seed + 12, must=[1600 - 1, 1600, D - 1600])
+    d_cols = sample_indices(D, nf - 2, seed + 13)
+    ref = oracle.ffn_sample(host_bits(X), host_bits(W1t), host_bits(W2t), host_bits(dY), "f16",
+                            t_rows, f_cols, d2_cols, d_cols, chunk=4096)
+    tr, fc, d2c, dc = (torch.as_tensor(v) for v in (t_rows, f_cols, d2_cols, d_cols))
+
+    def pick(t, r, c):
+        return t[r.to(t.device)][:, c.to(t.device)].float().cpu().numpy().astype(np.float64)
+
+    assert_close(pick(A, tr, fc), ref["A"], "A")
+    assert_close(pick(H, tr, fc), ref["H"], "H")
+    assert_close(pick(Y, tr, d2c), ref["Y"], "Y")
+    assert_close(pick(dH, tr, fc), ref["dH"], "dH")
+    assert_close(pick(dA, tr, fc), ref["dA"], "dA")
+    assert_close(pick(dX, tr, dc), ref["dX"], "dX")
+    assert_close(pick(dW1t, fc, dc), ref["dW1t"], "dW1")
+    assert_close(pick(dW2t, d2c, fc), ref["dW2t"], "dW2")
+    ctx.close()
+
+
+def test_ffn_block_T512():
+    say("case ffn block T=512")
+    ffn_case(512, seed=40)
+
+
+def test_ffn_block_T32768_bench_configuration():
+    # the benchmark's own configuration: T = 32768, N = 16 + 16, d = 2
+    say("case ffn block T=32768")
+    ffn_case(32768, seed=50, nt=6, nf=10)
