@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-link-peak", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--d2h-cus", type=int, default=None,
+                    help="compute units of the device-to-host copy stream (0: unrestricted)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain streaming kernel of known size (HBM counter calibration)")
     return ap.parse_args()
@@ -164,6 +166,7 @@ def main():
     d = args.d
     seed = 0
 
+    ctx_kw = {} if args.d2h_cus is None else {"d2h_cus": args.d2h_cus}
     link = None if args.no_link_peak else link_peak(torch, tiling)
     if link:
         log("link peak", link)
@@ -184,7 +187,7 @@ def main():
         dW2t = tiling.host_tensor((D, F), tdt)
         p1 = tiling.Plan(T, D, F, N1, d, dtype, W1t, dW1t)
         p2 = tiling.Plan(T, F, D, N2, d, dtype, W2t, dW2t)
-        ctx = tiling.Context(p1 if p1.info.ring_bytes >= p2.info.ring_bytes else p2)
+        ctx = tiling.Context(p1 if p1.info.ring_bytes >= p2.info.ring_bytes else p2, **ctx_kw)
         A = torch.empty((T, F), dtype=tdt, device="cuda")
         H = torch.empty_like(A)
         dA = torch.empty_like(A)
@@ -214,7 +217,7 @@ def main():
         inputs.fill_(Wt, "gaussian", seed, "W", std=0.02, device="cuda", chunk_rows=4096)
         dWt = tiling.host_tensor((M, K), tdt)
         p = tiling.Plan(T, K, M, N, d, dtype, Wt, dWt)
-        ctx = tiling.Context(p)
+        ctx = tiling.Context(p, **ctx_kw)
         Y = torch.empty((T, M), dtype=tdt, device="cuda")
         dX = torch.empty((T, K), dtype=torch.float32, device="cuda")
         flops_step = 6.0 * T * K * M

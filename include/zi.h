@@ -216,6 +216,21 @@ zi_status zi_ctx_set_timing(zi_ctx *ctx, int32_t enable);
 zi_status zi_ctx_reset_stats(zi_ctx *ctx);
 zi_status zi_ctx_stats(zi_ctx *ctx, zi_stats *out);
 
+/* A stream for the device-to-host copies whose work is confined to `n_cus`
+ * compute units: the mask enables the lowest n_cus CU indices, which the HIP
+ * runtime spreads round-robin over the XCCs, and it needs some in each, so
+ * n_cus must be a positive multiple of the XCC count (8 on MI355X), at most
+ * the CU count; ZI_ERR_ARG otherwise.
+ * The HIP runtime may carry out a device-to-host hipMemcpyAsync as a copy
+ * kernel on the stream's queue instead of a DMA engine; such a kernel's
+ * workgroups occupy compute units for as long as the copy waits on the host
+ * link, and a product kernel whose workgroup needs a whole compute unit
+ * cannot start there meanwhile.  Confining the copy stream to a few compute
+ * units bounds that loss.  Default priority.  The stream is owned by the
+ * caller: release it with zi_stream_destroy after its last use. */
+zi_status zi_copy_stream_create(int32_t n_cus, void **out);
+zi_status zi_stream_destroy(void *stream);
+
 /* Page-locked host memory (hipHostMalloc) for W^t / dW^t; 4096-byte aligned. */
 zi_status zi_host_alloc(uint64_t bytes, void **out);
 zi_status zi_host_free(void *ptr);

@@ -381,6 +381,34 @@ zi_status zi_host_alloc(uint64_t bytes, void **out) {
     return ZI_OK;
 }
 
+zi_status zi_copy_stream_create(int32_t n_cus, void **out) {
+    clear_error();
+    if (!out) return fail(ZI_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    if (n_cus < 1) return fail(ZI_ERR_ARG, "n_cus = %d must be at least 1", n_cus);
+    int dev = 0, cus = 0, xccs = 1;
+    HIPCHK(nullptr, hipGetDevice(&dev));
+    HIPCHK(nullptr, hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    HIPCHK(nullptr, hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, dev));
+    if (xccs < 1) xccs = 1;
+    if (n_cus > cus || n_cus % xccs)
+        return fail(ZI_ERR_ARG, "n_cus = %d must be a multiple of the %d XCCs, at most %d", n_cus, xccs,
+                    cus);
+    std::vector<uint32_t> mask((size_t)(cus + 31) / 32, 0u);
+    for (int i = 0; i < n_cus; ++i) mask[(size_t)i / 32] |= 1u << (i % 32);
+    hipStream_t s = nullptr;
+    HIPCHK(nullptr, hipExtStreamCreateWithCUMask(&s, (uint32_t)mask.size(), mask.data()));
+    *out = s;
+    return ZI_OK;
+}
+
+zi_status zi_stream_destroy(void *stream) {
+    clear_error();
+    if (!stream) return ZI_OK;
+    HIPCHK(nullptr, hipStreamDestroy(static_cast<hipStream_t>(stream)));
+    return ZI_OK;
+}
+
 zi_status zi_host_free(void *ptr) {
     clear_error();
     if (!ptr) return ZI_OK;

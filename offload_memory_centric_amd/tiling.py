@@ -89,16 +89,31 @@ def _out(plan) -> tuple:
     return (torch.float32,) if plan.f32_out else _lp(plan)
 
 
+# Compute units the device-to-host copy stream may use (see zi_copy_stream_create).
+D2H_CUS = 8
+
+
 class Context:
-    """The ring over a torch-allocated workspace and three torch streams."""
+    """The ring over a torch-allocated workspace and three streams.
+
+    By default the products and the host-to-device copies run on torch streams
+    and the device-to-host copies on a library stream confined to ``d2h_cus``
+    compute units (0: a torch stream as well).
+    """
 
     def __init__(self, plan: Plan, device: str = "cuda", workspace_bytes: Optional[int] = None,
-                 streams=None):
+                 streams=None, d2h_cus: int = D2H_CUS):
         nbytes = int(workspace_bytes if workspace_bytes is not None else plan.info.ring_bytes)
+        self.handle = None
+        self._own_stream = None
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         if streams is None:
-            streams = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device),
-                       torch.cuda.Stream(device=device))
+            if d2h_cus:
+                self._own_stream = zi.zi_copy_stream_create(d2h_cus)
+                d2h = self._own_stream
+            else:
+                d2h = torch.cuda.Stream(device=device)
+            streams = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device), d2h)
         self.streams = streams
         self.handle = zi.zi_ctx_create(plan.handle, self.workspace, nbytes, *streams)
 
@@ -154,6 +169,9 @@ class Context:
         if self.handle:
             zi.zi_ctx_destroy(self.handle)
             self.handle = None
+        if self._own_stream:
+            zi.zi_stream_destroy(self._own_stream)
+            self._own_stream = None
 
     def __del__(self):
         try:

@@ -97,6 +97,8 @@ _sigs = {
     "zi_ctx_set_timing": (_S, [_P, ctypes.c_int32]),
     "zi_ctx_reset_stats": (_S, [_P]),
     "zi_ctx_stats": (_S, [_P, ctypes.POINTER(zi_stats)]),
+    "zi_copy_stream_create": (_S, [ctypes.c_int32, ctypes.POINTER(_P)]),
+    "zi_stream_destroy": (_S, [_P]),
     "zi_host_alloc": (_S, [ctypes.c_uint64, ctypes.POINTER(_P)]),
     "zi_host_free": (_S, [_P]),
     "zi_last_error": (ctypes.c_char_p, []),
@@ -195,6 +197,16 @@ def zi_tiled_linear_bwd_recompute(ctx, plan, X, dY, dX, Yr) -> None:
 
 def zi_gelu_bwd(ctx, dtype: int, dH, A, dA, count: int) -> None:
     _check(_lib.zi_gelu_bwd(ctx, int(dtype), _ptr(dH), _ptr(A), _ptr(dA), int(count)))
+
+
+def zi_copy_stream_create(n_cus: int) -> int:
+    h = _P()
+    _check(_lib.zi_copy_stream_create(int(n_cus), ctypes.byref(h)))
+    return h.value
+
+
+def zi_stream_destroy(stream) -> None:
+    _check(_lib.zi_stream_destroy(_stream(stream)))
 
 
 def zi_sync(ctx) -> None:

@@ -14,12 +14,12 @@ from zi_testlib import (assert_close, host_bits, lib, make_linear_inputs, say, v
 pytestmark = pytest.mark.gpu
 
 
-def run_fwd_bwd(T, K, M, N, d, dtype, X, Wt, dY, f32_out=False, budget=0, want_bwd=True):
+def run_fwd_bwd(T, K, M, N, d, dtype, X, Wt, dY, f32_out=False, budget=0, want_bwd=True, **ctx_kw):
     tiling = lib()
     elem = torch.float32 if f32_out else inputs.torch_dtype(dtype)
     dWt = tiling.host_tensor((M, K), elem) if want_bwd else None
     plan = tiling.Plan(T, K, M, N, d, dtype, Wt, dWt, budget=budget, f32_out=f32_out)
-    ctx = tiling.Context(plan)
+    ctx = tiling.Context(plan, **ctx_kw)
     Y = torch.empty((T, M), dtype=elem, device="cuda")
     dX = torch.empty((T, K), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
@@ -190,6 +190,33 @@ def test_gradient_in_weight_slot_matches_separate_slots():
     assert torch.equal(sep["Y"], ins["Y"])
     assert torch.equal(sep["dX"], ins["dX"])
     assert torch.equal(sep["dWt"], ins["dWt"])
+
+
+@pytest.mark.parametrize("d2h_cus", [0, 8, 32])
+def test_device_to_host_stream_confinement(d2h_cus):
+    # the dW write-back stream confined to 8 or 32 compute units, or a plain
+    # torch stream (0): the same exact results
+    T, K, M, N, d = 128, 512, 2048, 4, 2
+    say("case d2h stream cus", d2h_cus)
+    X, Wt, dY = make_linear_inputs(T, K, M, "f16", "small_int", seed=6)
+    r = run_fwd_bwd(T, K, M, N, d, "f16", X, Wt, dY, d2h_cus=d2h_cus)
+    Y, dX, dWt = oracle_linear(X, Wt, dY, "f16")
+    assert np.array_equal(host_bits(r["Y"]), oracle.encode(Y, "f16"))
+    assert np.array_equal(r["dX"].cpu().numpy().astype(np.float64), dX)
+    assert np.array_equal(host_bits(r["dWt"]), oracle.encode(dWt, "f16"))
+
+
+def test_copy_stream_cu_count_checked():
+    from offload_memory_centric_amd import zi
+    say("case copy stream n_cus range")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for bad in (0, -1, 1, 12, cus + 8):
+        with pytest.raises(zi.ZiError) as e:
+            zi.zi_copy_stream_create(bad)
+        assert e.value.status == zi.ZI_ERR_ARG
+    for good in (8, cus):
+        s = zi.zi_copy_stream_create(good)
+        zi.zi_stream_destroy(s)
 
 
 def test_consecutive_calls_share_the_ring():
