@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--N", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-link-peak", action="store_true")
+    ap.add_argument("--link-peak-only", action="store_true",
+                    help="only measure the host-link peak and print it (run as a child process)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--d2h-cus", type=int, default=None,
@@ -142,12 +144,31 @@ def link_peak(torch, tiling, nbytes=1 << 30, reps=5):
             "duplex_h2d_plus_d2h_GBps": 2 * nbytes / t_both / 1e9, "bytes": nbytes, "reps": reps}
 
 
+def link_peak_in_child():
+    """The host-link peak, measured in a child process started before this one
+    touches the GPU.  Concurrent host-to-device and device-to-host copies on two
+    streams (the duplex figure) were seen to leave the HIP runtime of their
+    process serialising later copies and kernels, so they get a process of
+    their own."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--link-peak-only"],
+                       stdout=subprocess.PIPE, stderr=subprocess.PIPE, timeout=300)
+    if r.returncode != 0:
+        log("link peak child failed:", r.stderr.decode(errors="replace")[-500:])
+        return None
+    return json.loads(r.stdout.decode().strip().splitlines()[-1])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    link = None
+    if not args.no_link_peak and not args.link_peak_only and not args.copy_probe:
+        link = link_peak_in_child()
+        log("link peak", link)
 
     import numpy as np
     import torch
@@ -161,15 +182,15 @@ def main():
     if args.copy_probe:
         copy_probe(torch)
         return
+    if args.link_peak_only:
+        print(json.dumps(link_peak(torch, tiling)), flush=True)
+        return
     dtype = args.dtype or ("f16" if args.workload == "ffn" else "bf16")
     tdt = inputs.torch_dtype(dtype)
     d = args.d
     seed = 0
 
     ctx_kw = {} if args.d2h_cus is None else {"d2h_cus": args.d2h_cus}
-    link = None if args.no_link_peak else link_peak(torch, tiling)
-    if link:
-        log("link peak", link)
 
     # ---------------- workload ----------------
     if args.workload == "ffn":
@@ -335,8 +356,8 @@ def cpu_baseline(args, np, torch, config, env):
         X, dY, W1t, W2t = (_bits(torch, np, env[k]) for k in ("X", "dY", "W1t", "W2t"))
         T, D, F = config["T"], config["d_model"], config["d_ff"]
         rng = np.random.default_rng(0)
-        nt = 1
-        nf = 2
+        nt = 2
+        nf = 4
         t_rows = np.sort(rng.choice(T, nt, replace=False))
         f_cols = np.sort(rng.choice(F, nf, replace=False))
         d2 = np.sort(rng.choice(D, 2, replace=False))

@@ -216,6 +216,15 @@ zi_status zi_ctx_set_timing(zi_ctx *ctx, int32_t enable);
 zi_status zi_ctx_reset_stats(zi_ctx *ctx);
 zi_status zi_ctx_stats(zi_ctx *ctx, zi_stats *out);
 
+/* A new non-blocking stream of default priority, owned by the caller (release
+ * with zi_stream_destroy).  The HIP runtime multiplexes streams onto a few
+ * hardware queues; when the product stream and a copy stream share a queue, a
+ * wait enqueued on the copy stream also holds back the products queued behind
+ * it, and the ring loses its overlap.  Streams created one after another land
+ * on distinct queues, so a context's streams are best created together,
+ * rather than taken from a pool that other code has already drawn from. */
+zi_status zi_stream_create(void **out);
+
 /* A stream for the device-to-host copies whose work is confined to `n_cus`
  * compute units: the mask enables the lowest n_cus CU indices, which the HIP
  * runtime spreads round-robin over the XCCs, and it needs some in each, so

@@ -381,6 +381,16 @@ zi_status zi_host_alloc(uint64_t bytes, void **out) {
     return ZI_OK;
 }
 
+zi_status zi_stream_create(void **out) {
+    clear_error();
+    if (!out) return fail(ZI_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    hipStream_t s = nullptr;
+    HIPCHK(nullptr, hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+    *out = s;
+    return ZI_OK;
+}
+
 zi_status zi_copy_stream_create(int32_t n_cus, void **out) {
     clear_error();
     if (!out) return fail(ZI_ERR_ARG, "out is NULL");

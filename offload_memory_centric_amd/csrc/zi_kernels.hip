@@ -19,15 +19,18 @@
 // Memory pipeline.  With one wave per SIMD nothing hides a wait except work
 // already queued, so global reads must be issued far ahead of their use.  Every
 // operand is copied global -> LDS by the buffer unit (buffer_load ... lds,
-// 16 bytes per lane), which needs no registers, into a ring of kStages LDS
-// stages of BK = 32 reduction elements; the copy of step k + kStages is issued
-// as soon as every wave has finished reading step k, so kStages steps are in
-// flight.  Each step the waves wait only for the step they need next
-// (s_waitcnt vmcnt(N) with N = the copies still allowed in flight), meet at one
-// barrier, and read MFMA fragments from LDS:
-//   * reduction-contiguous operand: rows of 32 reduction values (64 B, four
-//     16-byte chunks); chunk c of row r sits at c ^ ((r >> 2) & 3); a fragment
-//     is one ds_read_b128 per lane;
+// 16 bytes per lane), which needs no registers.  A step covers BK = 64
+// reduction elements; one operand of one step (32 KiB) is a "unit", and the
+// LDS holds a ring of five units (160 KiB): while step k is multiplied, the
+// units of step k + 1 and the first of step k + 2 are in flight, and as soon
+// as every wave has finished reading step k its two slots take the next two
+// units.  Each wave waits only for the units it needs next (s_waitcnt vmcnt(N)
+// with N = the copies still allowed in flight), meets the others at one
+// barrier, and reads MFMA fragments from LDS:
+//   * reduction-contiguous operand: rows of 64 reduction values (128 B, eight
+//     16-byte chunks), so eight lanes fetch one whole 128-byte line of global
+//     memory; chunk c of row r sits at c ^ ((r >> 1) & 7); a fragment is one
+//     ds_read_b128 per lane;
 //   * reduction-strided operand: kept in its natural layout, rows of 256
 //     elements (512 B, sixteen 32-byte segments) per reduction index k;
 //     segment s of row k sits at s ^ 2 (k & 3); a fragment is two
@@ -37,7 +40,9 @@
 //     each lane 4 consecutive reduction values of one column: the MFMA layout.
 // The LDS serves 256 bytes per clock (64 banks of 4 bytes): both layouts let
 // every 16 lanes of a 16-byte read, and every 32 lanes of an 8-byte transposing
-// read, fall on distinct banks.
+// read, fall on distinct banks.  Full 128-byte rows matter: the vector L1
+// sends one request per 64-byte half line otherwise, and the number of
+// requests it keeps in flight, not the L2's bandwidth, bounds the fill rate.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -57,12 +62,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
-constexpr int BK = 32;                          // reduction elements per step
-constexpr int kOperandBytes = 256 * BK * 2;     // 16 KiB: one operand, one step
-constexpr int kStageBytes = 2 * kOperandBytes;  // Q and P
-constexpr int kStages = 5;                      // 160 KiB of LDS
-constexpr int kLdsBytes = kStages * kStageBytes;
-constexpr int kCopiesPerStep = 8;               // buffer->LDS copies per wave per step
+constexpr int BK = 64;                          // reduction elements per step
+constexpr int kUnitBytes = 256 * BK * 2;        // 32 KiB: one operand, one step
+constexpr int kUnits = 5;                       // ring of operand units: 160 KiB of LDS
+constexpr int kLdsBytes = kUnits * kUnitBytes;
+constexpr int kCopiesPerUnit = 8;               // buffer->LDS copies per wave per unit
 
 enum Epi { EPI_LP = 0, EPI_F32 = 1, EPI_GELU = 2, EPI_ACC = 3 };
 
@@ -102,56 +106,60 @@ __device__ __forceinline__ void copy16(rsrc_t rs, char *lds_block, uint32_t voff
         : "memory", "m0");
 }
 
-// Copy j (0..3) of wave w fills bytes [(4 w + j) * 1 KiB, +1 KiB) of an
-// operand's stage; lane l writes the 16 bytes at offset 16 l of that block.
+// Copy j (0..7) of wave w fills bytes [(8 w + j) * 1 KiB, +1 KiB) of an
+// operand unit; lane l writes the 16 bytes at offset 16 l of that block.
 
-// Reduction-contiguous operand, element (r, k) at M[r * ld + k].
+// Reduction-contiguous operand, element (r, k) at M[r * ld + k].  LDS rows of
+// 64 reduction values (128 B, eight 16-byte chunks); chunk c of row r sits at
+// c ^ ((r >> 1) & 7).  Eight lanes fetch one 128-byte row of global memory.
 struct RcOperand {
     const char *base;  // &M[r0 * ld]
-    uint32_t voff[4];  // per-lane byte offsets of the 4 copies (kOOB past the row extent)
+    uint32_t voff[8];
 
-    __device__ __forceinline__ static int chunk_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
+    __device__ __forceinline__ static int chunk_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
+    __device__ __forceinline__ static int chunk_of(int j, int wave, int lane) {
+        const int pos = (wave * 8 + j) * 1024 + lane * 16;
+        return chunk_pos(pos >> 7, (pos >> 4) & 7);
+    }
 
     __device__ __forceinline__ void init(const uint16_t *M, int64_t ld, int64_t r0, int64_t rext,
                                          int wave, int lane) {
         base = reinterpret_cast<const char *>(M + r0 * ld);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int pos = (wave * 4 + j) * 1024 + lane * 16;
-            const int r = pos >> 6;                     // 64 B per LDS row
-            const int c = chunk_pos(r, (pos >> 4) & 3);  // logical chunk (the map is an involution)
-            voff[j] = (r0 + r < rext) ? (uint32_t)((r * ld + c * 8) * 2) : kOOB;
+        for (int j = 0; j < 8; ++j) {
+            const int r = ((wave * 8 + j) * 1024 + lane * 16) >> 7;
+            voff[j] = (r0 + r < rext) ? (uint32_t)((r * ld + chunk_of(j, wave, lane) * 8) * 2) : kOOB;
         }
     }
 
-    __device__ __forceinline__ void issue(char *stage, int64_t k0, int64_t red, int wave, int lane) {
+    __device__ __forceinline__ void issue(char *unit, int64_t k0, int64_t red, int wave, int lane) {
         const rsrc_t rs = make_rsrc(base + k0 * 2);
         if (k0 + BK <= red) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) copy16(rs, stage + (wave * 4 + j) * 1024, voff[j]);
+            for (int j = 0; j < 8; ++j) copy16(rs, unit + (wave * 8 + j) * 1024, voff[j]);
         } else {  // last, ragged step: chunks past the reduction length read as zero
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int pos = (wave * 4 + j) * 1024 + lane * 16;
-                const int c = chunk_pos(pos >> 6, (pos >> 4) & 3);
-                copy16(rs, stage + (wave * 4 + j) * 1024, (k0 + c * 8 < red) ? voff[j] : kOOB);
-            }
+            for (int j = 0; j < 8; ++j)
+                copy16(rs, unit + (wave * 8 + j) * 1024,
+                       (k0 + chunk_of(j, wave, lane) * 8 < red) ? voff[j] : kOOB);
         }
     }
 
     // Fragment of rows rbase .. rbase+31, reduction values 16 ks + 8 (lane >> 5) .. +7.
-    __device__ __forceinline__ static u32x4 frag(const char *stage, int rbase, int ks, int lane) {
+    __device__ __forceinline__ static u32x4 frag(const char *unit, int rbase, int ks, int lane) {
         const int r = rbase + (lane & 31);
         const int c = ks * 2 + (lane >> 5);
-        return *reinterpret_cast<const u32x4 *>(stage + r * 64 + (chunk_pos(r, c) << 4));
+        return *reinterpret_cast<const u32x4 *>(unit + r * 128 + (chunk_pos(r, c) << 4));
     }
 };
 
-// Reduction-strided operand, element (r, k) at M[k * ld + r].
+// Reduction-strided operand, element (r, k) at M[k * ld + r].  LDS rows of 256
+// elements (512 B, sixteen 32-byte segments) per reduction index k; segment s
+// of row k sits at s ^ 2 (k & 3).
 struct RsOperand {
     const char *base;  // &M[r0]
     int64_t ldb;       // ld in bytes
-    uint32_t voff[4];
+    uint32_t voff[8];
 
     __device__ __forceinline__ static int seg_pos(int k, int s) { return s ^ ((k & 3) << 1); }
 
@@ -160,8 +168,8 @@ struct RsOperand {
         base = reinterpret_cast<const char *>(M + r0);
         ldb = ld * 2;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int pos = (wave * 4 + j) * 1024 + lane * 16;
+        for (int j = 0; j < 8; ++j) {
+            const int pos = (wave * 8 + j) * 1024 + lane * 16;
             const int k = pos >> 9;                          // 512 B per LDS row
             const int s = seg_pos(k, (pos >> 5) & 15);       // logical 32-byte segment
             const int r = s * 16 + ((pos >> 4) & 1) * 8;     // first of 8 elements
@@ -169,23 +177,23 @@ struct RsOperand {
         }
     }
 
-    __device__ __forceinline__ void issue(char *stage, int64_t k0, int64_t red, int wave, int lane) {
+    __device__ __forceinline__ void issue(char *unit, int64_t k0, int64_t red, int wave, int lane) {
         const rsrc_t rs = make_rsrc(base + k0 * ldb);
         if (k0 + BK <= red) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) copy16(rs, stage + (wave * 4 + j) * 1024, voff[j]);
+            for (int j = 0; j < 8; ++j) copy16(rs, unit + (wave * 8 + j) * 1024, voff[j]);
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int k = ((wave * 4 + j) * 1024 + lane * 16) >> 9;
-                copy16(rs, stage + (wave * 4 + j) * 1024, (k0 + k < red) ? voff[j] : kOOB);
+            for (int j = 0; j < 8; ++j) {
+                const int k = ((wave * 8 + j) * 1024 + lane * 16) >> 9;
+                copy16(rs, unit + (wave * 8 + j) * 1024, (k0 + k < red) ? voff[j] : kOOB);
             }
         }
     }
 
     // Fragment of columns rbase .. rbase+31 (rbase % 32 == 0), reduction values
     // 16 ks + 8 (lane >> 5) .. +7: two transposing reads of 4 values each.
-    __device__ __forceinline__ static u32x4 frag(const char *stage, int rbase, int ks, int lane) {
+    __device__ __forceinline__ static u32x4 frag(const char *unit, int rbase, int ks, int lane) {
         const int h = lane >> 4;
         const int s = lane & 15;
         const int r = rbase + 16 * (h & 1) + 4 * (s & 3);
@@ -193,7 +201,7 @@ struct RsOperand {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int k = 16 * ks + 8 * (h >> 1) + 4 * t + (s >> 2);
-            const char *p = stage + k * 512 + (seg_pos(k, r >> 4) << 5) + (r & 15) * 2;
+            const char *p = unit + k * 512 + (seg_pos(k, r >> 4) << 5) + (r & 15) * 2;
             const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4 *)(uintptr_t)lds_addr(p));
             const u32x2 w = __builtin_bit_cast(u32x2, v);
@@ -210,14 +218,12 @@ template <int n>
 __device__ __forceinline__ void wait_and_barrier() {
     if constexpr (n == 0)
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (n == kCopiesPerStep)
+    else if constexpr (n == 8)
         asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (n == 2 * kCopiesPerStep)
+    else if constexpr (n == 16)
         asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (n == 3 * kCopiesPerStep)
+    else if constexpr (n == 24)
         asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (n == 4 * kCopiesPerStep)
-        asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
         static_assert(n == 0, "unsupported in-flight count");
 }
@@ -311,23 +317,29 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     qo.init(static_cast<const uint16_t *>(a.Q), a.ldq, q0, a.cols, wave, lane);
     po.init(static_cast<const uint16_t *>(a.P), a.ldp, p0, a.rows, wave, lane);
 
+    // Operand units: Q of step k is unit 2k, P of step k is unit 2k + 1; unit u
+    // lives in slot u % kUnits.  While step k is computed, units up to 2k + 4
+    // are in flight; when every wave has read step k, its two slots take units
+    // 2k + 5 and 2k + 6.
     const int64_t ksteps = (a.red + BK - 1) / BK;
-    auto stage_of = [&](int64_t kt) -> char * { return lds + (int)(kt % kStages) * kStageBytes; };
-    auto issue = [&](int64_t kt) {
-        char *st = stage_of(kt);
-        qo.issue(st, kt * BK, a.red, wave, lane);
-        po.issue(st + kOperandBytes, kt * BK, a.red, wave, lane);
+    const int64_t nunits = 2 * ksteps;
+    auto slot = [&](int64_t u) -> char * { return lds + ((uint32_t)u % kUnits) * kUnitBytes; };
+    auto issue_unit = [&](int64_t u) {
+        if (u >= nunits) return;
+        if (u & 1)
+            po.issue(slot(u), (u >> 1) * BK, a.red, wave, lane);
+        else
+            qo.issue(slot(u), (u >> 1) * BK, a.red, wave, lane);
     };
 
-    // Fragments of substep ks (16 reduction values) of a stage: the wave's
-    // 4 q-blocks and 4 p-blocks.
     u32x4 fa[2][4], fb[2][4];
-    auto frags = [&](const char *st, int ks, u32x4 (&xa)[4], u32x4 (&xb)[4]) {
+    auto frags = [&](int64_t kt, int ks, u32x4 (&xa)[4], u32x4 (&xb)[4]) {
+        const char *qs = slot(2 * kt);
+        const char *ps = slot(2 * kt + 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xa[i] = OperandT<Q_RS>::frag(st, wq * 128 + i * 32, ks, lane);
+        for (int i = 0; i < 4; ++i) xa[i] = OperandT<Q_RS>::frag(qs, wq * 128 + i * 32, ks, lane);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            xb[j] = OperandT<P_RS>::frag(st + kOperandBytes, wp * 128 + j * 32, ks, lane);
+        for (int j = 0; j < 4; ++j) xb[j] = OperandT<P_RS>::frag(ps, wp * 128 + j * 32, ks, lane);
     };
     constexpr int kReads = (Q_RS ? 8 : 4) + (P_RS ? 8 : 4);  // LDS read instructions per substep
 
@@ -343,7 +355,6 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = mfma32<T>(xa[i], xb[j], acc[i][j]);
     };
-    // one LDS read, then one MFMA, for the first kReads MFMAs of a substep
     auto interleave = [&]() {
 #pragma unroll
         for (int g = 0; g < kReads; ++g) {
@@ -353,40 +364,48 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 16 - kReads, 0);
     };
 
-    // prologue: kStages steps in flight, wait for the first
+    // prologue: units 0..4 in flight, wait for the two of step 0
 #pragma unroll
-    for (int s = 0; s < kStages; ++s)
-        if (s < ksteps) issue(s);
-    if (ksteps >= kStages)
-        wait_and_barrier<(kStages - 1) * kCopiesPerStep>();
-    else
-        wait_and_barrier<0>();
-    frags(stage_of(0), 0, fa[0], fb[0]);
+    for (int u = 0; u < kUnits; ++u) issue_unit(u);
+    {
+        const int64_t later = nunits - 2 < 3 ? nunits - 2 : 3;
+        if (later == 3) wait_and_barrier<24>();
+        else if (later == 2) wait_and_barrier<16>();
+        else if (later == 1) wait_and_barrier<8>();
+        else wait_and_barrier<0>();
+    }
+    frags(0, 0, fa[0], fb[0]);
 
-    for (int64_t kt = 0; kt + 1 < ksteps; ++kt) {
-        // substep 0 of step kt; the fragments of substep 1 are read under it
-        frags(stage_of(kt), 1, fa[1], fb[1]);
+    auto first_three = [&](int64_t kt) {
+        frags(kt, 1, fa[1], fb[1]);
         mma(fa[0], fb[0]);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
-        // every wave has read all of step kt: once step kt + 1 has landed,
-        // recycle step kt's stage for step kt + kStages
-        if (ksteps - 2 - kt >= kStages - 2)
-            wait_and_barrier<(kStages - 2) * kCopiesPerStep>();
+        frags(kt, 2, fa[0], fb[0]);
+        mma(fa[1], fb[1]);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        frags(kt, 3, fa[1], fb[1]);
+        mma(fa[0], fb[0]);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int64_t kt = 0; kt + 1 < ksteps; ++kt) {
+        first_three(kt);
+        // step kt + 1 must have landed; unit 2 kt + 4 may still be in flight
+        if (2 * kt + 4 < nunits)
+            wait_and_barrier<8>();
         else
             wait_and_barrier<0>();
-        if (kt + kStages < ksteps) issue(kt + kStages);
+        issue_unit(2 * kt + 5);
+        issue_unit(2 * kt + 6);
         __builtin_amdgcn_sched_barrier(0);
-        // substep 1 of step kt; substep 0 of step kt + 1 is read under it
-        frags(stage_of(kt + 1), 0, fa[0], fb[0]);
+        frags(kt + 1, 0, fa[0], fb[0]);
         mma(fa[1], fb[1]);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
     }
-    // last step: nothing left to copy
-    frags(stage_of(ksteps - 1), 1, fa[1], fb[1]);
-    mma(fa[0], fb[0]);
-    interleave();
+    first_three(ksteps - 1);
     mma(fa[1], fb[1]);
 
     // Epilogue.  Accumulator register 4g + e of block (i, j) holds

@@ -96,24 +96,25 @@ D2H_CUS = 8
 class Context:
     """The ring over a torch-allocated workspace and three streams.
 
-    By default the products and the host-to-device copies run on torch streams
-    and the device-to-host copies on a library stream confined to ``d2h_cus``
-    compute units (0: a torch stream as well).
+    By default the context creates its own three streams, one after another, so
+    that they sit on distinct hardware queues (see zi_stream_create): products,
+    host-to-device copies, and device-to-host copies confined to ``d2h_cus``
+    compute units (0: unconfined).  The products do not run on torch's current
+    stream: inputs must be complete before a call (torch.cuda.synchronize()),
+    and outputs are ready once sync() returns.
     """
 
     def __init__(self, plan: Plan, device: str = "cuda", workspace_bytes: Optional[int] = None,
                  streams=None, d2h_cus: int = D2H_CUS):
         nbytes = int(workspace_bytes if workspace_bytes is not None else plan.info.ring_bytes)
         self.handle = None
-        self._own_stream = None
+        self._own_streams = []
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         if streams is None:
-            if d2h_cus:
-                self._own_stream = zi.zi_copy_stream_create(d2h_cus)
-                d2h = self._own_stream
-            else:
-                d2h = torch.cuda.Stream(device=device)
-            streams = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device), d2h)
+            for _ in range(2):
+                self._own_streams.append(zi.zi_stream_create())
+            self._own_streams.append(zi.zi_copy_stream_create(d2h_cus) if d2h_cus else zi.zi_stream_create())
+            streams = tuple(self._own_streams)
         self.streams = streams
         self.handle = zi.zi_ctx_create(plan.handle, self.workspace, nbytes, *streams)
 
@@ -169,9 +170,8 @@ class Context:
         if self.handle:
             zi.zi_ctx_destroy(self.handle)
             self.handle = None
-        if self._own_stream:
-            zi.zi_stream_destroy(self._own_stream)
-            self._own_stream = None
+        while self._own_streams:
+            zi.zi_stream_destroy(self._own_streams.pop())
 
     def __del__(self):
         try:

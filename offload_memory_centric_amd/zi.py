@@ -97,6 +97,7 @@ _sigs = {
     "zi_ctx_set_timing": (_S, [_P, ctypes.c_int32]),
     "zi_ctx_reset_stats": (_S, [_P]),
     "zi_ctx_stats": (_S, [_P, ctypes.POINTER(zi_stats)]),
+    "zi_stream_create": (_S, [ctypes.POINTER(_P)]),
     "zi_copy_stream_create": (_S, [ctypes.c_int32, ctypes.POINTER(_P)]),
     "zi_stream_destroy": (_S, [_P]),
     "zi_host_alloc": (_S, [ctypes.c_uint64, ctypes.POINTER(_P)]),
@@ -197,6 +198,12 @@ def zi_tiled_linear_bwd_recompute(ctx, plan, X, dY, dX, Yr) -> None:
 
 def zi_gelu_bwd(ctx, dtype: int, dH, A, dA, count: int) -> None:
     _check(_lib.zi_gelu_bwd(ctx, int(dtype), _ptr(dH), _ptr(A), _ptr(dA), int(count)))
+
+
+def zi_stream_create() -> int:
+    h = _P()
+    _check(_lib.zi_stream_create(ctypes.byref(h)))
+    return h.value
 
 
 def zi_copy_stream_create(n_cus: int) -> int:

@@ -139,6 +139,8 @@ def test_null_arguments_are_rejected_without_a_gpu(zi):
         assert f(*([None] * nargs)) == zi.ZI_ERR_ARG, name
     lib.zi_ctx_create.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64] + [ctypes.c_void_p] * 4
     assert lib.zi_ctx_create(None, None, 0, None, None, None, None) == zi.ZI_ERR_ARG
+    lib.zi_stream_create.argtypes = [ctypes.c_void_p]
+    assert lib.zi_stream_create(None) == zi.ZI_ERR_ARG
     lib.zi_copy_stream_create.argtypes = [ctypes.c_int32, ctypes.c_void_p]
     out = ctypes.c_void_p()
     assert lib.zi_copy_stream_create(8, None) == zi.ZI_ERR_ARG
