@@ -86,10 +86,14 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw 32-bit buffer, gfx9 layout
 
 typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
 
-// Buffer descriptor: 48-bit base, stride 0, kNumRecords bytes.
+// Buffer descriptor: 48-bit base, stride 0, kNumRecords bytes.  The base is
+// the same for every lane; readfirstlane states so, keeping the descriptor in
+// scalar registers where the instruction needs it.
 __device__ __forceinline__ rsrc_t make_rsrc(const char *base) {
     const uint64_t b = (uint64_t)(uintptr_t)base;
-    return rsrc_t{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, kNumRecords, kRsrcWord3};
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    return rsrc_t{lo, hi & 0xffffu, kNumRecords, kRsrcWord3};
 }
 
 // One 16-byte-per-lane copy global -> LDS at lds_block + 16 * lane.  Written as
@@ -132,24 +136,24 @@ struct RcOperand {
         }
     }
 
-    __device__ __forceinline__ void issue(char *unit, int64_t k0, int64_t red, int wave, int lane) {
+    // Copy j (0..7) of this wave for the step starting at reduction index k0.
+    // Chunks at or past the reduction length (a ragged last step, or a step
+    // past the end) read as zero.
+    __device__ __forceinline__ void issue(char *unit, int64_t k0, int64_t red, int wave, int lane, int j) {
         const rsrc_t rs = make_rsrc(base + k0 * 2);
-        if (k0 + BK <= red) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) copy16(rs, unit + (wave * 8 + j) * 1024, voff[j]);
-        } else {  // last, ragged step: chunks past the reduction length read as zero
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                copy16(rs, unit + (wave * 8 + j) * 1024,
-                       (k0 + chunk_of(j, wave, lane) * 8 < red) ? voff[j] : kOOB);
-        }
+        const bool ok = k0 + chunk_of(j, wave, lane) * 8 < red;
+        copy16(rs, unit + (wave * 8 + j) * 1024, ok ? voff[j] : kOOB);
     }
 
-    // Fragment of rows rbase .. rbase+31, reduction values 16 ks + 8 (lane >> 5) .. +7.
-    __device__ __forceinline__ static u32x4 frag(const char *unit, int rbase, int ks, int lane) {
+    // Fragment of rows rbase .. rbase+31, reduction values 16 ks + 8 (lane >> 5) .. +7:
+    // one 16-byte read.
+    static constexpr int kReadsPerFrag = 1;
+    __device__ __forceinline__ static void frag_part(const char *unit, int rbase, int ks, int lane, int t,
+                                                     u32x4 &out) {
+        (void)t;
         const int r = rbase + (lane & 31);
         const int c = ks * 2 + (lane >> 5);
-        return *reinterpret_cast<const u32x4 *>(unit + r * 128 + (chunk_pos(r, c) << 4));
+        out = *reinterpret_cast<const u32x4 *>(unit + r * 128 + (chunk_pos(r, c) << 4));
     }
 };
 
@@ -177,38 +181,30 @@ struct RsOperand {
         }
     }
 
-    __device__ __forceinline__ void issue(char *unit, int64_t k0, int64_t red, int wave, int lane) {
+    // Copy j (0..7) of this wave for the step starting at reduction index k0;
+    // rows at or past the reduction length read as zero.
+    __device__ __forceinline__ void issue(char *unit, int64_t k0, int64_t red, int wave, int lane, int j) {
         const rsrc_t rs = make_rsrc(base + k0 * ldb);
-        if (k0 + BK <= red) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) copy16(rs, unit + (wave * 8 + j) * 1024, voff[j]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int k = ((wave * 8 + j) * 1024 + lane * 16) >> 9;
-                copy16(rs, unit + (wave * 8 + j) * 1024, (k0 + k < red) ? voff[j] : kOOB);
-            }
-        }
+        const int k = ((wave * 8 + j) * 1024 + lane * 16) >> 9;
+        copy16(rs, unit + (wave * 8 + j) * 1024, (k0 + k < red) ? voff[j] : kOOB);
     }
 
     // Fragment of columns rbase .. rbase+31 (rbase % 32 == 0), reduction values
-    // 16 ks + 8 (lane >> 5) .. +7: two transposing reads of 4 values each.
-    __device__ __forceinline__ static u32x4 frag(const char *unit, int rbase, int ks, int lane) {
+    // 16 ks + 8 (lane >> 5) .. +7: two transposing reads of 4 values each
+    // (t = 0, 1), each filling half of `out`.
+    static constexpr int kReadsPerFrag = 2;
+    __device__ __forceinline__ static void frag_part(const char *unit, int rbase, int ks, int lane, int t,
+                                                     u32x4 &out) {
         const int h = lane >> 4;
         const int s = lane & 15;
         const int r = rbase + 16 * (h & 1) + 4 * (s & 3);
-        u32x4 out;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int k = 16 * ks + 8 * (h >> 1) + 4 * t + (s >> 2);
-            const char *p = unit + k * 512 + (seg_pos(k, r >> 4) << 5) + (r & 15) * 2;
-            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(uintptr_t)lds_addr(p));
-            const u32x2 w = __builtin_bit_cast(u32x2, v);
-            out[2 * t] = w[0];
-            out[2 * t + 1] = w[1];
-        }
-        return out;
+        const int k = 16 * ks + 8 * (h >> 1) + 4 * t + (s >> 2);
+        const char *p = unit + k * 512 + (seg_pos(k, r >> 4) << 5) + (r & 15) * 2;
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(uintptr_t)lds_addr(p));
+        const u32x2 w = __builtin_bit_cast(u32x2, v);
+        out[2 * t] = w[0];
+        out[2 * t + 1] = w[1];
     }
 };
 
@@ -318,30 +314,45 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     po.init(static_cast<const uint16_t *>(a.P), a.ldp, p0, a.rows, wave, lane);
 
     // Operand units: Q of step k is unit 2k, P of step k is unit 2k + 1; unit u
-    // lives in slot u % kUnits.  While step k is computed, units up to 2k + 4
-    // are in flight; when every wave has read step k, its two slots take units
-    // 2k + 5 and 2k + 6.
+    // lives in slot u % kUnits.  A step is four substeps of 16 reduction values
+    // (16 MFMAs each).  Under substeps 0 and 1 of step k the waves copy unit
+    // 2k + 4 (into the slot step k - 1 has released); at the end of substep 2
+    // every wave has read all of step k, and once step k + 1 has landed they
+    // meet at a barrier; under substep 3 they copy unit 2k + 5 into the slot of
+    // unit 2k.  So while step k is multiplied, up to three units are in flight.
+    // Copies and the fragment reads of the next substep are spread evenly
+    // between the MFMAs, so that no wave stalls on a burst of copies while its
+    // matrix unit idles.
     const int64_t ksteps = (a.red + BK - 1) / BK;
     const int64_t nunits = 2 * ksteps;
     auto slot = [&](int64_t u) -> char * { return lds + ((uint32_t)u % kUnits) * kUnitBytes; };
-    auto issue_unit = [&](int64_t u) {
-        if (u >= nunits) return;
+    auto copy = [&](int64_t u, int j) {  // copy j of unit u (reads zeros past the last unit)
+        char *st = slot(u);
+        const int64_t k0 = (u >> 1) * BK;
         if (u & 1)
-            po.issue(slot(u), (u >> 1) * BK, a.red, wave, lane);
+            po.issue(st, k0, a.red, wave, lane, j);
         else
-            qo.issue(slot(u), (u >> 1) * BK, a.red, wave, lane);
+            qo.issue(st, k0, a.red, wave, lane, j);
     };
 
-    u32x4 fa[2][4], fb[2][4];
-    auto frags = [&](int64_t kt, int ks, u32x4 (&xa)[4], u32x4 (&xb)[4]) {
-        const char *qs = slot(2 * kt);
-        const char *ps = slot(2 * kt + 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xa[i] = OperandT<Q_RS>::frag(qs, wq * 128 + i * 32, ks, lane);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xb[j] = OperandT<P_RS>::frag(ps, wp * 128 + j * 32, ks, lane);
+    using QOp = OperandT<Q_RS>;
+    using POp = OperandT<P_RS>;
+    constexpr int QR = QOp::kReadsPerFrag, PR = POp::kReadsPerFrag;
+    constexpr int kReads = 4 * QR + 4 * PR;  // LDS read instructions per substep
+
+    // Read r of a substep, in the order its MFMAs consume the fragments:
+    // Q0, P0..P3, Q1..Q3.
+    auto read = [&](int r, const char *qs, const char *ps, int ks, u32x4 (&ya)[4], u32x4 (&yb)[4]) {
+        if (r < QR) {
+            QOp::frag_part(qs, wq * 128, ks, lane, r, ya[0]);
+        } else if (r < QR + 4 * PR) {
+            const int f = (r - QR) / PR;
+            POp::frag_part(ps, wp * 128 + f * 32, ks, lane, (r - QR) % PR, yb[f]);
+        } else {
+            const int f = 1 + (r - QR - 4 * PR) / QR;
+            QOp::frag_part(qs, wq * 128 + f * 32, ks, lane, (r - QR - 4 * PR) % QR, ya[f]);
+        }
     };
-    constexpr int kReads = (Q_RS ? 8 : 4) + (P_RS ? 8 : 4);  // LDS read instructions per substep
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -349,64 +360,59 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-    auto mma = [&](const u32x4 (&xa)[4], const u32x4 (&xb)[4]) {
+    // One substep: 16 MFMAs on (xa, xb); between them the reads of the next
+    // substep (stage qs/ps, substep ks, into ya/yb) and `ncopy` copies.
+    auto substep = [&](const u32x4 (&xa)[4], const u32x4 (&xb)[4], u32x4 (&ya)[4], u32x4 (&yb)[4],
+                       const char *qs, const char *ps, int ks, bool reads, int ncopy, auto &&copy_c) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int m = 0; m < 16; ++m) {
+            acc[m >> 2][m & 3] = mfma32<T>(xa[m >> 2], xb[m & 3], acc[m >> 2][m & 3]);
+            if (reads) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32<T>(xa[i], xb[j], acc[i][j]);
-    };
-    auto interleave = [&]() {
-#pragma unroll
-        for (int g = 0; g < kReads; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                for (int r = (m * kReads + 15) / 16; r < ((m + 1) * kReads + 15) / 16; ++r)
+                    read(r, qs, ps, ks, ya, yb);
+            }
+            if (ncopy > 0 && m % (16 / ncopy) == (16 / ncopy) / 2) copy_c(m / (16 / ncopy));
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16 - kReads, 0);
     };
+    auto no_copy = [](int) {};
 
-    // prologue: units 0..4 in flight, wait for the two of step 0
+    u32x4 fa[2][4], fb[2][4];
+    // prologue: units 0..3 in flight, wait for the two of step 0
 #pragma unroll
-    for (int u = 0; u < kUnits; ++u) issue_unit(u);
-    {
-        const int64_t later = nunits - 2 < 3 ? nunits - 2 : 3;
-        if (later == 3) wait_and_barrier<24>();
-        else if (later == 2) wait_and_barrier<16>();
-        else if (later == 1) wait_and_barrier<8>();
-        else wait_and_barrier<0>();
-    }
-    frags(0, 0, fa[0], fb[0]);
+    for (int u = 0; u < 4; ++u)
+        if (u < nunits)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) copy(u, j);
+    if (nunits >= 4)
+        wait_and_barrier<16>();
+    else
+        wait_and_barrier<0>();
+#pragma unroll
+    for (int r = 0; r < kReads; ++r) read(r, slot(0), slot(1), 0, fa[0], fb[0]);
 
+    // substeps 0..2 of step kt, unit 2 kt + 4 copied under substeps 0 and 1
     auto first_three = [&](int64_t kt) {
-        frags(kt, 1, fa[1], fb[1]);
-        mma(fa[0], fb[0]);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
-        frags(kt, 2, fa[0], fb[0]);
-        mma(fa[1], fb[1]);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
-        frags(kt, 3, fa[1], fb[1]);
-        mma(fa[0], fb[0]);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
+        const char *qs = slot(2 * kt), *ps = slot(2 * kt + 1);
+        const int64_t u = 2 * kt + 4;
+        substep(fa[0], fb[0], fa[1], fb[1], qs, ps, 1, true, 4, [&](int c) { copy(u, c); });
+        substep(fa[1], fb[1], fa[0], fb[0], qs, ps, 2, true, 4, [&](int c) { copy(u, 4 + c); });
+        substep(fa[0], fb[0], fa[1], fb[1], qs, ps, 3, true, 0, no_copy);
     };
     for (int64_t kt = 0; kt + 1 < ksteps; ++kt) {
         first_three(kt);
         // step kt + 1 must have landed; unit 2 kt + 4 may still be in flight
-        if (2 * kt + 4 < nunits)
-            wait_and_barrier<8>();
-        else
-            wait_and_barrier<0>();
-        issue_unit(2 * kt + 5);
-        issue_unit(2 * kt + 6);
-        __builtin_amdgcn_sched_barrier(0);
-        frags(kt + 1, 0, fa[0], fb[0]);
-        mma(fa[1], fb[1]);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
+        wait_and_barrier<8>();
+        const int64_t u = 2 * kt + 5;
+        substep(fa[1], fb[1], fa[0], fb[0], slot(2 * kt + 2), slot(2 * kt + 3), 0, true, 8,
+                [&](int c) { copy(u, c); });
     }
     first_three(ksteps - 1);
-    mma(fa[1], fb[1]);
+    substep(fa[1], fb[1], fa[0], fb[0], nullptr, nullptr, 0, false, 0, no_copy);
+    // the copies past the last unit are still in flight: none may land after
+    // the workgroup has released its LDS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue.  Accumulator register 4g + e of block (i, j) holds
     // C[p][q] with p = j-block row (lane & 31) and q = 8 g + 4 (lane >> 5) + e.
