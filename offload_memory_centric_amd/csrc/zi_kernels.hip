@@ -89,11 +89,11 @@ typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
 // Buffer descriptor: 48-bit base, stride 0, kNumRecords bytes.  The base is
 // the same for every lane; readfirstlane states so, keeping the descriptor in
 // scalar registers where the instruction needs it.
-__device__ __forceinline__ rsrc_t make_rsrc(const char *base) {
+__device__ __forceinline__ rsrc_t make_rsrc(const char *base, uint32_t records = kNumRecords) {
     const uint64_t b = (uint64_t)(uintptr_t)base;
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    return rsrc_t{lo, hi & 0xffffu, kNumRecords, kRsrcWord3};
+    return rsrc_t{lo, hi & 0xffffu, records, kRsrcWord3};
 }
 
 // One 16-byte-per-lane copy global -> LDS at lds_block + 16 * lane.  Written as
@@ -145,15 +145,39 @@ struct RcOperand {
         copy16(rs, unit + (wave * 8 + j) * 1024, ok ? voff[j] : kOOB);
     }
 
-    // Fragment of rows rbase .. rbase+31, reduction values 16 ks + 8 (lane >> 5) .. +7:
-    // one 16-byte read.
+    // The same when the reduction length is a multiple of BK: a whole step is
+    // in range or (past the last unit) none of it, which the descriptor's
+    // record count expresses without a per-lane select.
+    __device__ __forceinline__ void issue_aligned(char *unit, int64_t k0, bool valid, int wave, int j) {
+        copy16(make_rsrc(base + k0 * 2, valid ? kNumRecords : 0u), unit + (wave * 8 + j) * 1024, voff[j]);
+    }
+
+    // Fragment reads.  Fragment f (0..3) of substep ks holds rows
+    // wq * 128 + 32 f + (lane & 31) and reduction values 16 ks + 8 (lane >> 5)
+    // .. +7: one 16-byte read.  Its address is the unit's, plus a per-lane part
+    // that depends on ks only through the swizzle (flo[ks], fixed for the
+    // kernel), plus 32 f rows (a constant): one add per substep.
     static constexpr int kReadsPerFrag = 1;
-    __device__ __forceinline__ static void frag_part(const char *unit, int rbase, int ks, int lane, int t,
-                                                     u32x4 &out) {
+    uint32_t flo[4];
+    __device__ __forceinline__ void init_reads(int wq, int lane) {
+        const int r = lane & 31;  // the swizzle sees r modulo 32
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            flo[ks] = (uint32_t)((wq * 128 + r) * 128 + (chunk_pos(r, ks * 2 + (lane >> 5)) << 4));
+    }
+    // Per-lane base of the reads of substep ks in the unit at LDS address
+    // `unit`: one add, hidden from the optimiser so that the constant parts of
+    // the addresses stay in the instructions' offset fields.
+    struct Bases { uint32_t b; };
+    __device__ __forceinline__ Bases bases(uint32_t unit, int ks) const {
+        Bases r{unit + flo[ks]};
+        asm volatile("" : "+v"(r.b));
+        return r;
+    }
+    __device__ __forceinline__ static void frag(const Bases &b, int ks, int f, int t, u32x4 &out) {
+        (void)ks;
         (void)t;
-        const int r = rbase + (lane & 31);
-        const int c = ks * 2 + (lane >> 5);
-        out = *reinterpret_cast<const u32x4 *>(unit + r * 128 + (chunk_pos(r, c) << 4));
+        out = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((uintptr_t)(b.b + f * 32 * 128));
     }
 };
 
@@ -189,19 +213,42 @@ struct RsOperand {
         copy16(rs, unit + (wave * 8 + j) * 1024, (k0 + k < red) ? voff[j] : kOOB);
     }
 
-    // Fragment of columns rbase .. rbase+31 (rbase % 32 == 0), reduction values
-    // 16 ks + 8 (lane >> 5) .. +7: two transposing reads of 4 values each
-    // (t = 0, 1), each filling half of `out`.
+    __device__ __forceinline__ void issue_aligned(char *unit, int64_t k0, bool valid, int wave, int j) {
+        copy16(make_rsrc(base + k0 * ldb, valid ? kNumRecords : 0u), unit + (wave * 8 + j) * 1024, voff[j]);
+    }
+
+    // Fragment reads.  Fragment f (0..3) of substep ks holds columns
+    // wq * 128 + 32 f + .. 31 and reduction values 16 ks + 8 (lane >> 5) .. +7:
+    // two transposing reads of 4 values each (t = 0, 1), each filling half of
+    // `out`.  The segment swizzle mixes f into the per-lane address but not ks
+    // or t, so the address is the unit's plus flo[f] (fixed for the kernel)
+    // plus (16 ks + 4 t) rows of 512 bytes (a constant).
     static constexpr int kReadsPerFrag = 2;
-    __device__ __forceinline__ static void frag_part(const char *unit, int rbase, int ks, int lane, int t,
-                                                     u32x4 &out) {
+    uint32_t flo[4];
+    __device__ __forceinline__ void init_reads(int wq, int lane) {
         const int h = lane >> 4;
         const int s = lane & 15;
-        const int r = rbase + 16 * (h & 1) + 4 * (s & 3);
-        const int k = 16 * ks + 8 * (h >> 1) + 4 * t + (s >> 2);
-        const char *p = unit + k * 512 + (seg_pos(k, r >> 4) << 5) + (r & 15) * 2;
+        const int kl = 8 * (h >> 1) + (s >> 2);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const int r = wq * 128 + f * 32 + 16 * (h & 1) + 4 * (s & 3);
+            flo[f] = (uint32_t)(kl * 512 + (seg_pos(kl, r >> 4) << 5) + (r & 15) * 2);
+        }
+    }
+    struct Bases { uint32_t b[4]; };
+    __device__ __forceinline__ Bases bases(uint32_t unit, int ks) const {
+        (void)ks;
+        Bases r;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            r.b[f] = unit + flo[f];
+            asm volatile("" : "+v"(r.b[f]));
+        }
+        return r;
+    }
+    __device__ __forceinline__ static void frag(const Bases &b, int ks, int f, int t, u32x4 &out) {
         const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(uintptr_t)lds_addr(p));
+            (__attribute__((address_space(3))) s16x4 *)(uintptr_t)(b.b[f] + (16 * ks + 4 * t) * 512));
         const u32x2 w = __builtin_bit_cast(u32x2, v);
         out[2 * t] = w[0];
         out[2 * t + 1] = w[1];
@@ -292,7 +339,7 @@ __device__ __forceinline__ void tile_coords(int w, int tiles_p, int tiles_q, int
 template <bool RS>
 using OperandT = typename std::conditional<RS, RsOperand, RcOperand>::type;
 
-template <typename T, bool Q_RS, bool P_RS, int EPI>
+template <typename T, bool Q_RS, bool P_RS, int EPI, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
@@ -312,6 +359,8 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     OperandT<P_RS> po;
     qo.init(static_cast<const uint16_t *>(a.Q), a.ldq, q0, a.cols, wave, lane);
     po.init(static_cast<const uint16_t *>(a.P), a.ldp, p0, a.rows, wave, lane);
+    qo.init_reads(wq, lane);
+    po.init_reads(wp, lane);
 
     // Operand units: Q of step k is unit 2k, P of step k is unit 2k + 1; unit u
     // lives in slot u % kUnits.  A step is four substeps of 16 reduction values
@@ -326,14 +375,23 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     const int64_t ksteps = (a.red + BK - 1) / BK;
     const int64_t nunits = 2 * ksteps;
     auto slot = [&](int64_t u) -> char * { return lds + ((uint32_t)u % kUnits) * kUnitBytes; };
-    auto copy = [&](int64_t u, int j) {  // copy j of unit u (reads zeros past the last unit)
-        char *st = slot(u);
+    // copy j of unit u into slot st (zeros past the last unit)
+    auto copy_to = [&](char *st, int64_t u, int j) {
         const int64_t k0 = (u >> 1) * BK;
-        if (u & 1)
-            po.issue(st, k0, a.red, wave, lane, j);
-        else
-            qo.issue(st, k0, a.red, wave, lane, j);
+        if constexpr (ALIGNED) {
+            const bool valid = u < nunits;
+            if (u & 1)
+                po.issue_aligned(st, k0, valid, wave, j);
+            else
+                qo.issue_aligned(st, k0, valid, wave, j);
+        } else {
+            if (u & 1)
+                po.issue(st, k0, a.red, wave, lane, j);
+            else
+                qo.issue(st, k0, a.red, wave, lane, j);
+        }
     };
+    auto copy = [&](int64_t u, int j) { copy_to(slot(u), u, j); };
 
     using QOp = OperandT<Q_RS>;
     using POp = OperandT<P_RS>;
@@ -342,15 +400,17 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
 
     // Read r of a substep, in the order its MFMAs consume the fragments:
     // Q0, P0..P3, Q1..Q3.
-    auto read = [&](int r, const char *qs, const char *ps, int ks, u32x4 (&ya)[4], u32x4 (&yb)[4]) {
+    using QB = typename QOp::Bases;
+    using PB = typename POp::Bases;
+    auto read = [&](int r, const QB &qb, const PB &pb, int ks, u32x4 (&ya)[4], u32x4 (&yb)[4]) {
         if (r < QR) {
-            QOp::frag_part(qs, wq * 128, ks, lane, r, ya[0]);
+            QOp::frag(qb, ks, 0, r, ya[0]);
         } else if (r < QR + 4 * PR) {
             const int f = (r - QR) / PR;
-            POp::frag_part(ps, wp * 128 + f * 32, ks, lane, (r - QR) % PR, yb[f]);
+            POp::frag(pb, ks, f, (r - QR) % PR, yb[f]);
         } else {
             const int f = 1 + (r - QR - 4 * PR) / QR;
-            QOp::frag_part(qs, wq * 128 + f * 32, ks, lane, (r - QR - 4 * PR) % QR, ya[f]);
+            QOp::frag(qb, ks, f, (r - QR - 4 * PR) % QR, ya[f]);
         }
     };
 
@@ -364,13 +424,19 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     // substep (stage qs/ps, substep ks, into ya/yb) and `ncopy` copies.
     auto substep = [&](const u32x4 (&xa)[4], const u32x4 (&xb)[4], u32x4 (&ya)[4], u32x4 (&yb)[4],
                        const char *qs, const char *ps, int ks, bool reads, int ncopy, auto &&copy_c) {
+        QB qb{};
+        PB pb{};
+        if (reads) {
+            qb = qo.bases(lds_addr(qs), ks);
+            pb = po.bases(lds_addr(ps), ks);
+        }
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             acc[m >> 2][m & 3] = mfma32<T>(xa[m >> 2], xb[m & 3], acc[m >> 2][m & 3]);
             if (reads) {
 #pragma unroll
                 for (int r = (m * kReads + 15) / 16; r < ((m + 1) * kReads + 15) / 16; ++r)
-                    read(r, qs, ps, ks, ya, yb);
+                    read(r, qb, pb, ks, ya, yb);
             }
             if (ncopy > 0 && m % (16 / ncopy) == (16 / ncopy) / 2) copy_c(m / (16 / ncopy));
             __builtin_amdgcn_sched_barrier(0);
@@ -389,8 +455,12 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
         wait_and_barrier<16>();
     else
         wait_and_barrier<0>();
+    {
+        const QB qb = qo.bases(lds_addr(slot(0)), 0);
+        const PB pb = po.bases(lds_addr(slot(1)), 0);
 #pragma unroll
-    for (int r = 0; r < kReads; ++r) read(r, slot(0), slot(1), 0, fa[0], fb[0]);
+        for (int r = 0; r < kReads; ++r) read(r, qb, pb, 0, fa[0], fb[0]);
+    }
 
     // substeps 0..2 of step kt, unit 2 kt + 4 copied under substeps 0 and 1
     auto first_three = [&](int64_t kt) {
@@ -400,7 +470,8 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
         substep(fa[1], fb[1], fa[0], fb[0], qs, ps, 2, true, 4, [&](int c) { copy(u, 4 + c); });
         substep(fa[0], fb[0], fa[1], fb[1], qs, ps, 3, true, 0, no_copy);
     };
-    for (int64_t kt = 0; kt + 1 < ksteps; ++kt) {
+    int64_t kt = 0;
+    for (; kt + 1 < ksteps; ++kt) {
         first_three(kt);
         // step kt + 1 must have landed; unit 2 kt + 4 may still be in flight
         wait_and_barrier<8>();
@@ -493,8 +564,12 @@ hipError_t run(const GemmArgs &a, hipStream_t s) {
     const int tiles_q = (int)((a.cols + kTileQ - 1) / kTileQ);
     const int64_t nt = (int64_t)tiles_p * tiles_q;
     if (nt <= 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI>), dim3((unsigned)nt), dim3(kThreads), 0, s,
-                       a, tiles_p, tiles_q);
+    if (a.red % BK == 0)
+        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, true>), dim3((unsigned)nt), dim3(kThreads), 0, s,
+                           a, tiles_p, tiles_q);
+    else
+        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, false>), dim3((unsigned)nt), dim3(kThreads), 0, s,
+                           a, tiles_p, tiles_q);
     return hipGetLastError();
 }
 
