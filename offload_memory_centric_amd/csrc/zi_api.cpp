@@ -287,9 +287,17 @@ zi_status run_bwd(zi_ctx *c, const zi_plan *p, const void *X, const void *dY, fl
     const int d = c->d;
     const int64_t base = c->seq, dbase = c->dw_seq;
     const double tile_flops = 2.0 * (double)pr.T * (double)pr.K * (double)n;
+    // With separate gradient slots and at least two weight slots, the dX
+    // product of tiles 2j and 2j + 1 is one launch over both (a reduction of
+    // 2n), which halves the fp32 read-add-store passes over dX.  Tile 2j stays
+    // in its slot until that launch has read it; the dW product of tile 2j + 1
+    // runs after it and covers the copy of the next tile into the freed slot.
+    const bool pairs = c->dw_slots > 0 && d >= 2 && N >= 2 && n % kGemmStep == 0;
     zi_status st;
-    for (int64_t j = 0; j < std::min<int64_t>(d, N); ++j)
+    int64_t staged = std::min<int64_t>(d, N);
+    for (int64_t j = 0; j < staged; ++j)
         if ((st = stage(c, p, base + j, j)) != ZI_OK) return st;
+    int64_t released = -1;  // every tile <= released has had its weight slot freed
     for (int64_t i = 0; i < N; ++i) {
         const int s = (int)((base + i) % d);
         HIPCHK(c, hipStreamWaitEvent(c->comp, c->w_ready[s], 0));
@@ -308,26 +316,40 @@ zi_status run_bwd(zi_ctx *c, const zi_plan *p, const void *X, const void *dY, fl
             a.out_f32 = f32 ? 1 : 0;
             if ((st = gemm(c, K_FWD_RECOMPUTE, GemmOp::Fwd, pr.dtype, a, tile_flops)) != ZI_OK) return st;
         }
-        {  // dX (+)= dY_i W_i^T: W_i^t[r][k] read across its rows
+        const bool first_of_pair = pairs && (i % 2 == 0) && i + 1 < N;
+        const bool second_of_pair = pairs && (i % 2 == 1);
+        if (!first_of_pair) {  // dX (+)= dY_i W_i^T (or over tiles i-1, i): W^t[r][k] read across its rows
+            const int64_t i0 = second_of_pair ? i - 1 : i;
             GemmArgs a{};
-            a.Q = c->wslot(s);
+            a.Q = c->wslot(second_of_pair ? (int)((base + i0) % d) : s);
             a.ldq = pr.K;
-            a.P = dYi;
+            if (second_of_pair) {
+                a.Q2 = c->wslot(s);
+                a.qsplit = n;
+            }
+            a.P = static_cast<const uint16_t *>(dY) + i0 * n;
             a.ldp = pr.M;
             a.C = dX;
             a.ldc = pr.K;
             a.rows = pr.T;
             a.cols = pr.K;
-            a.red = n;
-            a.accumulate = i > 0 ? 1 : 0;
-            if ((st = gemm(c, K_DX, GemmOp::Dx, pr.dtype, a, tile_flops)) != ZI_OK) return st;
+            a.red = (i - i0 + 1) * n;
+            a.accumulate = i0 > 0 ? 1 : 0;
+            if ((st = gemm(c, K_DX, GemmOp::Dx, pr.dtype, a, tile_flops * (double)(i - i0 + 1))) != ZI_OK)
+                return st;
         }
         char *dst;
         hipEvent_t ready, done;
         int ds = -1;
         if (c->dw_slots > 0) {
-            HIPCHK(c, hipEventRecord(c->w_free[s], c->comp));
-            c->w_free_rec[s] = 1;
+            if (!first_of_pair) {
+                for (int64_t t = (second_of_pair ? i - 1 : i); t <= i; ++t) {
+                    const int ts = (int)((base + t) % d);
+                    HIPCHK(c, hipEventRecord(c->w_free[ts], c->comp));
+                    c->w_free_rec[ts] = 1;
+                }
+                released = i;
+            }
             ds = (int)((dbase + i) % c->dw_slots);
             if (c->dw_free_rec[ds]) HIPCHK(c, hipStreamWaitEvent(c->comp, c->dw_free[ds], 0));
             dst = c->dwslot(ds);
@@ -354,11 +376,15 @@ zi_status run_bwd(zi_ctx *c, const zi_plan *p, const void *X, const void *dY, fl
         }
         HIPCHK(c, hipEventRecord(ready, c->comp));
         if ((st = write_back(c, p, i, dst, ready, done)) != ZI_OK) return st;
-        if (ds >= 0)
+        if (ds >= 0) {
             c->dw_free_rec[ds] = 1;
-        else
+        } else {
             c->w_free_rec[s] = 1;
-        if (i + d < N && (st = stage(c, p, base + i + d, i + d)) != ZI_OK) return st;
+            released = i;
+        }
+        // stage every tile whose slot has now been released
+        for (; staged < N && staged - d <= released; ++staged)
+            if ((st = stage(c, p, base + staged, staged)) != ZI_OK) return st;
     }
     c->seq += N;
     c->dw_seq += N;

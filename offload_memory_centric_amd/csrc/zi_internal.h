@@ -29,6 +29,11 @@ struct GemmArgs {
     int64_t red;    // reduction length
     int accumulate; // Dx only: 0 = overwrite, 1 = add into C
     int out_f32;    // Fwd / Dw: write fp32 instead of the 16-bit format
+    // Dx only: reduction rows k >= qsplit of Q come from Q2 (row k - qsplit), so
+    // one launch can consume two weight tiles held in different ring slots.
+    // qsplit = 0: no split.  Otherwise a multiple of the kernel's step (64).
+    const void *Q2;
+    int64_t qsplit;
 };
 
 // dtype: 1 = fp16, 2 = bf16.  Returns the launch status (hipGetLastError).
@@ -41,5 +46,7 @@ hipError_t launch_gelu_bwd(int dtype, const float *dH, const void *A, void *dA, 
 // Macro-tile of the GEMM kernels (rows of p, columns of q per workgroup).
 constexpr int kTileP = 256;
 constexpr int kTileQ = 256;
+// Reduction values per pipeline step of the GEMM kernels.
+constexpr int kGemmStep = 64;
 
 }  // namespace zi

@@ -62,7 +62,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
-constexpr int BK = 64;                          // reduction elements per step
+constexpr int BK = kGemmStep;                        // reduction elements per step
 constexpr int kUnitBytes = 256 * BK * 2;        // 32 KiB: one operand, one step
 constexpr int kUnits = 5;                       // ring of operand units: 160 KiB of LDS
 constexpr int kLdsBytes = kUnits * kUnitBytes;
@@ -185,15 +185,28 @@ struct RcOperand {
 // elements (512 B, sixteen 32-byte segments) per reduction index k; segment s
 // of row k sits at s ^ 2 (k & 3).
 struct RsOperand {
-    const char *base;  // &M[r0]
-    int64_t ldb;       // ld in bytes
+    const char *base;   // &M[r0]
+    const char *base2;  // &M2[r0]: reduction rows from `split` on (split = 0: none)
+    int64_t split;
+    int64_t ldb;        // ld in bytes
     uint32_t voff[8];
+
+    __device__ __forceinline__ void set_split(const void *M2, int64_t split_, int64_t r0) {
+        split = M2 ? split_ : 0;
+        base2 = M2 ? reinterpret_cast<const char *>(static_cast<const uint16_t *>(M2) + r0) : base;
+    }
+    // Address of reduction row k0 (a step never straddles `split`).
+    __device__ __forceinline__ const char *row(int64_t k0) const {
+        return (split && k0 >= split) ? base2 + (k0 - split) * ldb : base + k0 * ldb;
+    }
 
     __device__ __forceinline__ static int seg_pos(int k, int s) { return s ^ ((k & 3) << 1); }
 
     __device__ __forceinline__ void init(const uint16_t *M, int64_t ld, int64_t r0, int64_t rext,
                                          int wave, int lane) {
         base = reinterpret_cast<const char *>(M + r0);
+        base2 = base;
+        split = 0;
         ldb = ld * 2;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -208,13 +221,13 @@ struct RsOperand {
     // Copy j (0..7) of this wave for the step starting at reduction index k0;
     // rows at or past the reduction length read as zero.
     __device__ __forceinline__ void issue(char *unit, int64_t k0, int64_t red, int wave, int lane, int j) {
-        const rsrc_t rs = make_rsrc(base + k0 * ldb);
+        const rsrc_t rs = make_rsrc(row(k0));
         const int k = ((wave * 8 + j) * 1024 + lane * 16) >> 9;
         copy16(rs, unit + (wave * 8 + j) * 1024, (k0 + k < red) ? voff[j] : kOOB);
     }
 
     __device__ __forceinline__ void issue_aligned(char *unit, int64_t k0, bool valid, int wave, int j) {
-        copy16(make_rsrc(base + k0 * ldb, valid ? kNumRecords : 0u), unit + (wave * 8 + j) * 1024, voff[j]);
+        copy16(make_rsrc(row(k0), valid ? kNumRecords : 0u), unit + (wave * 8 + j) * 1024, voff[j]);
     }
 
     // Fragment reads.  Fragment f (0..3) of substep ks holds columns
@@ -359,6 +372,7 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     OperandT<P_RS> po;
     qo.init(static_cast<const uint16_t *>(a.Q), a.ldq, q0, a.cols, wave, lane);
     po.init(static_cast<const uint16_t *>(a.P), a.ldp, p0, a.rows, wave, lane);
+    if constexpr (Q_RS) qo.set_split(a.Q2, a.qsplit, q0);
     qo.init_reads(wq, lane);
     po.init_reads(wp, lane);
 

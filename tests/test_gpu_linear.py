@@ -188,8 +188,11 @@ def test_gradient_in_weight_slot_matches_separate_slots():
     ins = run_fwd_bwd(T, K, M, N, d, "f16", X, Wt, dY, budget=d * tile)
     assert sep["info"].dw_slots == 2 and ins["info"].dw_slots == 0
     assert torch.equal(sep["Y"], ins["Y"])
-    assert torch.equal(sep["dX"], ins["dX"])
     assert torch.equal(sep["dWt"], ins["dWt"])
+    # with separate gradient slots the dX products of tiles 2j, 2j+1 are one
+    # launch, so dX is summed in another order: equal up to fp32 rounding
+    err = (sep["dX"] - ins["dX"]).abs().max().item()
+    assert err <= 1e-5 * ins["dX"].abs().max().item(), err
 
 
 @pytest.mark.parametrize("d2h_cus", [0, 8, 32])
@@ -217,6 +220,22 @@ def test_copy_stream_cu_count_checked():
     for good in (8, cus):
         s = zi.zi_copy_stream_create(good)
         zi.zi_stream_destroy(s)
+
+
+@pytest.mark.parametrize("N,d", [(3, 2), (5, 3), (6, 2)])
+def test_paired_dx_odd_and_even_tile_counts(N, d):
+    # n = 512 (a multiple of the kernel step): dX of tile pairs in one launch,
+    # an odd last tile alone; small integers keep every result exact
+    T, K, n = 128, 512, 512
+    M = N * n
+    say("case paired dX N", N, "d", d)
+    X, Wt, dY = make_linear_inputs(T, K, M, "f16", "small_int", seed=11)
+    r = run_fwd_bwd(T, K, M, N, d, "f16", X, Wt, dY)
+    assert r["info"].dw_slots == 2
+    Y, dX, dWt = oracle_linear(X, Wt, dY, "f16")
+    assert np.array_equal(host_bits(r["Y"]), oracle.encode(Y, "f16"))
+    assert np.array_equal(r["dX"].cpu().numpy().astype(np.float64), dX)
+    assert np.array_equal(host_bits(r["dWt"]), oracle.encode(dWt, "f16"))
 
 
 def test_consecutive_calls_share_the_ring():
