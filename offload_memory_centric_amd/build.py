@@ -31,13 +31,44 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def device_asm(src: str = "zi_kernels.hip") -> str:
+    """Path of the gfx950 assembly that the build keeps for a HIP source."""
+    stem = os.path.splitext(os.path.basename(src))[0]
+    return os.path.join(OBJDIR, "%s-hip-amdgcn-amd-amdhsa-%s.s" % (stem, ARCH))
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc()] + COMMON + DEVICE + ["-c", os.path.join(CSRC, src), "-o", obj]
+    # HIP sources keep their intermediate files next to the object, so that
+    # the device assembly that went into the object can be checked.
+    temps = ["-save-temps=obj"] if src.endswith(".hip") else []
+    cmd = [_hipcc()] + COMMON + DEVICE + temps + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("compile failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
+    if temps:
+        keep = device_asm(src)
+        stem = os.path.splitext(os.path.basename(src))[0]
+        for f in os.listdir(OBJDIR):
+            if f.startswith(stem + "-") or f.startswith(os.path.basename(src) + "-"):
+                if os.path.join(OBJDIR, f) != keep:
+                    os.remove(os.path.join(OBJDIR, f))
     return obj
+
+
+def check_device_asm(src: str = "zi_kernels.hip") -> None:
+    """Fail unless the kernels' matrix-core instructions keep their required
+    wait states (the MFMAs are inline assembly, which the compiler does not
+    pad)."""
+    from . import asm_check
+    path = device_asm(src)
+    res = asm_check.check_file(path)
+    bad = {k: v for k, v in res.items() if v}
+    if not res:
+        raise RuntimeError("no kernels found in %s" % path)
+    if bad:
+        lines = ["%s: %s" % (k, v[0]) for k, v in bad.items()]
+        raise RuntimeError("MFMA wait-state check failed in %d kernels:\n%s" % (len(bad), "\n".join(lines)))
 
 
 def build(verbose: bool = False) -> str:
@@ -50,6 +81,7 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
+    check_device_asm()
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -152,18 +152,18 @@ struct RcOperand {
         copy16(make_rsrc(base + k0 * 2, valid ? kNumRecords : 0u), unit + (wave * 8 + j) * 1024, voff[j]);
     }
 
-    // Fragment reads.  Fragment f (0..3) of substep ks holds rows
-    // wq * 128 + 32 f + (lane & 31) and reduction values 16 ks + 8 (lane >> 5)
-    // .. +7: one 16-byte read.  Its address is the unit's, plus a per-lane part
-    // that depends on ks only through the swizzle (flo[ks], fixed for the
-    // kernel), plus 32 f rows (a constant): one add per substep.
+    // Fragment reads (v_mfma_f32_16x16x32).  Fragment f (0..7) of substep ks
+    // holds rows wq * 128 + 16 f + (lane & 15) and reduction values
+    // 32 ks + 8 (lane >> 4) .. +7: one 16-byte read.  Its address is the
+    // unit's, plus a per-lane part that depends on ks only through the
+    // swizzle (flo[ks], fixed for the kernel), plus 16 f rows (a constant).
     static constexpr int kReadsPerFrag = 1;
-    uint32_t flo[4];
+    uint32_t flo[2];
     __device__ __forceinline__ void init_reads(int wq, int lane) {
-        const int r = lane & 31;  // the swizzle sees r modulo 32
+        const int r = lane & 15;  // the swizzle sees r modulo 16
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            flo[ks] = (uint32_t)((wq * 128 + r) * 128 + (chunk_pos(r, ks * 2 + (lane >> 5)) << 4));
+        for (int ks = 0; ks < 2; ++ks)
+            flo[ks] = (uint32_t)((wq * 128 + r) * 128 + (chunk_pos(r, ks * 4 + (lane >> 4)) << 4));
     }
     // Per-lane base of the reads of substep ks in the unit at LDS address
     // `unit`: one add, hidden from the optimiser so that the constant parts of
@@ -174,16 +174,17 @@ struct RcOperand {
         asm volatile("" : "+v"(r.b));
         return r;
     }
-    __device__ __forceinline__ static void frag(const Bases &b, int ks, int f, int t, u32x4 &out) {
+    __device__ __forceinline__ void frag(const Bases &b, int ks, int f, u32x4 &out) const {
         (void)ks;
-        (void)t;
-        out = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((uintptr_t)(b.b + f * 32 * 128));
+        out = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((uintptr_t)(b.b + f * 16 * 128));
     }
 };
 
 // Reduction-strided operand, element (r, k) at M[k * ld + r].  LDS rows of 256
 // elements (512 B, sixteen 32-byte segments) per reduction index k; segment s
-// of row k sits at s ^ 2 (k & 3).
+// of row k sits at s ^ ((k & 3) | ((k >> 1) & 4)), so that the eight rows one
+// transposing read touches (k = 8 h + 4 t + 0..3 for two h) fall on eight
+// different bank groups.
 struct RsOperand {
     const char *base;   // &M[r0]
     const char *base2;  // &M2[r0]: reduction rows from `split` on (split = 0: none)
@@ -200,7 +201,7 @@ struct RsOperand {
         return (split && k0 >= split) ? base2 + (k0 - split) * ldb : base + k0 * ldb;
     }
 
-    __device__ __forceinline__ static int seg_pos(int k, int s) { return s ^ ((k & 3) << 1); }
+    __device__ __forceinline__ static int seg_pos(int k, int s) { return s ^ ((k & 3) | ((k >> 1) & 4)); }
 
     __device__ __forceinline__ void init(const uint16_t *M, int64_t ld, int64_t r0, int64_t rext,
                                          int wave, int lane) {
@@ -230,41 +231,44 @@ struct RsOperand {
         copy16(make_rsrc(row(k0), valid ? kNumRecords : 0u), unit + (wave * 8 + j) * 1024, voff[j]);
     }
 
-    // Fragment reads.  Fragment f (0..3) of substep ks holds columns
-    // wq * 128 + 32 f + .. 31 and reduction values 16 ks + 8 (lane >> 5) .. +7:
-    // two transposing reads of 4 values each (t = 0, 1), each filling half of
-    // `out`.  The segment swizzle mixes f into the per-lane address but not ks
-    // or t, so the address is the unit's plus flo[f] (fixed for the kernel)
-    // plus (16 ks + 4 t) rows of 512 bytes (a constant).
+    // Fragment reads (v_mfma_f32_16x16x32).  Fragment f (0..7) of substep ks
+    // holds columns wq * 128 + 16 f + (lane & 15) and reduction values
+    // 32 ks + 8 (lane >> 4) .. +7: two transposing reads of 4 values each
+    // (rows 0..3 and 4..7 of the lane's eight), issued together.  ds_read_b64_tr_b16 hands lane j
+    // of each 16 the (j % 4)-th of the 4 values read by lanes 4e + j / 4
+    // (e = 0..3); pointing those lanes at 4 consecutive rows x 4 four-column
+    // groups gives lane j 4 consecutive reduction values of column j.  The
+    // swizzle mixes f into the per-lane address but not ks or t, so the
+    // address is the unit's plus flo[f] (fixed for the kernel) plus
+    // (32 ks + 4 t) rows of 512 bytes (a constant).
     static constexpr int kReadsPerFrag = 2;
-    uint32_t flo[4];
+    uint32_t flo[8];
     __device__ __forceinline__ void init_reads(int wq, int lane) {
-        const int h = lane >> 4;
         const int s = lane & 15;
-        const int kl = 8 * (h >> 1) + (s >> 2);
+        const int kl = 8 * (lane >> 4) + (s >> 2);
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            const int r = wq * 128 + f * 32 + 16 * (h & 1) + 4 * (s & 3);
+        for (int f = 0; f < 8; ++f) {
+            const int r = wq * 128 + f * 16 + 4 * (s & 3);
             flo[f] = (uint32_t)(kl * 512 + (seg_pos(kl, r >> 4) << 5) + (r & 15) * 2);
         }
     }
-    struct Bases { uint32_t b[4]; };
+    // The reads of one fragment share a per-lane base, formed right before
+    // them (one add) and hidden from the optimiser so that the constant parts
+    // of the addresses stay in the instructions' offset fields.
+    struct Bases { uint32_t unit; };
     __device__ __forceinline__ Bases bases(uint32_t unit, int ks) const {
         (void)ks;
-        Bases r;
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            r.b[f] = unit + flo[f];
-            asm volatile("" : "+v"(r.b[f]));
-        }
-        return r;
+        return Bases{unit};
     }
-    __device__ __forceinline__ static void frag(const Bases &b, int ks, int f, int t, u32x4 &out) {
-        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(uintptr_t)(b.b[f] + (16 * ks + 4 * t) * 512));
-        const u32x2 w = __builtin_bit_cast(u32x2, v);
-        out[2 * t] = w[0];
-        out[2 * t + 1] = w[1];
+    __device__ __forceinline__ void frag(const Bases &b, int ks, int f, u32x4 &out) const {
+        uint32_t base = b.unit + flo[f];
+        asm volatile("" : "+v"(base));
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(uintptr_t)(base + (32 * ks) * 512));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(uintptr_t)(base + (32 * ks + 4) * 512));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+        out = u32x4{w0[0], w0[1], w1[0], w1[1]};
     }
 };
 
@@ -286,19 +290,48 @@ __device__ __forceinline__ void wait_and_barrier() {
 
 // ---- MFMA ------------------------------------------------------------------------
 
+// v_mfma_f32_16x16x32: A (16 x 32) and B (32 x 16) give each lane 8 values
+// (lane l: row / column l % 16, reduction values 8 (l / 16) .. +7); the 16 x 16
+// fp32 result gives lane l column l % 16, rows 4 (l / 16) .. +3.  Per FLOP it
+// moves half the accumulator traffic of the 32 x 32 x 16 form, and under the
+// power limit it sustains ~17 % more FLOP/s on random data.
+//
+// Written as inline assembly with the accumulator tied to an AGPR tuple:
+// with 64 small accumulators the register allocator otherwise moves them
+// between registers inside the loop.  The compiler does not see these as
+// MFMAs, so the wait states it would insert around them are written out
+// where they matter (mfma_fence): before the accumulators are first used and
+// before the epilogue reads them.  Inside the loop an accumulator is reused
+// only 64 MFMAs later, far beyond any dependency latency.  The build checks
+// the compiled code for these wait states.
 template <typename T>
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c);
 
-template <>
-__device__ __forceinline__ f32x16 mfma32<_Float16>(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+// A point that every write of the accumulators comes before and every read
+// after, with more than the longest XDL-result latency of wait states
+// (NOPS_FIRST: at its start, else at its end).  Eight volatile statements,
+// which keep their order, each tied to one row of accumulators.
+template <bool NOPS_FIRST>
+__device__ __forceinline__ void mfma_fence(f32x4 (&acc)[8][8]) {
+    if constexpr (NOPS_FIRST) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        asm volatile(""
+                     : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                       "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+    if constexpr (!NOPS_FIRST) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
 template <>
-__device__ __forceinline__ f32x16 mfma32<__bf16>(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma16<_Float16>(u32x4 a, u32x4 b, f32x4 c) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    return c;
+}
+
+template <>
+__device__ __forceinline__ f32x4 mfma16<__bf16>(u32x4 a, u32x4 b, f32x4 c) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    return c;
 }
 
 // ---- conversions and GeLU ---------------------------------------------------------
@@ -349,6 +382,17 @@ __device__ __forceinline__ void tile_coords(int w, int tiles_p, int tiles_q, int
 
 // ---- the GEMM ---------------------------------------------------------------------
 
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled by construction (a
+// large loop body can exceed the unroller's size limit, and a rolled loop
+// would index the accumulators at run time).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 template <bool RS>
 using OperandT = typename std::conditional<RS, RsOperand, RcOperand>::type;
 
@@ -388,9 +432,9 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     // matrix unit idles.
     const int64_t ksteps = (a.red + BK - 1) / BK;
     const int64_t nunits = 2 * ksteps;
-    auto slot = [&](int64_t u) -> char * { return lds + ((uint32_t)u % kUnits) * kUnitBytes; };
+    auto slot = [&](int64_t u) __attribute__((always_inline)) -> char * { return lds + ((uint32_t)u % kUnits) * kUnitBytes; };
     // copy j of unit u into slot st (zeros past the last unit)
-    auto copy_to = [&](char *st, int64_t u, int j) {
+    auto copy_to = [&](char *st, int64_t u, int j) __attribute__((always_inline)) {
         const int64_t k0 = (u >> 1) * BK;
         if constexpr (ALIGNED) {
             const bool valid = u < nunits;
@@ -405,60 +449,82 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
                 qo.issue(st, k0, a.red, wave, lane, j);
         }
     };
-    auto copy = [&](int64_t u, int j) { copy_to(slot(u), u, j); };
+    auto copy = [&](int64_t u, int j) __attribute__((always_inline)) { copy_to(slot(u), u, j); };
 
     using QOp = OperandT<Q_RS>;
     using POp = OperandT<P_RS>;
-    constexpr int QR = QOp::kReadsPerFrag, PR = POp::kReadsPerFrag;
-    constexpr int kReads = 4 * QR + 4 * PR;  // LDS read instructions per substep
-
-    // Read r of a substep, in the order its MFMAs consume the fragments:
-    // Q0, P0..P3, Q1..Q3.
     using QB = typename QOp::Bases;
     using PB = typename POp::Bases;
-    auto read = [&](int r, const QB &qb, const PB &pb, int ks, u32x4 (&ya)[4], u32x4 (&yb)[4]) {
-        if (r < QR) {
-            QOp::frag(qb, ks, 0, r, ya[0]);
-        } else if (r < QR + 4 * PR) {
-            const int f = (r - QR) / PR;
-            POp::frag(pb, ks, f, (r - QR) % PR, yb[f]);
+
+    // acc[i][j]: the 16 x 16 block of q-block i and p-block j of this wave.
+    // Register e of block (i, j) holds C[p][q] with
+    // p = p0 + wp 128 + 16 j + (lane & 15), q = q0 + wq 128 + 16 i + 4 (lane >> 4) + e.
+    // An accumulating product starts from C, so its epilogue is a plain
+    // store.  C is loaded straight into the accumulator registers (every
+    // lane, every block: out-of-range elements, and all of them when not
+    // accumulating, come back as zeros from the buffer unit), issued before
+    // the first operand copies, so the prologue's wait for the first two
+    // units (vmcnt counts loads in issue order) covers it too.  Row block j
+    // has its own descriptor, so a lane offset stays below 16 ldc + 256
+    // elements (the host keeps that under the descriptor's range).
+    const int64_t pb = p0 + wp * 128 + (lane & 15);
+    const int64_t qb = q0 + wq * 128 + 4 * (lane >> 4);
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if constexpr (EPI == EPI_ACC) {
+            const int64_t prow = p0 + wp * 128 + 16 * j;
+            const rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(static_cast<const float *>(a.C) + prow * a.ldc + q0),
+                                        a.accumulate ? kNumRecords : 0u);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int64_t p = pb + j * 16, q = qb + i * 16;
+                const uint32_t off =
+                    (p < a.rows && q < a.cols) ? (uint32_t)(((lane & 15) * a.ldc + (q - q0)) * 4) : kOOB;
+                asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=a"(acc[i][j]) : "v"(off), "s"(rs) : "memory");
+            }
         } else {
-            const int f = 1 + (r - QR - 4 * PR) / QR;
-            QOp::frag(qb, ks, f, (r - QR - 4 * PR) % QR, ya[f]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i][j] = f32x4{};
         }
-    };
+    }
 
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-    // One substep: 16 MFMAs on (xa, xb); between them the reads of the next
-    // substep (stage qs/ps, substep ks, into ya/yb) and `ncopy` copies.
-    auto substep = [&](const u32x4 (&xa)[4], const u32x4 (&xb)[4], u32x4 (&ya)[4], u32x4 (&yb)[4],
-                       const char *qs, const char *ps, int ks, bool reads, int ncopy, auto &&copy_c) {
+    // Fragments.  MFMA m of a substep multiplies Q fragment m / 8 with P
+    // fragment m % 8.  Q fragment i < 7 is dead after MFMA 8 i + 7, so the
+    // next substep's Q fragment i is read into the same registers right after
+    // it; Q fragment 7 and the P fragments are used to the end of the substep
+    // and are double-buffered (parity `par` of the substep).  P reads are
+    // spread over the first half of the substep.  One substep covers 32
+    // reduction values; `ncopy` copies are spread evenly between its MFMAs.
+    u32x4 xq[7], xq7[2], xp[2][8];
+    auto substep = [&](auto PAR, const char *qs, const char *ps, int ks, bool reads, int ncopy, auto &&copy_c) __attribute__((always_inline)) {
+        constexpr int par = decltype(PAR)::value;
         QB qb{};
         PB pb{};
         if (reads) {
             qb = qo.bases(lds_addr(qs), ks);
             pb = po.bases(lds_addr(ps), ks);
         }
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            acc[m >> 2][m & 3] = mfma32<T>(xa[m >> 2], xb[m & 3], acc[m >> 2][m & 3]);
+        static_for<0, 64>([&](auto M_) __attribute__((always_inline)) {
+            constexpr int m = decltype(M_)::value;
+            constexpr int i = m >> 3, j = m & 7;
+            if constexpr (i < 7)
+                acc[i][j] = mfma16<T>(xq[i], xp[par][j], acc[i][j]);
+            else
+                acc[i][j] = mfma16<T>(xq7[par], xp[par][j], acc[i][j]);
             if (reads) {
-#pragma unroll
-                for (int r = (m * kReads + 15) / 16; r < ((m + 1) * kReads + 15) / 16; ++r)
-                    read(r, qb, pb, ks, ya, yb);
+                if constexpr (m % 4 == 1 && m < 32) po.frag(pb, ks, m / 4, xp[par ^ 1][m / 4]);  // P0..P7
+                if constexpr (m % 8 == 7 && m < 56) qo.frag(qb, ks, m / 8, xq[m / 8]);          // Q0..Q6
+                if constexpr (m == 34) qo.frag(qb, ks, 7, xq7[par ^ 1]);                         // Q7
             }
-            if (ncopy > 0 && m % (16 / ncopy) == (16 / ncopy) / 2) copy_c(m / (16 / ncopy));
+            if (ncopy > 0 && m % (64 / ncopy) == (64 / ncopy) / 2) copy_c(m / (64 / ncopy));
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     };
-    auto no_copy = [](int) {};
+    auto no_copy = [](int) __attribute__((always_inline)) {};
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
 
-    u32x4 fa[2][4], fb[2][4];
     // prologue: units 0..3 in flight, wait for the two of step 0
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -473,71 +539,65 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
         const QB qb = qo.bases(lds_addr(slot(0)), 0);
         const PB pb = po.bases(lds_addr(slot(1)), 0);
 #pragma unroll
-        for (int r = 0; r < kReads; ++r) read(r, qb, pb, 0, fa[0], fb[0]);
+        for (int f = 0; f < 7; ++f) qo.frag(qb, 0, f, xq[f]);
+        qo.frag(qb, 0, 7, xq7[0]);
+#pragma unroll
+        for (int f = 0; f < 8; ++f) po.frag(pb, 0, f, xp[0][f]);
     }
 
-    // substeps 0..2 of step kt, unit 2 kt + 4 copied under substeps 0 and 1
-    auto first_three = [&](int64_t kt) {
-        const char *qs = slot(2 * kt), *ps = slot(2 * kt + 1);
+    mfma_fence<false>(acc);  // accumulator writes, then the first MFMA
+
+    // substep 0 of step kt; unit 2 kt + 4 is copied under it
+    auto first_half = [&](int64_t kt) __attribute__((always_inline)) {
         const int64_t u = 2 * kt + 4;
-        substep(fa[0], fb[0], fa[1], fb[1], qs, ps, 1, true, 4, [&](int c) { copy(u, c); });
-        substep(fa[1], fb[1], fa[0], fb[0], qs, ps, 2, true, 4, [&](int c) { copy(u, 4 + c); });
-        substep(fa[0], fb[0], fa[1], fb[1], qs, ps, 3, true, 0, no_copy);
+        substep(P0{}, slot(2 * kt), slot(2 * kt + 1), 1, true, 8, [&](int c) __attribute__((always_inline)) { copy(u, c); });
     };
-    int64_t kt = 0;
-    for (; kt + 1 < ksteps; ++kt) {
-        first_three(kt);
-        // step kt + 1 must have landed; unit 2 kt + 4 may still be in flight
+    // Every MFMA sits in this loop.  Its last pass reads fragments of a
+    // step past the end (slots that hold zeros or stale data) and copies past
+    // the end; nothing uses them.  A tail outside the loop would let the
+    // register allocator place accumulator copies between the MFMAs, which
+    // it cannot see as such and so would not separate by the wait states
+    // they need.
+    for (int64_t kt = 0; kt < ksteps; ++kt) {
+        first_half(kt);
+        // every wave has read all of step kt, and step kt + 1 must have
+        // landed; unit 2 kt + 4 may still be in flight
         wait_and_barrier<8>();
         const int64_t u = 2 * kt + 5;
-        substep(fa[1], fb[1], fa[0], fb[0], slot(2 * kt + 2), slot(2 * kt + 3), 0, true, 8,
-                [&](int c) { copy(u, c); });
+        substep(P1{}, slot(2 * kt + 2), slot(2 * kt + 3), 0, true, 8, [&](int c) __attribute__((always_inline)) { copy(u, c); });
     }
-    first_three(ksteps - 1);
-    substep(fa[1], fb[1], fa[0], fb[0], nullptr, nullptr, 0, false, 0, no_copy);
+    mfma_fence<true>(acc);  // the last MFMA, then accumulator reads
     // the copies past the last unit are still in flight: none may land after
     // the workgroup has released its LDS
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // Epilogue.  Accumulator register 4g + e of block (i, j) holds
-    // C[p][q] with p = j-block row (lane & 31) and q = 8 g + 4 (lane >> 5) + e.
-    const int64_t pb = p0 + wp * 128 + (lane & 31);
-    const int64_t qb = q0 + wq * 128 + 4 * (lane >> 5);
+    // Epilogue.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
+        const int64_t q = qb + i * 16;
+        if (q >= a.cols) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t p = pb + j * 32;
+        for (int j = 0; j < 8; ++j) {
+            const int64_t p = pb + j * 16;
             if (p >= a.rows) continue;
+            f32x4 v = acc[i][j];
+            const int64_t off = p * a.ldc + q;
+            if constexpr (EPI == EPI_F32 || EPI == EPI_ACC) {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(a.C) + off) = v;
+            } else if constexpr (EPI == EPI_LP) {
+                u32x2 o = {bits16<T>(v[0]) | (bits16<T>(v[1]) << 16), bits16<T>(v[2]) | (bits16<T>(v[3]) << 16)};
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.C) + off) = o;
+            } else {  // EPI_GELU: A = RNE(acc); H = RNE(GeLU(A))
+                uint32_t b[4], h[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t q = qb + i * 32 + 8 * g;
-                if (q >= a.cols) continue;
-                f32x4 v = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                           acc[i][j][4 * g + 3]};
-                const int64_t off = p * a.ldc + q;
-                if constexpr (EPI == EPI_F32) {
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(a.C) + off) = v;
-                } else if constexpr (EPI == EPI_ACC) {
-                    f32x4 *c = reinterpret_cast<f32x4 *>(static_cast<float *>(a.C) + off);
-                    if (a.accumulate) v += *c;
-                    *c = v;
-                } else if constexpr (EPI == EPI_LP) {
-                    u32x2 o = {bits16<T>(v[0]) | (bits16<T>(v[1]) << 16),
-                               bits16<T>(v[2]) | (bits16<T>(v[3]) << 16)};
-                    *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.C) + off) = o;
-                } else {  // EPI_GELU: A = RNE(acc); H = RNE(GeLU(A))
-                    uint32_t b[4], h[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        b[e] = bits16<T>(v[e]);
-                        h[e] = bits16<T>(gelu_f32(value16<T>(b[e])));
-                    }
-                    *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.C) + off) =
-                        u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
-                    *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.C2) + off) =
-                        u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                for (int e = 0; e < 4; ++e) {
+                    b[e] = bits16<T>(v[e]);
+                    h[e] = bits16<T>(gelu_f32(value16<T>(b[e])));
                 }
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.C) + off) =
+                    u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.C2) + off) =
+                    u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
             }
         }
     }
@@ -578,6 +638,9 @@ hipError_t run(const GemmArgs &a, hipStream_t s) {
     const int tiles_q = (int)((a.cols + kTileQ - 1) / kTileQ);
     const int64_t nt = (int64_t)tiles_p * tiles_q;
     if (nt <= 0) return hipSuccess;
+    if (a.red < 1) return hipErrorInvalidValue;
+    // the accumulating epilogue addresses 16 rows of C through one descriptor
+    if (EPI == EPI_ACC && (a.ldc < 0 || (16 * a.ldc + 256) * 4 >= (int64_t)kNumRecords)) return hipErrorInvalidValue;
     if (a.red % BK == 0)
         hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, true>), dim3((unsigned)nt), dim3(kThreads), 0, s,
                            a, tiles_p, tiles_q);
