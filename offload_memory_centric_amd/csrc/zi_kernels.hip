@@ -12,8 +12,8 @@
 // four consecutive q, and every epilogue store is one 8- or 16-byte vector.
 //
 // Workgroup: 256 threads = 4 wave64s in a 2 x 2 arrangement over a
-// 256 (p) x 256 (q) macro-tile; each wave owns 128 x 128 = 4 x 4 MFMA blocks
-// of 32 x 32 (v_mfma_f32_32x32x16_{f16,bf16}, fp32 accumulators: 256 per lane,
+// 256 (p) x 256 (q) macro-tile; each wave owns 128 x 128 = 8 x 8 MFMA blocks
+// of 16 x 16 (v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulators: 256 per lane,
 // so the kernel runs one wave per SIMD).
 //
 // Memory pipeline.  With one wave per SIMD nothing hides a wait except work
@@ -33,8 +33,8 @@
 //     ds_read_b128 per lane;
 //   * reduction-strided operand: kept in its natural layout, rows of 256
 //     elements (512 B, sixteen 32-byte segments) per reduction index k;
-//     segment s of row k sits at s ^ 2 (k & 3); a fragment is two
-//     ds_read_b64_tr_b16 per lane.  That instruction, per 16 lanes, hands lane
+//     segment s of row k sits at s ^ ((k & 3) | ((k >> 1) & 4)); a fragment
+//     is two ds_read_b64_tr_b16 per lane.  That instruction, per 16 lanes, hands lane
 //     j the (j % 4)-th element read by lanes 4e + j / 4 (e = 0..3); pointing
 //     those 16 lanes at 4 consecutive rows x 4 four-element column groups gives
 //     each lane 4 consecutive reduction values of one column: the MFMA layout.
@@ -56,10 +56,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 constexpr int BK = kGemmStep;                        // reduction elements per step
@@ -421,15 +418,16 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     po.init_reads(wp, lane);
 
     // Operand units: Q of step k is unit 2k, P of step k is unit 2k + 1; unit u
-    // lives in slot u % kUnits.  A step is four substeps of 16 reduction values
-    // (16 MFMAs each).  Under substeps 0 and 1 of step k the waves copy unit
-    // 2k + 4 (into the slot step k - 1 has released); at the end of substep 2
+    // lives in slot u % kUnits.  A step is two substeps of 32 reduction values
+    // (64 MFMAs each); the fragments of a substep are read from LDS during the
+    // one before.  Under substep 0 of step k the waves copy unit 2k + 4 (into
+    // the slot step k - 1 has released) and read substep 1 of step k; then
     // every wave has read all of step k, and once step k + 1 has landed they
-    // meet at a barrier; under substep 3 they copy unit 2k + 5 into the slot of
-    // unit 2k.  So while step k is multiplied, up to three units are in flight.
-    // Copies and the fragment reads of the next substep are spread evenly
-    // between the MFMAs, so that no wave stalls on a burst of copies while its
-    // matrix unit idles.
+    // meet at a barrier; under substep 1 they copy unit 2k + 5 into the slot of
+    // unit 2k and read substep 0 of step k + 1.  So while step k is multiplied,
+    // up to three units are in flight.  Copies and fragment reads are spread
+    // evenly between the MFMAs, so that no wave stalls on a burst of copies
+    // while its matrix unit idles.
     const int64_t ksteps = (a.red + BK - 1) / BK;
     const int64_t nunits = 2 * ksteps;
     auto slot = [&](int64_t u) __attribute__((always_inline)) -> char * { return lds + ((uint32_t)u % kUnits) * kUnitBytes; };
