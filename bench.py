@@ -253,22 +253,37 @@ def main():
         plans = (p,)
     torch.cuda.synchronize()
 
+    # Per-step marks: an event on the compute stream after every step (no
+    # host synchronisation, so the ring's prefetch still crosses steps).
+    comp = torch.cuda.ExternalStream(ctx.streams[0])
+
+    def marked(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record(comp)
+        for i in range(n):
+            step()
+            ev[i + 1].record(comp)
+        return ev
+
+    def spans(ev):
+        return [round(ev[i].elapsed_time(ev[i + 1]), 3) for i in range(len(ev) - 1)]
+
     # ---------------- warmup ----------------
-    for _ in range(args.warmup):
-        step()
+    wev = marked(args.warmup)
     ctx.sync()
     torch.cuda.synchronize()
+    warm_ms = spans(wev)
 
     # ---------------- timed steps ----------------
     ctx.set_timing(True)
     ctx.reset_stats()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    tev = marked(args.steps)
     ctx.sync()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_ms = spans(tev)
     st = ctx.stats()
     ctx.set_timing(False)
 
@@ -318,6 +333,8 @@ def main():
         "data": "synthetic (seeded Gaussian: X, dY ~ N(0,1), W ~ N(0, 0.02^2))",
         "config": config,
         "pct_mfma_peak": round(100.0 * tflops * 1e12 / PEAK_MFMA_F16, 2),
+        "step_ms": step_ms,
+        "warmup_step_ms": warm_ms,
         "exposed_stall_pct": round(100.0 * stall, 2),
         "h2d_GBps_achieved": round(h2d_rate / 1e9, 2),
         "d2h_GBps_achieved": round(d2h_rate / 1e9, 2),

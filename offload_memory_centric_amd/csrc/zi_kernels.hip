@@ -21,12 +21,12 @@
 // operand is copied global -> LDS by the buffer unit (buffer_load ... lds,
 // 16 bytes per lane), which needs no registers.  A step covers BK = 64
 // reduction elements; one operand of one step (32 KiB) is a "unit", and the
-// LDS holds a ring of five units (160 KiB): while step k is multiplied, the
-// units of step k + 1 and the first of step k + 2 are in flight, and as soon
-// as every wave has finished reading step k its two slots take the next two
-// units.  Each wave waits only for the units it needs next (s_waitcnt vmcnt(N)
-// with N = the copies still allowed in flight), meets the others at one
-// barrier, and reads MFMA fragments from LDS:
+// LDS holds a ring of five units (160 KiB).  While step s is multiplied (from
+// registers), the fragments of step s + 1 are read from its two units and
+// the next units are in flight: step s + 2's pair and the first unit of step
+// s + 3.  Each wave waits only for the units it needs next (s_waitcnt
+// vmcnt(N) with N = the copies still allowed in flight), meets the others at
+// one barrier per step, and reads MFMA fragments from LDS:
 //   * reduction-contiguous operand: rows of 64 reduction values (128 B, eight
 //     16-byte chunks), so eight lanes fetch one whole 128-byte line of global
 //     memory; chunk c of row r sits at c ^ ((r >> 1) & 7); a fragment is one
@@ -149,9 +149,9 @@ struct RcOperand {
         copy16(make_rsrc(base + k0 * 2, valid ? kNumRecords : 0u), unit + (wave * 8 + j) * 1024, voff[j]);
     }
 
-    // Fragment reads (v_mfma_f32_16x16x32).  Fragment f (0..7) of substep ks
-    // holds rows wq * 128 + 16 f + (lane & 15) and reduction values
-    // 32 ks + 8 (lane >> 4) .. +7: one 16-byte read.  Its address is the
+    // Fragment reads (v_mfma_f32_16x16x32).  Fragment f (0..7) of half ks
+    // (0, 1) of a step holds rows wq * 128 + 16 f + (lane & 15) and reduction
+    // values 32 ks + 8 (lane >> 4) .. +7: one 16-byte read.  Its address is the
     // unit's, plus a per-lane part that depends on ks only through the
     // swizzle (flo[ks], fixed for the kernel), plus 16 f rows (a constant).
     static constexpr int kReadsPerFrag = 1;
@@ -162,7 +162,7 @@ struct RcOperand {
         for (int ks = 0; ks < 2; ++ks)
             flo[ks] = (uint32_t)((wq * 128 + r) * 128 + (chunk_pos(r, ks * 4 + (lane >> 4)) << 4));
     }
-    // Per-lane base of the reads of substep ks in the unit at LDS address
+    // Per-lane base of the reads of half ks in the unit at LDS address
     // `unit`: one add, hidden from the optimiser so that the constant parts of
     // the addresses stay in the instructions' offset fields.
     struct Bases { uint32_t b; };
@@ -217,19 +217,22 @@ struct RsOperand {
     }
 
     // Copy j (0..7) of this wave for the step starting at reduction index k0;
-    // rows at or past the reduction length read as zero.
+    // rows at or past the reduction length read as zero.  Row k of the unit
+    // lies in bytes [k ldb, (k + 1) ldb) from row(k0), so a descriptor that
+    // ends after the last valid row cuts the rest off, with no per-lane select.
     __device__ __forceinline__ void issue(char *unit, int64_t k0, int64_t red, int wave, int lane, int j) {
-        const rsrc_t rs = make_rsrc(row(k0));
-        const int k = ((wave * 8 + j) * 1024 + lane * 16) >> 9;
-        copy16(rs, unit + (wave * 8 + j) * 1024, (k0 + k < red) ? voff[j] : kOOB);
+        (void)lane;
+        const int64_t rem = red - k0;  // valid rows from k0 on (none past the end)
+        const uint32_t records = rem <= 0 ? 0u : (rem >= kGemmStep ? kNumRecords : (uint32_t)(rem * ldb));
+        copy16(make_rsrc(row(k0), records), unit + (wave * 8 + j) * 1024, voff[j]);
     }
 
     __device__ __forceinline__ void issue_aligned(char *unit, int64_t k0, bool valid, int wave, int j) {
         copy16(make_rsrc(row(k0), valid ? kNumRecords : 0u), unit + (wave * 8 + j) * 1024, voff[j]);
     }
 
-    // Fragment reads (v_mfma_f32_16x16x32).  Fragment f (0..7) of substep ks
-    // holds columns wq * 128 + 16 f + (lane & 15) and reduction values
+    // Fragment reads (v_mfma_f32_16x16x32).  Fragment f (0..7) of half ks
+    // (0, 1) of a step holds columns wq * 128 + 16 f + (lane & 15) and reduction values
     // 32 ks + 8 (lane >> 4) .. +7: two transposing reads of 4 values each
     // (rows 0..3 and 4..7 of the lane's eight), issued together.  ds_read_b64_tr_b16 hands lane j
     // of each 16 the (j % 4)-th of the 4 values read by lanes 4e + j / 4
@@ -298,9 +301,11 @@ __device__ __forceinline__ void wait_and_barrier() {
 // between registers inside the loop.  The compiler does not see these as
 // MFMAs, so the wait states it would insert around them are written out
 // where they matter (mfma_fence): before the accumulators are first used and
-// before the epilogue reads them.  Inside the loop an accumulator is reused
-// only 64 MFMAs later, far beyond any dependency latency.  The build checks
-// the compiled code for these wait states.
+// before the epilogue reads them.  Inside the loop an accumulator feeds the
+// next MFMA on the same registers directly (back-to-back chaining, which
+// needs no wait states) and is then not touched for 126 MFMAs, far beyond any
+// dependency latency.  The build checks the compiled code for these wait
+// states.
 template <typename T>
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c);
 
@@ -417,17 +422,10 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     qo.init_reads(wq, lane);
     po.init_reads(wp, lane);
 
-    // Operand units: Q of step k is unit 2k, P of step k is unit 2k + 1; unit u
-    // lives in slot u % kUnits.  A step is two substeps of 32 reduction values
-    // (64 MFMAs each); the fragments of a substep are read from LDS during the
-    // one before.  Under substep 0 of step k the waves copy unit 2k + 4 (into
-    // the slot step k - 1 has released) and read substep 1 of step k; then
-    // every wave has read all of step k, and once step k + 1 has landed they
-    // meet at a barrier; under substep 1 they copy unit 2k + 5 into the slot of
-    // unit 2k and read substep 0 of step k + 1.  So while step k is multiplied,
-    // up to three units are in flight.  Copies and fragment reads are spread
-    // evenly between the MFMAs, so that no wave stalls on a burst of copies
-    // while its matrix unit idles.
+    // Operand units: Q of step s is unit 2s, P of step s is unit 2s + 1; unit
+    // u lives in slot u % kUnits.  Copies and fragment reads are spread evenly
+    // between the MFMAs, so that no wave stalls on a burst of copies while its
+    // matrix unit idles.
     const int64_t ksteps = (a.red + BK - 1) / BK;
     const int64_t nunits = 2 * ksteps;
     auto slot = [&](int64_t u) __attribute__((always_inline)) -> char * { return lds + ((uint32_t)u % kUnits) * kUnitBytes; };
@@ -487,82 +485,102 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
         }
     }
 
-    // Fragments.  MFMA m of a substep multiplies Q fragment m / 8 with P
-    // fragment m % 8.  Q fragment i < 7 is dead after MFMA 8 i + 7, so the
-    // next substep's Q fragment i is read into the same registers right after
-    // it; Q fragment 7 and the P fragments are used to the end of the substep
-    // and are double-buffered (parity `par` of the substep).  P reads are
-    // spread over the first half of the substep.  One substep covers 32
-    // reduction values; `ncopy` copies are spread evenly between its MFMAs.
-    u32x4 xq[7], xq7[2], xp[2][8];
-    auto substep = [&](auto PAR, const char *qs, const char *ps, int ks, bool reads, int ncopy, auto &&copy_c) __attribute__((always_inline)) {
+    // Fragments of one step (64 reduction values in two halves h = 0, 1):
+    // Q fragment (i, h) and P fragment (j, h).  Block (i, j) takes its two
+    // MFMAs back to back (h = 0, then h = 1), so the matrix core chains the
+    // second onto the first through its accumulator without a register-file
+    // round trip, which saves power (and so clock) under the board's limit.
+    // MFMA m of a step is block (i, j) = ((m / 2) / 8, (m / 2) % 8), half m % 2.
+    // Q row i is dead after MFMA 16 i + 15, so the next step's Q fragments of
+    // row i are read into the same registers right after it; Q row 7 and the P
+    // fragments are used to the end of the step and are double-buffered
+    // (parity `par` of the step).  P reads are spread over the first half.
+    u32x4 xq[7][2], xq7[2][2], xp[2][8][2];
+    // One step: 128 MFMAs; between them the reads of the next step (from
+    // the slots qs, ps) and 16 copies: copy_a(0..7) in the first half,
+    // copy_b(0..7) in the second.
+    auto step = [&](auto PAR, const char *qs, const char *ps, auto &&copy_a, auto &&copy_b) __attribute__((always_inline)) {
         constexpr int par = decltype(PAR)::value;
-        QB qb{};
-        PB pb{};
-        if (reads) {
-            qb = qo.bases(lds_addr(qs), ks);
-            pb = po.bases(lds_addr(ps), ks);
-        }
-        static_for<0, 64>([&](auto M_) __attribute__((always_inline)) {
+        const QB qb0 = qo.bases(lds_addr(qs), 0), qb1 = qo.bases(lds_addr(qs), 1);
+        const PB pb0 = po.bases(lds_addr(ps), 0), pb1 = po.bases(lds_addr(ps), 1);
+        static_for<0, 128>([&](auto M_) __attribute__((always_inline)) {
             constexpr int m = decltype(M_)::value;
-            constexpr int i = m >> 3, j = m & 7;
+            constexpr int blk = m >> 1, h = m & 1, i = blk >> 3, j = blk & 7;
             if constexpr (i < 7)
-                acc[i][j] = mfma16<T>(xq[i], xp[par][j], acc[i][j]);
+                acc[i][j] = mfma16<T>(xq[i][h], xp[par][j][h], acc[i][j]);
             else
-                acc[i][j] = mfma16<T>(xq7[par], xp[par][j], acc[i][j]);
-            if (reads) {
-                if constexpr (m % 4 == 1 && m < 32) po.frag(pb, ks, m / 4, xp[par ^ 1][m / 4]);  // P0..P7
-                if constexpr (m % 8 == 7 && m < 56) qo.frag(qb, ks, m / 8, xq[m / 8]);          // Q0..Q6
-                if constexpr (m == 34) qo.frag(qb, ks, 7, xq7[par ^ 1]);                         // Q7
+                acc[i][j] = mfma16<T>(xq7[par][h], xp[par][j][h], acc[i][j]);
+            if constexpr (m % 4 == 1 && m < 64) {  // P fragment (m / 8, (m / 4) % 2) of the next step
+                constexpr int f = m / 8, hh = (m / 4) & 1;
+                po.frag(hh ? pb1 : pb0, hh, f, xp[par ^ 1][f][hh]);
             }
-            if (ncopy > 0 && m % (64 / ncopy) == (64 / ncopy) / 2) copy_c(m / (64 / ncopy));
+            if constexpr (m % 16 == 15 && m < 112) {  // Q row m / 16 of the next step
+                qo.frag(qb0, 0, m / 16, xq[m / 16][0]);
+                qo.frag(qb1, 1, m / 16, xq[m / 16][1]);
+            }
+            if constexpr (m == 66) qo.frag(qb0, 0, 7, xq7[par ^ 1][0]);
+            if constexpr (m == 70) qo.frag(qb1, 1, 7, xq7[par ^ 1][1]);
+            if constexpr (m % 8 == 4) {
+                if constexpr (m < 64)
+                    copy_a(m / 8);
+                else
+                    copy_b((m - 64) / 8);
+            }
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-    auto no_copy = [](int) __attribute__((always_inline)) {};
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
 
-    // prologue: units 0..3 in flight, wait for the two of step 0
+    // Prologue: units 0..4 in flight (units past the last one read zeros);
+    // wait for units 0..3, read the fragments of step 0 from units 0 and 1.
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-        if (u < nunits)
+    for (int u = 0; u < 5; ++u)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) copy(u, j);
-    if (nunits >= 4)
-        wait_and_barrier<16>();
-    else
-        wait_and_barrier<0>();
+        for (int j = 0; j < 8; ++j) copy(u, j);
+    wait_and_barrier<8>();
     {
-        const QB qb = qo.bases(lds_addr(slot(0)), 0);
-        const PB pb = po.bases(lds_addr(slot(1)), 0);
+        const QB qb0 = qo.bases(lds_addr(slot(0)), 0), qb1 = qo.bases(lds_addr(slot(0)), 1);
+        const PB pb0 = po.bases(lds_addr(slot(1)), 0), pb1 = po.bases(lds_addr(slot(1)), 1);
 #pragma unroll
-        for (int f = 0; f < 7; ++f) qo.frag(qb, 0, f, xq[f]);
-        qo.frag(qb, 0, 7, xq7[0]);
+        for (int f = 0; f < 7; ++f) {
+            qo.frag(qb0, 0, f, xq[f][0]);
+            qo.frag(qb1, 1, f, xq[f][1]);
+        }
+        qo.frag(qb0, 0, 7, xq7[0][0]);
+        qo.frag(qb1, 1, 7, xq7[0][1]);
 #pragma unroll
-        for (int f = 0; f < 8; ++f) po.frag(pb, 0, f, xp[0][f]);
+        for (int f = 0; f < 8; ++f) {
+            po.frag(pb0, 0, f, xp[0][f][0]);
+            po.frag(pb1, 1, f, xp[0][f][1]);
+        }
     }
 
     mfma_fence<false>(acc);  // accumulator writes, then the first MFMA
 
-    // substep 0 of step kt; unit 2 kt + 4 is copied under it
-    auto first_half = [&](int64_t kt) __attribute__((always_inline)) {
-        const int64_t u = 2 * kt + 4;
-        substep(P0{}, slot(2 * kt), slot(2 * kt + 1), 1, true, 8, [&](int c) __attribute__((always_inline)) { copy(u, c); });
-    };
-    // Every MFMA sits in this loop.  Its last pass reads fragments of a
-    // step past the end (slots that hold zeros or stale data) and copies past
-    // the end; nothing uses them.  A tail outside the loop would let the
-    // register allocator place accumulator copies between the MFMAs, which
-    // it cannot see as such and so would not separate by the wait states
-    // they need.
-    for (int64_t kt = 0; kt < ksteps; ++kt) {
-        first_half(kt);
-        // every wave has read all of step kt, and step kt + 1 must have
-        // landed; unit 2 kt + 4 may still be in flight
+    // Step s reads step s + 1 from units 2s + 2, 2s + 3 (landed), copies unit
+    // 2s + 5 under its first half (into the slot of unit 2s, read during step
+    // s - 1) and unit 2s + 6 under its second (slot of unit 2s + 1); at its
+    // end every wave has read units 2s + 2, 2s + 3, and units 2s + 4 and
+    // 2s + 5 must have landed (unit 2s + 6 may still be in flight).
+    //
+    // Every MFMA sits in this loop, whose body is two steps (the register
+    // parity).  With an odd step count its last pass runs one step past the
+    // end, on fragments read from units past the last one: zeros, which add
+    // nothing.  A tail outside the loop would let the register allocator
+    // place accumulator copies between the MFMAs, which it cannot see as such
+    // and so would not separate by the wait states they need.
+    const int64_t npairs = (ksteps + 1) / 2;
+    for (int64_t t = 0; t < npairs; ++t) {
+        const int64_t s0 = 2 * t, s1 = 2 * t + 1;
+        step(P0{}, slot(2 * s0 + 2), slot(2 * s0 + 3),
+             [&](int c) __attribute__((always_inline)) { copy(2 * s0 + 5, c); },
+             [&](int c) __attribute__((always_inline)) { copy(2 * s0 + 6, c); });
         wait_and_barrier<8>();
-        const int64_t u = 2 * kt + 5;
-        substep(P1{}, slot(2 * kt + 2), slot(2 * kt + 3), 0, true, 8, [&](int c) __attribute__((always_inline)) { copy(u, c); });
+        step(P1{}, slot(2 * s1 + 2), slot(2 * s1 + 3),
+             [&](int c) __attribute__((always_inline)) { copy(2 * s1 + 5, c); },
+             [&](int c) __attribute__((always_inline)) { copy(2 * s1 + 6, c); });
+        wait_and_barrier<8>();
     }
     mfma_fence<true>(acc);  // the last MFMA, then accumulator reads
     // the copies past the last unit are still in flight: none may land after
