@@ -26,6 +26,12 @@ Rules (in wait states: one per instruction, n + 1 for ``s_nop n``):
   accumulators straight from memory is inline assembly too, so the compiler
   does not wait for it).
 
+* ``m0`` belongs to the global -> LDS copies: it may appear only as the
+  destination of an ``s_mov_b32`` that is directly followed by a
+  ``buffer_load ... lds``.  The copies' inline assembly sets it and declares
+  it clobbered, but the compiler treats m0 as reserved and does not promise to
+  honour that, so no compiler-generated instruction may depend on it.
+
 Control flow: the file is walked in order, and for every branch the last
 instructions before it are also checked against the first instructions at its
 target, so a loop's back edge and a forward jump are covered too.
@@ -194,6 +200,14 @@ def check_kernel(body: List[Tuple[int, str]]) -> List[str]:
             branches.append((len(instrs), b.group(1)))
         instrs.append(ins)
     found = check_sequence(instrs)
+    for k, ins in enumerate(instrs):
+        if not any(a == "m0" for a in ins.args):
+            continue
+        nxt = instrs[k + 1] if k + 1 < len(instrs) else None
+        ok = (ins.op == "s_mov_b32" and ins.args[0] == "m0" and nxt is not None and
+              nxt.op.startswith("buffer_load") and "lds" in nxt.args[-1].split())
+        if not ok:
+            found.append("line %d: %r uses m0 outside a global -> LDS copy" % (ins.line, ins.text))
     for at, target in branches:
         if target in labels:
             found += check_sequence(_window(instrs, at + 1, False) + _window(instrs, labels[target], True))

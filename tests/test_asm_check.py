@@ -80,6 +80,13 @@ def test_load_into_accumulators_needs_a_wait():
     assert findings(load + "\tv_accvgpr_mov_b32 a4, a0\n")
 
 
+def test_m0_only_for_lds_copies():
+    copy = "\ts_mov_b32 m0, s4\n\tbuffer_load_dwordx4 v10, s[4:7], 0 offen lds\n"
+    assert findings(copy) == []
+    assert findings("\ts_mov_b32 m0, s4\n\ts_nop 0\n\tbuffer_load_dwordx4 v10, s[4:7], 0 offen lds\n")
+    assert findings(copy + "\ts_add_u32 s5, m0, 4\n")
+
+
 def test_built_kernels_pass():
     path = build.device_asm()
     if not os.path.exists(path):

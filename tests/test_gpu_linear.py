@@ -115,6 +115,21 @@ def test_ragged_integers_bit_exact():
     assert np.array_equal(host_bits(r["dWt"]), oracle.encode(dWt, "f16"))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,K,M,N,d", [(192, 320, 576, 3, 2), (64, 192, 576, 1, 1), (128, 64, 384, 6, 2)])
+def test_odd_step_counts_bit_exact(dtype, T, K, M, N, d):
+    # reduction lengths that are multiples of the 64-value step but an odd
+    # number of steps (forward K, dW T, dX n, and the paired dX 2n), where the
+    # main loop runs one step past the end on zero fragments
+    say("case odd steps", dtype, T, K, M, N, d)
+    X, Wt, dY = make_linear_inputs(T, K, M, dtype, "small_int", seed=11)
+    r = run_fwd_bwd(T, K, M, N, d, dtype, X, Wt, dY)
+    Y, dX, dWt = oracle_linear(X, Wt, dY, dtype)
+    assert np.array_equal(host_bits(r["Y"]), oracle.encode(Y, dtype)), "Y bits"
+    assert np.array_equal(r["dX"].cpu().numpy().astype(np.float64), dX), "dX exact"
+    assert np.array_equal(host_bits(r["dWt"]), oracle.encode(dWt, dtype)), "dW bits"
+
+
 def test_minimum_shapes():
     T, K, M, N, d = 1, 8, 8, 1, 1
     say("case minimum")
