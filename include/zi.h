@@ -148,7 +148,10 @@ zi_status zi_plan_predict(const zi_plan *plan, int32_t backward, double flop_rat
  * consecutive calls share the ring, so the copies of the next call's first
  * tiles overlap the previous call's last products.
  * workspace_dev: 256-byte aligned device memory of at least info.ring_bytes.
- * The context keeps no reference to the plan. */
+ * The context keeps no reference to the plan.  The first context created on
+ * a device also builds that device's GeLU tables (H over every 16-bit A, read
+ * by the forward GeLU epilogue) on compute_stream and waits for them;
+ * ZI_ERR_HIP if that fails. */
 zi_status zi_ctx_create(const zi_plan *plan, void *workspace_dev, uint64_t workspace_bytes,
                         void *compute_stream, void *h2d_stream, void *d2h_stream,
                         zi_ctx **out);

@@ -25,6 +25,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -452,6 +453,22 @@ zi_status zi_host_free(void *ptr) {
     return ZI_OK;
 }
 
+// The forward GeLU epilogue reads per-device tables of H over every 16-bit A;
+// the first context created on a device builds them (once, on its compute
+// stream, and waits for them).
+static zi_status ensure_gelu_tables(int device, hipStream_t stream) {
+    static std::mutex mu;
+    static std::vector<char> built;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)built.size() <= device) built.resize(device + 1, 0);
+    if (built[device]) return ZI_OK;
+    hipError_t e = build_gelu_tables(stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "building the GeLU tables");
+    built[device] = 1;
+    return ZI_OK;
+}
+
 zi_status zi_ctx_create(const zi_plan *plan, void *workspace_dev, uint64_t workspace_bytes,
                         void *compute_stream, void *h2d_stream, void *d2h_stream, zi_ctx **out) {
     clear_error();
@@ -471,6 +488,10 @@ zi_status zi_ctx_create(const zi_plan *plan, void *workspace_dev, uint64_t works
         return fail(ZI_ERR_HIP, "hipGetDevice failed");
     }
     c->device = dev;
+    if (ensure_gelu_tables(dev, static_cast<hipStream_t>(compute_stream)) != ZI_OK) {
+        delete c;
+        return ZI_ERR_HIP;
+    }
     c->comp = static_cast<hipStream_t>(compute_stream);
     c->h2d = static_cast<hipStream_t>(h2d_stream);
     c->d2h = static_cast<hipStream_t>(d2h_stream);

@@ -39,6 +39,10 @@ struct GemmArgs {
 // dtype: 1 = fp16, 2 = bf16.  Returns the launch status (hipGetLastError).
 hipError_t launch_gemm(GemmOp op, int dtype, const GemmArgs &a, hipStream_t stream);
 
+// Builds the per-device tables H = RNE16(GeLU(A)) over every 16-bit A (fp16
+// and bf16) that the forward GeLU epilogue reads; enqueued on `stream`.
+hipError_t build_gelu_tables(hipStream_t stream);
+
 // dA[i] = RNE(dH[i] * GeLU'(A[i])), i < count.
 hipError_t launch_gelu_bwd(int dtype, const float *dH, const void *A, void *dA, int64_t count,
                            hipStream_t stream);

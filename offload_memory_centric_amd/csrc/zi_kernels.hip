@@ -353,9 +353,39 @@ __device__ __forceinline__ float value16(uint32_t b) {
     return (float)__builtin_bit_cast(T, (uint16_t)b);
 }
 
-// GeLU(a) = a * Phi(a), Phi(a) = erfc(-a / sqrt 2) / 2 (exact erf form).
-__device__ __forceinline__ float gelu_f32(float a) {
-    return a * (0.5f * erfcf(-a * 0.70710678118654752f));
+// GeLU(a) = a * Phi(a), Phi(a) = erfc(-a / sqrt 2) / 2 (exact erf form), in
+// fp64.  The forward epilogue rounds it once to 16 bits, and its input is a
+// 16-bit value, so it is a table of 65536 entries per type, built once per
+// device (build_gelu_table) and looked up from LDS in the epilogue.
+__device__ __forceinline__ double gelu_f64(double a) { return a * (0.5 * erfc(-a / sqrt(2.0))); }
+
+// double -> float rounded to odd (truncate, then set the last bit if
+// inexact): a later round-to-nearest-even to a format at least two bits
+// narrower then gives the correctly rounded result of the double.
+__device__ __forceinline__ float round_to_odd_f32(double h) {
+    float f = (float)h;
+    if ((double)f != h) {
+        uint32_t u = __builtin_bit_cast(uint32_t, f);
+        if (fabs((double)f) > fabs(h)) u -= 1;  // rounded away from zero: one step back
+        f = __builtin_bit_cast(float, u | 1u);
+    }
+    return f;
+}
+
+__device__ uint16_t g_gelu_f16[65536];
+__device__ uint16_t g_gelu_bf16[65536];
+
+template <typename T>
+__device__ __forceinline__ uint16_t *gelu_table();
+template <>
+__device__ __forceinline__ uint16_t *gelu_table<_Float16>() { return g_gelu_f16; }
+template <>
+__device__ __forceinline__ uint16_t *gelu_table<__bf16>() { return g_gelu_bf16; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void gelu_table_kernel() {
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    gelu_table<T>()[i] = (uint16_t)bits16<T>(round_to_odd_f32(gelu_f64((double)value16<T>(i))));
 }
 
 // GeLU'(a) = Phi(a) + a * phi(a), phi(a) = exp(-a^2 / 2) / sqrt(2 pi).
@@ -592,6 +622,21 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue.
+    if constexpr (EPI == EPI_GELU) {
+        // H = table[A]: the GeLU table of this type goes into the now idle LDS
+        // (128 KiB: 32 one-KiB copies per wave).  Every wave's copies of the
+        // main loop must have landed before the table overwrites the ring.
+        asm volatile("s_barrier" ::: "memory");
+        const rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(gelu_table<T>()), 65536u * 2u);
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+            const int blk = wave * 32 + c;
+            copy16(rs, lds + blk * 1024, (uint32_t)(blk * 1024 + lane * 16));
+        }
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    [[maybe_unused]] const __attribute__((address_space(3))) uint16_t *gtab =
+        (const __attribute__((address_space(3))) uint16_t *)(uintptr_t)lds_addr(lds);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int64_t q = qb + i * 16;
@@ -607,12 +652,12 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
             } else if constexpr (EPI == EPI_LP) {
                 u32x2 o = {bits16<T>(v[0]) | (bits16<T>(v[1]) << 16), bits16<T>(v[2]) | (bits16<T>(v[3]) << 16)};
                 *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.C) + off) = o;
-            } else {  // EPI_GELU: A = RNE(acc); H = RNE(GeLU(A))
+            } else {  // EPI_GELU: A = RNE(acc); H = RNE(GeLU(A)) from the table
                 uint32_t b[4], h[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     b[e] = bits16<T>(v[e]);
-                    h[e] = bits16<T>(gelu_f32(value16<T>(b[e])));
+                    h[e] = gtab[b[e]];
                 }
                 *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.C) + off) =
                     u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
@@ -691,6 +736,14 @@ hipError_t launch_gemm(GemmOp op, int dtype, const GemmArgs &a, hipStream_t stre
     if (dtype == 1) return dispatch<_Float16>(op, a, stream);
     if (dtype == 2) return dispatch<__bf16>(op, a, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t build_gelu_tables(hipStream_t stream) {
+    hipLaunchKernelGGL(gelu_table_kernel<_Float16>, dim3(256), dim3(256), 0, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gelu_table_kernel<__bf16>, dim3(256), dim3(256), 0, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_gelu_bwd(int dtype, const float *dH, const void *A, void *dA, int64_t count,

@@ -89,3 +89,48 @@ def test_gelu_bwd_kernel_elementwise():
     ulp = np.maximum(np.abs(ref), 2.0 ** -14) * 2.0 ** -10
     assert np.all(np.abs(got - ref) <= ulp), float(np.max(np.abs(got - ref) / ulp))
     ctx.close()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_gelu_epilogue_every_16bit_input(dtype):
+    # X = e_0 and column m of W holds the 16-bit value with bits m in row 0
+    # (zeros elsewhere): A[0][m] is that value, so H is GeLU at every 16-bit
+    # input, and must be the oracle's fp64 GeLU rounded once (a mismatch is
+    # allowed only where the fp64 value sits within 1e-12 of a rounding tie,
+    # where the last ulp of the two erfc implementations decides)
+    T, K, M, N, d = 1, 8, 65536, 1, 1
+    say("case gelu table", dtype)
+    tiling = lib()
+    tdt = inputs.torch_dtype(dtype)
+    Wt = tiling.host_tensor((M, K), tdt)
+    w = Wt.view(torch.int16)
+    w.zero_()
+    w[:, 0] = torch.arange(M, dtype=torch.int32).to(torch.int16)
+    X = torch.zeros((T, K), dtype=tdt, device="cuda")
+    X[0, 0] = 1
+    plan = tiling.Plan(T, K, M, N, d, dtype, Wt)
+    ctx = tiling.Context(plan)
+    A = torch.empty((T, M), dtype=tdt, device="cuda")
+    H = torch.empty_like(A)
+    torch.cuda.synchronize()
+    ctx.fwd_gelu(plan, X, A, H)
+    ctx.sync()
+    a_bits, h_bits = host_bits(A).ravel(), host_bits(H).ravel()
+    w_val = oracle.decode(np.arange(M, dtype=np.uint16), dtype)
+    a_val = oracle.decode(a_bits, dtype)
+    fin = np.isfinite(w_val)
+    assert np.array_equal(a_val[fin], w_val[fin]), "A is not the input value"
+    fin = np.isfinite(a_val)
+    h_ref = oracle.gelu(a_val[fin])
+    want = oracle.encode(h_ref, dtype)
+    got = h_bits[fin]
+    bad = np.nonzero(got != want)[0]
+    say("  %d finite inputs, %d differ from the oracle" % (fin.sum(), bad.size))
+    if bad.size:
+        g, o, r = oracle.decode(got[bad], dtype), oracle.decode(want[bad], dtype), h_ref[bad]
+        assert np.all(np.abs(r - 0.5 * (g + o)) <= 1e-12 * np.abs(r)), "H off the oracle away from a tie"
+        assert bad.size <= 4, bad.size
+    inf_pos = np.nonzero(np.isposinf(a_val))[0]
+    assert inf_pos.size and np.all(np.isposinf(oracle.decode(h_bits[inf_pos], dtype)))
+    ctx.close()
+    plan.close()
