@@ -311,10 +311,18 @@ def main():
         try:
             R = sum(v["flops"] for k, v in kinds.items() if k != "gelu_bwd") / (
                 sum(v["ms"] for k, v in kinds.items() if k != "gelu_bwd") * 1e-3)
+            ait = flops_step / h2d_bytes_step
+            link_roof = ait * link["h2d_GBps"] * 1e9
+            # the step can go no faster than its products or its host-to-device bytes
+            attainable = min(R, link_roof)
             pred = {"kernel_flop_rate_TFLOPs": R / 1e12,
                     "link_h2d_GBps": link["h2d_GBps"],
                     "balance_flop_per_byte": R / (link["h2d_GBps"] * 1e9),
-                    "ait_step_flop_per_h2d_byte": flops_step / h2d_bytes_step}
+                    "ait_step_flop_per_h2d_byte": ait,
+                    "link_roofline_TFLOPs": link_roof / 1e12,
+                    "bound": "link" if link_roof < R else "mfma",
+                    "attainable_TFLOPs": attainable / 1e12,
+                    "frac_of_attainable": tflops * 1e12 / attainable}
         except ZeroDivisionError:
             pred = None
 
