@@ -66,8 +66,6 @@ constexpr int kLdsBytes = kUnits * kUnitBytes;
 
 enum Epi { EPI_LP = 0, EPI_F32 = 1, EPI_GELU = 2, EPI_ACC = 3 };
 
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
-
 __device__ __forceinline__ uint32_t lds_addr(const char *p) { return (uint32_t)(uintptr_t)p; }
 
 // ---- global -> LDS copies -------------------------------------------------------
@@ -280,16 +278,8 @@ struct RsOperand {
 // its LDS reads have returned, then meet the other waves.
 template <int n>
 __device__ __forceinline__ void wait_and_barrier() {
-    if constexpr (n == 0)
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (n == 8)
-        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (n == 16)
-        asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (n == 24)
-        asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
-        static_assert(n == 0, "unsupported in-flight count");
+    static_assert(n == 8, "the pipeline keeps one unit (8 copies per wave) in flight");
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ---- MFMA ------------------------------------------------------------------------
