@@ -24,6 +24,16 @@ double exactly):
   backward with the GeLU derivative.  A, H and dA are stored by the method in
   the 16-bit input format, so the oracle rounds them there (RNE) too.
 
+* ``adam_step``    the optimizer step that runs beside the path: the
+  transformer-math page (section "Applying the test: which state can live
+  where", its remark on the Adam update) puts it on the CPU because it is
+  elementwise (ait about 0.5); the GPU ZeRO-sharding page (section "The
+  architecture: every piece explained", the state taxonomy and offload) gives
+  its state as an fp32 master weight and first and second moments, and its
+  section "End-to-end flow" has the updated 16-bit parameters become the next
+  step's resting copy.  The update itself is Adam as Kingma and Ba publish it
+  (bias-corrected moments, no weight decay), in double precision.
+
 Host layout of a weight: out-major, W^t[M x K] (row m holds column m of W), the
 layout of ``nn.Linear.weight``; tile i is then rows [i*n, (i+1)*n) of W^t.
 
@@ -385,3 +395,20 @@ def ffn_sample(X, W1t, W2t, dY, dtype: str, t_rows, f_cols, d2_cols, d_cols,
             "dH": dH_rows[:, f_cols], "dA": dA_rows[:, f_cols], "dX": dX_s,
             "dW1t": dW1t_s, "dW2t": dW2t_s,
             "A_cols": A_cols, "dA_cols": dA_cols}
+
+
+def adam_step(master, m, v, grad, step: int, lr: float, beta1: float, beta2: float, eps: float):
+    """One Adam step (Kingma and Ba: bias-corrected first and second moments,
+    no weight decay) in double precision; returns (master, m, v) after step
+    `step` (1 for the first).  grad is the gradient of this step (dW)."""
+    if step < 1:
+        raise ValueError("step counts from 1")
+    master = np.asarray(master, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(grad, dtype=np.float64)
+    m1 = beta1 * m + (1.0 - beta1) * g
+    v1 = beta2 * v + (1.0 - beta2) * g * g
+    m_hat = m1 / (1.0 - beta1 ** step)
+    v_hat = v1 / (1.0 - beta2 ** step)
+    return master - lr * m_hat / (np.sqrt(v_hat) + eps), m1, v1
