@@ -243,6 +243,75 @@ zi_status zi_stream_create(void **out);
 zi_status zi_copy_stream_create(int32_t n_cus, void **out);
 zi_status zi_stream_destroy(void *stream);
 
+/* ---- Adam on the host: the optimizer step beside the path -----------------
+ *
+ * The Adam update is elementwise, about 12 FLOPs against 24 bytes, so no tier
+ * hides it behind GPU work and it runs on the CPU, next to the memory it
+ * touches (transformer-math page, section "Applying the test: which state can
+ * live where").  Its state is 12 bytes per parameter: an fp32 master weight
+ * and two fp32 moments (GPU ZeRO-sharding page, section "The architecture:
+ * every piece explained", and its offload paragraph: optimizer state and
+ * update on the CPU); the updated 16-bit parameters become the next step's
+ * resting copy (same page, section "End-to-end flow").
+ *
+ * One step of Adam (Kingma and Ba: bias-corrected moments, no weight decay),
+ * per element, in fp32 and in this order:
+ *   m      = beta1 * m + (1 - beta1) * g
+ *   v      = beta2 * v + (1 - beta2) * (g * g)
+ *   master = master - ((lr / (1 - beta1^step)) * m) / (sqrt(v * (1 / (1 - beta2^step))) + eps)
+ *   w      = RNE of master in the 16-bit format
+ * (the two bias factors are computed in double and rounded to fp32 once). */
+typedef struct {
+    float lr;     /* step size, finite and >= 0 */
+    float beta1;  /* in [0, 1) */
+    float beta2;  /* in [0, 1) */
+    float eps;    /* >= 0 */
+} zi_adam_hparams;
+
+/* One Adam step over `count` elements, on `threads` host threads (<= 0: as
+ * many as the process may run on).  grad: `count` gradients in the 16-bit
+ * format `dtype` (grad_f32 = 0) or in fp32 (grad_f32 = 1); master, m, v: fp32
+ * state, updated in place; w: `count` outputs in `dtype`.  Host memory of any
+ * kind; no GPU is involved.  ZI_ERR_ARG on a NULL pointer (count > 0),
+ * count < 0, step < 1, a bad dtype or hyperparameters out of range; nothing
+ * is written then. */
+zi_status zi_adam_update(const zi_adam_hparams *hp, int32_t dtype, int32_t grad_f32, int64_t step,
+                         int64_t count, const void *grad, float *master, float *m, float *v, void *w,
+                         int32_t threads);
+
+/* An optimizer for one plan's weight.  master, m, v: caller-owned host arrays
+ * of M * K fp32 each, in the layout of W^t (master holds the weights the
+ * 16-bit W_host was rounded from, m and v the moments, zero before the first
+ * step); the plan must have W_host and dW_host.  Every tile keeps its own
+ * step count, starting at 1.
+ * Attached to a context (zi_ctx_attach_adam), the optimizer updates tile i as
+ * soon as dW_i has landed in dW_host -- on its own host threads, while the
+ * GPU goes on with the next tiles -- and writes the new 16-bit tile into the
+ * plan's W_host.  Any later copy of tile i to the device waits, on the
+ * calling host thread, until that update is done; zi_sync() on the context
+ * also waits for the updates queued so far.  Updates run in the order their
+ * gradients were written back.  A failed update (a HIP error while waiting
+ * for its gradient) is reported by zi_adam_wait() and zi_sync(). */
+typedef struct zi_adam zi_adam;
+zi_status zi_adam_create(const zi_plan *plan, const zi_adam_hparams *hp, float *master, float *m, float *v,
+                         int32_t threads, zi_adam **out);
+/* Waits for the queued updates, then releases the optimizer.  Detach it from
+ * every context first (destroy the context, or attach NULL for its plan). */
+zi_status zi_adam_destroy(zi_adam *adam);
+/* Attach `adam` (or NULL: detach) to `plan` on `ctx`.  ZI_ERR_STATE if adam
+ * was made for another plan. */
+zi_status zi_ctx_attach_adam(zi_ctx *ctx, const zi_plan *plan, zi_adam *adam);
+/* Wait until every queued update is done; the first error, if any. */
+zi_status zi_adam_wait(zi_adam *adam);
+/* Totals since creation: tiles updated, seconds the update threads were busy,
+ * and host bytes the updates moved (28 per parameter with 16-bit gradients). */
+typedef struct {
+    int64_t tiles_done;
+    double busy_s;
+    double bytes;
+} zi_adam_stats;
+zi_status zi_adam_stats_get(zi_adam *adam, zi_adam_stats *out);
+
 /* Page-locked host memory (hipHostMalloc) for W^t / dW^t; 4096-byte aligned. */
 zi_status zi_host_alloc(uint64_t bytes, void **out);
 zi_status zi_host_free(void *ptr);

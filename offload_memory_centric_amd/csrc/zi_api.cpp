@@ -84,6 +84,13 @@ struct zi_ctx {
     size_t pool_used = 0;
     std::vector<KernelRec> krec;
     std::vector<CopyRec> crec;
+    std::vector<std::pair<const zi_plan *, zi_adam *>> adams;  // optimizers attached per plan
+
+    zi_adam *adam_of(const zi_plan *p) const {
+        for (const auto &e : adams)
+            if (e.first == p) return e.second;
+        return nullptr;
+    }
 
     char *wslot(int s) const { return ws + (uint64_t)s * slot_bytes; }
     char *dwslot(int s) const { return ws + (uint64_t)d * slot_bytes + (uint64_t)s * dw_slot_bytes; }
@@ -183,6 +190,8 @@ zi_status check_dev_ptr(const void *p, const char *name) {
 
 // Copy global tile g (tile index `tile` of plan p) into its slot.
 zi_status stage(zi_ctx *c, const zi_plan *p, int64_t g, int64_t tile) {
+    // the tile's pending optimizer update must have rewritten W_host first
+    if (zi_adam *a = c->adam_of(p)) adam_wait_tile(a, tile);
     const int s = (int)(g % c->d);
     if (c->w_free_rec[s]) HIPCHK(c, hipStreamWaitEvent(c->h2d, c->w_free[s], 0));
     const uint64_t bytes = p->info.tile_bytes;
@@ -377,6 +386,16 @@ zi_status run_bwd(zi_ctx *c, const zi_plan *p, const void *X, const void *dY, fl
         }
         HIPCHK(c, hipEventRecord(ready, c->comp));
         if ((st = write_back(c, p, i, dst, ready, done)) != ZI_OK) return st;
+        if (zi_adam *a = c->adam_of(p)) {  // update tile i on the host once dW_i has landed
+            hipEvent_t landed = nullptr;
+            HIPCHK(c, hipEventCreateWithFlags(&landed, hipEventDisableTiming | hipEventBlockingSync));
+            const hipError_t e = hipEventRecord(landed, c->d2h);
+            if (e != hipSuccess) {
+                (void)hipEventDestroy(landed);
+                return hip_fail(c, e, "hipEventRecord(gradient landed)");
+            }
+            adam_enqueue(a, i, landed);
+        }
         if (ds >= 0) {
             c->dw_free_rec[ds] = 1;
         } else {
@@ -577,6 +596,22 @@ zi_status zi_tiled_linear_bwd_recompute(zi_ctx *ctx, const zi_plan *plan, const 
     return run_bwd(ctx, plan, X_dev, dY_dev, dX_dev, Yr_dev);
 }
 
+zi_status zi_ctx_attach_adam(zi_ctx *ctx, const zi_plan *plan, zi_adam *adam) {
+    clear_error();
+    if (!ctx || !plan) return fail(ZI_ERR_ARG, "context and plan are required");
+    if (adam && adam_plan(adam) != plan) return fail(ZI_ERR_STATE, "the optimizer was made for another plan");
+    for (auto it = ctx->adams.begin(); it != ctx->adams.end(); ++it) {
+        if (it->first != plan) continue;
+        if (adam)
+            it->second = adam;
+        else
+            ctx->adams.erase(it);
+        return ZI_OK;
+    }
+    if (adam) ctx->adams.emplace_back(plan, adam);
+    return ZI_OK;
+}
+
 zi_status zi_gelu_bwd(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const void *A_dev, void *dA_dev,
                       int64_t count) {
     clear_error();
@@ -611,6 +646,10 @@ zi_status zi_sync(zi_ctx *ctx) {
     if (e1 != hipSuccess) return hip_fail(ctx, e1, "hipStreamSynchronize(compute)");
     if (e2 != hipSuccess) return hip_fail(ctx, e2, "hipStreamSynchronize(h2d)");
     if (e3 != hipSuccess) return hip_fail(ctx, e3, "hipStreamSynchronize(d2h)");
+    for (const auto &e : ctx->adams) {
+        const zi_status st = adam_wait_all(e.second);
+        if (st != ZI_OK) return st;
+    }
     if (ctx->sticky != ZI_OK) return fail(ctx->sticky, "%s", ctx->sticky_msg.c_str());
     return ZI_OK;
 }

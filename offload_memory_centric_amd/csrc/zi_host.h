@@ -30,4 +30,14 @@ struct Prediction {
 };
 Prediction simulate_pass(const PassModel &m);
 
+// The host optimizer (zi_adam.cpp), as the context drives it.
+const zi_plan *adam_plan(const zi_adam *a);
+// Queue the update of `tile`; it starts once `landed_event` (a hipEvent_t
+// recorded after the tile's gradient copy) has completed, and owns the event.
+void adam_enqueue(zi_adam *a, int64_t tile, void *landed_event);
+// Block until every queued update of `tile` is done.
+void adam_wait_tile(zi_adam *a, int64_t tile);
+// Block until the queue is empty; the first failure, if any.
+zi_status adam_wait_all(zi_adam *a);
+
 }  // namespace zi

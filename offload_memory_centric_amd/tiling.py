@@ -154,6 +154,11 @@ class Context:
         _need(dA, count, lp, "dA")
         zi.zi_gelu_bwd(self.handle, zi.DTYPE_CODES[dtype], dH, A, dA, count)
 
+    def attach_adam(self, plan: Plan, adam: Optional["Adam"]):
+        """Update each tile of `plan` on the host as its gradient lands (see Adam);
+        None detaches."""
+        zi.zi_ctx_attach_adam(self.handle, plan.handle, None if adam is None else adam.handle)
+
     def sync(self):
         zi.zi_sync(self.handle)
 
@@ -172,6 +177,45 @@ class Context:
             self.handle = None
         while self._own_streams:
             zi.zi_stream_destroy(self._own_streams.pop())
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Adam:
+    """Host Adam for one plan's weight (zi_adam_*): fp32 master, m and v of
+    M x K elements each, in the layout of W^t, in host memory (torch CPU
+    tensors).  master starts as the exact fp32 value of the plan's 16-bit
+    W_host unless given; m and v start at zero."""
+
+    def __init__(self, plan: Plan, lr: float = 1e-4, beta1: float = 0.9, beta2: float = 0.999,
+                 eps: float = 1e-8, threads: int = 0, master: Optional[torch.Tensor] = None):
+        W_host, dW_host = plan._keep
+        if W_host is None or dW_host is None:
+            raise ValueError("the plan needs W_host and dW_host")
+        shape = (plan.M, plan.K)
+        self.master = (W_host.float() if master is None else master).contiguous()
+        if tuple(self.master.shape) != shape or self.master.dtype != torch.float32 or self.master.is_cuda:
+            raise ValueError("master must be a host fp32 tensor of shape %s" % (shape,))
+        self.m = torch.zeros(shape, dtype=torch.float32)
+        self.v = torch.zeros(shape, dtype=torch.float32)
+        self.hp = zi.zi_adam_hparams(lr=lr, beta1=beta1, beta2=beta2, eps=eps)
+        self.plan = plan
+        self.handle = zi.zi_adam_create(plan.handle, self.hp, self.master, self.m, self.v, threads)
+
+    def wait(self):
+        zi.zi_adam_wait(self.handle)
+
+    def stats(self) -> dict:
+        return zi.zi_adam_stats_get(self.handle)
+
+    def close(self):
+        if self.handle:
+            zi.zi_adam_destroy(self.handle)
+            self.handle = None
 
     def __del__(self):
         try:

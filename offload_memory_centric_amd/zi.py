@@ -53,6 +53,15 @@ class zi_prediction(ctypes.Structure):
                 ("d_pages", ctypes.c_int32)]
 
 
+class zi_adam_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float)]
+
+
+class zi_adam_stats(ctypes.Structure):
+    _fields_ = [("tiles_done", ctypes.c_int64), ("busy_s", ctypes.c_double), ("bytes", ctypes.c_double)]
+
+
 class zi_stats(ctypes.Structure):
     _fields_ = [("kind_count", ctypes.c_int32), ("kind_name", (ctypes.c_char * 24) * 8),
                 ("launches", ctypes.c_int64 * 8), ("kernel_ms", ctypes.c_double * 8),
@@ -100,6 +109,14 @@ _sigs = {
     "zi_stream_create": (_S, [ctypes.POINTER(_P)]),
     "zi_copy_stream_create": (_S, [ctypes.c_int32, ctypes.POINTER(_P)]),
     "zi_stream_destroy": (_S, [_P]),
+    "zi_adam_update": (_S, [ctypes.POINTER(zi_adam_hparams), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                            ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_int32]),
+    "zi_adam_create": (_S, [_P, ctypes.POINTER(zi_adam_hparams), _P, _P, _P, ctypes.c_int32,
+                            ctypes.POINTER(_P)]),
+    "zi_adam_destroy": (_S, [_P]),
+    "zi_ctx_attach_adam": (_S, [_P, _P, _P]),
+    "zi_adam_wait": (_S, [_P]),
+    "zi_adam_stats_get": (_S, [_P, ctypes.POINTER(zi_adam_stats)]),
     "zi_host_alloc": (_S, [ctypes.c_uint64, ctypes.POINTER(_P)]),
     "zi_host_free": (_S, [_P]),
     "zi_last_error": (ctypes.c_char_p, []),
@@ -118,6 +135,8 @@ def _ptr(x) -> int:
         return None
     if hasattr(x, "data_ptr"):
         return x.data_ptr()
+    if hasattr(x, "__array_interface__"):  # numpy array
+        return x.__array_interface__["data"][0]
     return int(x)
 
 
@@ -232,6 +251,37 @@ def zi_ctx_stats(ctx) -> zi_stats:
     out = zi_stats()
     _check(_lib.zi_ctx_stats(ctx, ctypes.byref(out)))
     return out
+
+
+def zi_adam_update(hp: zi_adam_hparams, dtype: int, grad_f32: int, step: int, count: int, grad, master, m, v,
+                   w, threads: int = 0) -> None:
+    _check(_lib.zi_adam_update(ctypes.byref(hp), int(dtype), int(grad_f32), int(step), int(count), _ptr(grad),
+                               _ptr(master), _ptr(m), _ptr(v), _ptr(w), int(threads)))
+
+
+def zi_adam_create(plan, hp: zi_adam_hparams, master, m, v, threads: int = 0) -> int:
+    h = _P()
+    _check(_lib.zi_adam_create(plan, ctypes.byref(hp), _ptr(master), _ptr(m), _ptr(v), int(threads),
+                               ctypes.byref(h)))
+    return h.value
+
+
+def zi_adam_destroy(adam) -> None:
+    _check(_lib.zi_adam_destroy(adam))
+
+
+def zi_ctx_attach_adam(ctx, plan, adam) -> None:
+    _check(_lib.zi_ctx_attach_adam(ctx, plan, adam))
+
+
+def zi_adam_wait(adam) -> None:
+    _check(_lib.zi_adam_wait(adam))
+
+
+def zi_adam_stats_get(adam) -> dict:
+    s = zi_adam_stats()
+    _check(_lib.zi_adam_stats_get(adam, ctypes.byref(s)))
+    return {"tiles_done": s.tiles_done, "busy_s": s.busy_s, "bytes": s.bytes}
 
 
 def zi_host_alloc(nbytes: int) -> int:
