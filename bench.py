@@ -58,6 +58,11 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--d2h-cus", type=int, default=None,
                     help="compute units of the device-to-host copy stream (0: unrestricted)")
+    ap.add_argument("--adam", action="store_true",
+                    help="attach the host Adam to every weight: each tile is updated on the host "
+                         "once its gradient has landed, overlapped with the next tiles")
+    ap.add_argument("--adam-threads", type=int, default=16,
+                    help="host threads that share each tile's update (one tile at a time)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain streaming kernel of known size (HBM counter calibration)")
     return ap.parse_args()
@@ -356,11 +361,81 @@ def main():
                      "traffic": measured_traffic(config, dom_name)},
     }
 
+    adams = []
+    if args.adam:
+        result["adam"] = host_adam_leg(args, torch, tiling, ctx, plans, marked, spans, ms_step)
+        adams = result["adam"].pop("_objs")
+
     # ---------------- CPU baseline (oracle, after the GPU timing) ----------------
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, np, torch, config, locals())
     print(json.dumps(result), flush=True)
     ctx.close()
+    for a in adams:
+        a.close()
+
+
+def host_stream_GBps(torch, nelem=1 << 28, reps=3):
+    """Practical host memory bandwidth: a += b over fp32 arrays of 1 GiB on
+    torch's CPU threads, 12 bytes per element (a read and written in place,
+    b read; no write-allocate traffic, as in the optimizer's own pattern)."""
+    a = torch.ones(nelem)
+    b = torch.ones(nelem)
+    a.add_(b)
+    best = float("inf")
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        a.add_(b)
+        best = min(best, time.perf_counter() - t0)
+    return 12.0 * nelem / best / 1e9
+
+
+def host_adam_leg(args, torch, tiling, ctx, plans, marked, spans, ms_without):
+    """The same steps again with the host Adam attached to every weight: each
+    tile is updated on the host as soon as its gradient has landed, while the
+    GPU goes on with the next tiles.  Reports the step time with the optimizer
+    beside the step time of the path alone, and the optimizer's bandwidth
+    against the host's practical bandwidth."""
+    log("host Adam on %d weight(s), %d threads per tile update" % (len(plans), args.adam_threads))
+    adams = []
+    for pl in plans:
+        a = tiling.Adam(pl, lr=1e-4, threads=args.adam_threads)
+        ctx.attach_adam(pl, a)
+        adams.append(a)
+    # the warmup step pays the first touch of the optimizer state
+    marked(max(1, args.warmup))
+    ctx.sync()
+    torch.cuda.synchronize()
+    before = [a.stats() for a in adams]
+    t0 = time.perf_counter()
+    ev = marked(args.steps)
+    ctx.sync()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    after = [a.stats() for a in adams]
+    tiles = sum(x["tiles_done"] - y["tiles_done"] for x, y in zip(after, before))
+    busy = sum(x["busy_s"] - y["busy_s"] for x, y in zip(after, before))
+    nbytes = sum(x["bytes"] - y["bytes"] for x, y in zip(after, before))
+    params = sum(pl.K * pl.M for pl in plans)
+    ms_with = wall / args.steps * 1e3
+    peak = host_stream_GBps(torch)
+    achieved = nbytes / busy / 1e9 if busy > 0 else None
+    return {
+        "threads": args.adam_threads,
+        "params": params,
+        "host_state_bytes": 12 * params,
+        "ms_per_step_with_optimizer": round(ms_with, 3),
+        "ms_per_step_without": round(ms_without, 3),
+        "exposed_ms_per_step": round(ms_with - ms_without, 3),
+        "step_ms_with_optimizer": spans(ev),
+        "tiles_per_step": tiles / args.steps,
+        "busy_ms_per_step": round(busy / args.steps * 1e3, 3),
+        "roofline": {"bound": "host memory", "achieved": round(achieved, 2) if achieved else None,
+                     "peak": round(peak, 2), "unit": "GB/s",
+                     "frac": round(achieved / peak, 3) if achieved else None,
+                     "bytes_per_param": 28, "peak_kind": "measured a += b on the host"},
+        "_objs": adams,
+    }
 
 
 def _bits(torch, np, t):

@@ -13,14 +13,16 @@
 // agree bit for bit.
 //
 // With a context attached, each tile is updated as soon as its dW has been
-// written back: a coordinator thread per optimizer waits for the tile's copy
-// event, then splits the tile over the worker threads.
+// written back: one coordinator thread per process takes the tiles of every
+// optimizer in the order they were queued, waits for each tile's copy event,
+// then splits the tile over a persistent pool of worker threads.
 #include <hip/hip_runtime_api.h>
 #include <immintrin.h>
 #include <math.h>
 #include <sched.h>
 #include <string.h>
 
+#include <algorithm>
 #include <chrono>
 #include <condition_variable>
 #include <deque>
@@ -246,91 +248,249 @@ struct zi_adam {
     int dtype = ZI_F16;
     int grad_f32 = 0;
     int64_t N = 0, tile_elems = 0;
-
-    struct Task {
-        int64_t tile;
-        hipEvent_t landed;
-    };
-    std::mutex mu;
-    std::condition_variable cv;
-    std::deque<Task> queue;
+    // Guarded by the engine's mutex.
     std::vector<int64_t> queued, done;  // per tile: updates queued / completed (= its step count)
-    bool stop = false;
+    int64_t pending = 0;                // updates queued and not yet completed
     zi_status err = ZI_OK;
     std::string err_msg;
     int64_t tiles_done = 0;
     double busy_s = 0, bytes = 0;
+};
+
+namespace zi {
+namespace {
+
+// Persistent fork-join pool: run() splits one span over the caller and up to
+// `workers` pool threads, in contiguous chunks of whole 64-element blocks.
+// Used by one thread at a time (the engine's coordinator).
+class Pool {
+  public:
+    void ensure(int workers) {
+        while ((int)threads_.size() < workers) {
+            const int j = (int)threads_.size() + 1;
+            uint64_t now;
+            {
+                std::lock_guard<std::mutex> lock(mu_);
+                now = gen_;  // a new worker waits for the next span, not the last one
+            }
+            threads_.emplace_back([this, j, now] { work(j, now); });
+        }
+    }
+
+    void run(const Span &s, int64_t count, int parts) {
+        const int64_t blocks = (count + 63) / 64;
+        parts = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)parts, blocks,
+                                                             (int64_t)threads_.size() + 1}));
+        if (parts == 1) {
+            run_span(s, 0, count);
+            return;
+        }
+        {
+            std::lock_guard<std::mutex> lock(mu_);
+            span_ = &s;
+            count_ = count;
+            blocks_ = blocks;
+            parts_ = parts;
+            pending_ = parts - 1;
+            ++gen_;
+        }
+        go_.notify_all();
+        int64_t b, e;
+        range(0, b, e);
+        run_span(s, b, e);
+        std::unique_lock<std::mutex> lock(mu_);
+        fin_.wait(lock, [&] { return pending_ == 0; });
+    }
+
+    void shutdown() {
+        {
+            std::lock_guard<std::mutex> lock(mu_);
+            quit_ = true;
+        }
+        go_.notify_all();
+        for (auto &t : threads_) t.join();
+        threads_.clear();
+        std::lock_guard<std::mutex> lock(mu_);
+        quit_ = false;
+    }
+
+  private:
+    void range(int j, int64_t &b, int64_t &e) const {
+        b = std::min<int64_t>(count_, blocks_ * j / parts_ * 64);
+        e = std::min<int64_t>(count_, blocks_ * (j + 1) / parts_ * 64);
+    }
+
+    void work(int j, uint64_t seen) {
+        for (;;) {
+            int64_t b = 0, e = 0;
+            const Span *s = nullptr;
+            {
+                std::unique_lock<std::mutex> lock(mu_);
+                go_.wait(lock, [&] { return quit_ || gen_ != seen; });
+                if (quit_) return;
+                seen = gen_;
+                if (j >= parts_) continue;  // not needed for this span
+                s = span_;
+                range(j, b, e);
+            }
+            run_span(*s, b, e);
+            {
+                std::lock_guard<std::mutex> lock(mu_);
+                --pending_;
+            }
+            fin_.notify_one();
+        }
+    }
+
+    std::vector<std::thread> threads_;
+    std::mutex mu_;
+    std::condition_variable go_, fin_;
+    uint64_t gen_ = 0;
+    bool quit_ = false;
+    const Span *span_ = nullptr;
+    int64_t count_ = 0, blocks_ = 0;
+    int parts_ = 1, pending_ = 0;
+};
+
+// One engine per process.  Its coordinator thread takes the queued tile
+// updates of every optimizer in the order they were queued (the order the
+// gradients were written back, which is also the order the next passes need
+// the tiles in), waits for each tile's gradient to land, and splits the
+// update over the pool, so the host's cores work on one tile at a time.
+struct Engine {
+    struct Task {
+        zi_adam *a;
+        int64_t tile;
+        hipEvent_t landed;
+    };
+    std::mutex life;  // serialises starting and stopping the coordinator
+    std::mutex mu;    // guards the queue and every optimizer's counters
+    std::condition_variable cv;
+    std::deque<Task> queue;
     std::thread coordinator;
+    int users = 0;
+    bool stop = false;
+    Pool pool;
 
     void run() {
-        (void)hipSetDevice(device);
+        int cur_dev = -1;
         for (;;) {
             Task t;
             {
                 std::unique_lock<std::mutex> lock(mu);
                 cv.wait(lock, [&] { return stop || !queue.empty(); });
-                if (queue.empty()) return;
+                if (queue.empty()) break;
                 t = queue.front();
+                queue.pop_front();
             }
+            zi_adam *a = t.a;
+            if (a->device != cur_dev && hipSetDevice(a->device) == hipSuccess) cur_dev = a->device;
             const hipError_t e = hipEventSynchronize(t.landed);
             (void)hipEventDestroy(t.landed);
             const auto t0 = std::chrono::steady_clock::now();
-            const int64_t step = done[t.tile] + 1;
+            const int64_t step = a->done[t.tile] + 1;  // only this thread writes done[]
             if (e == hipSuccess) {
-                const int64_t off = t.tile * tile_elems;
+                const int64_t off = t.tile * a->tile_elems;
                 Span s;
-                s.k = adam_consts(hp, step);
-                s.dtype = dtype;
-                s.grad_f32 = grad_f32;
-                s.grad = static_cast<const char *>(plan->prob.dW_host) + off * (grad_f32 ? 4 : 2);
-                s.master = master + off;
-                s.m = m + off;
-                s.v = v + off;
-                s.w = static_cast<char *>(const_cast<void *>(plan->prob.W_host)) + off * 2;
-                parallel_update(s, tile_elems, threads);
+                s.k = adam_consts(a->hp, step);
+                s.dtype = a->dtype;
+                s.grad_f32 = a->grad_f32;
+                s.grad = static_cast<const char *>(a->plan->prob.dW_host) + off * (a->grad_f32 ? 4 : 2);
+                s.master = a->master + off;
+                s.m = a->m + off;
+                s.v = a->v + off;
+                s.w = static_cast<char *>(const_cast<void *>(a->plan->prob.W_host)) + off * 2;
+                pool.ensure(a->threads - 1);
+                pool.run(s, a->tile_elems, a->threads);
             }
             const double secs = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
             {
                 std::lock_guard<std::mutex> lock(mu);
-                if (e != hipSuccess && err == ZI_OK) {
-                    err = ZI_ERR_HIP;
-                    err_msg = std::string("waiting for a gradient tile: ") + hipGetErrorString(e);
+                if (e != hipSuccess && a->err == ZI_OK) {
+                    a->err = ZI_ERR_HIP;
+                    a->err_msg = std::string("waiting for a gradient tile: ") + hipGetErrorString(e);
                 }
-                done[t.tile] = step;  // also on failure, so that no waiter hangs
+                a->done[t.tile] = step;  // also on failure, so that no waiter hangs
+                --a->pending;
                 if (e == hipSuccess) {
-                    ++tiles_done;
-                    busy_s += secs;
-                    bytes += (double)tile_elems * (grad_f32 ? 30.0 : 28.0);
+                    ++a->tiles_done;
+                    a->busy_s += secs;
+                    a->bytes += (double)a->tile_elems * (a->grad_f32 ? 30.0 : 28.0);
                 }
-                queue.pop_front();
             }
             cv.notify_all();
         }
+        pool.shutdown();
+    }
+
+    // Register an optimizer; the first one starts the coordinator.
+    bool join_user() {
+        std::lock_guard<std::mutex> l(life);
+        {
+            std::lock_guard<std::mutex> lock(mu);
+            if (users++ > 0) return true;
+            stop = false;
+        }
+        try {
+            coordinator = std::thread([this] { run(); });
+        } catch (...) {
+            std::lock_guard<std::mutex> lock(mu);
+            --users;
+            return false;
+        }
+        return true;
+    }
+
+    // Unregister an optimizer whose updates are all done; the last one stops
+    // the coordinator and the pool.
+    void leave_user() {
+        std::lock_guard<std::mutex> l(life);
+        bool last;
+        {
+            std::lock_guard<std::mutex> lock(mu);
+            last = --users == 0;
+            if (last) stop = true;
+        }
+        if (!last) return;
+        cv.notify_all();
+        coordinator.join();
     }
 };
 
-namespace zi {
+// Never destroyed: the coordinator is joined when the last optimizer goes,
+// and an optimizer never released leaves a thread blocked on the queue,
+// which process exit ends.
+Engine &engine() {
+    static Engine *e = new Engine;
+    return *e;
+}
+
+}  // namespace
 
 // Hooks for the context (zi_api.cpp).
 const zi_plan *adam_plan(const zi_adam *a) { return a->plan; }
 
 void adam_enqueue(zi_adam *a, int64_t tile, void *landed_event) {
+    Engine &g = engine();
     {
-        std::lock_guard<std::mutex> lock(a->mu);
+        std::lock_guard<std::mutex> lock(g.mu);
         ++a->queued[tile];
-        a->queue.push_back(zi_adam::Task{tile, static_cast<hipEvent_t>(landed_event)});
+        ++a->pending;
+        g.queue.push_back(Engine::Task{a, tile, static_cast<hipEvent_t>(landed_event)});
     }
-    a->cv.notify_all();
+    g.cv.notify_all();
 }
 
 void adam_wait_tile(zi_adam *a, int64_t tile) {
-    std::unique_lock<std::mutex> lock(a->mu);
-    a->cv.wait(lock, [&] { return a->done[tile] >= a->queued[tile]; });
+    Engine &g = engine();
+    std::unique_lock<std::mutex> lock(g.mu);
+    g.cv.wait(lock, [&] { return a->done[tile] >= a->queued[tile]; });
 }
 
 zi_status adam_wait_all(zi_adam *a) {
-    std::unique_lock<std::mutex> lock(a->mu);
-    a->cv.wait(lock, [&] { return a->queue.empty(); });
+    Engine &g = engine();
+    std::unique_lock<std::mutex> lock(g.mu);
+    g.cv.wait(lock, [&] { return a->pending == 0; });
     if (a->err != ZI_OK) return fail(a->err, "%s", a->err_msg.c_str());
     return ZI_OK;
 }
@@ -392,9 +552,7 @@ zi_status zi_adam_create(const zi_plan *plan, const zi_adam_hparams *hp, float *
     a->tile_elems = plan->info.n * plan->prob.K;
     a->queued.assign(a->N, 0);
     a->done.assign(a->N, 0);
-    try {
-        a->coordinator = std::thread([a] { a->run(); });
-    } catch (...) {
+    if (!engine().join_user()) {
         delete a;
         return fail(ZI_ERR_ARG, "could not start the optimizer thread");
     }
@@ -406,12 +564,7 @@ zi_status zi_adam_destroy(zi_adam *a) {
     clear_error();
     if (!a) return ZI_OK;
     zi_status st = adam_wait_all(a);
-    {
-        std::lock_guard<std::mutex> lock(a->mu);
-        a->stop = true;
-    }
-    a->cv.notify_all();
-    if (a->coordinator.joinable()) a->coordinator.join();
+    engine().leave_user();
     delete a;
     return st;
 }
@@ -425,7 +578,7 @@ zi_status zi_adam_wait(zi_adam *a) {
 zi_status zi_adam_stats_get(zi_adam *a, zi_adam_stats *out) {
     clear_error();
     if (!a || !out) return fail(ZI_ERR_ARG, "optimizer and out are required");
-    std::lock_guard<std::mutex> lock(a->mu);
+    std::lock_guard<std::mutex> lock(engine().mu);
     out->tiles_done = a->tiles_done;
     out->busy_s = a->busy_s;
     out->bytes = a->bytes;

@@ -85,6 +85,11 @@ class zi_stats(ctypes.Structure):
 if not os.path.exists(LIB_PATH):
     raise ImportError("libzi.so is not built (expected at %s); run "
                       "`python -m offload_memory_centric_amd.build`" % LIB_PATH)
+# torch ships its own HIP runtime under the same soname as the system's.  Load
+# torch first so that libzi binds to that copy: a process that ends up with two
+# HIP runtimes finds no device in the one that initialises second.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p
