@@ -63,6 +63,12 @@ def parse():
                          "once its gradient has landed, overlapped with the next tiles")
     ap.add_argument("--adam-threads", type=int, default=16,
                     help="host threads that share each tile's update (one tile at a time)")
+    ap.add_argument("--choose", action="store_true",
+                    help="measure the products' rates at several tile widths, let the planner "
+                         "choose N and d from them, and time every width (prints its own JSON line)")
+    ap.add_argument("--widths", type=str, default=None,
+                    help="comma-separated tile widths for --choose (default: the 256-multiples of "
+                         "the block's down-projection between 800 and 6400 columns)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain streaming kernel of known size (HBM counter calibration)")
     return ap.parse_args()
@@ -189,6 +195,9 @@ def main():
         return
     if args.link_peak_only:
         print(json.dumps(link_peak(torch, tiling)), flush=True)
+        return
+    if args.choose:
+        print(json.dumps(choose_leg(args, torch, tiling, inputs, link)), flush=True)
         return
     dtype = args.dtype or ("f16" if args.workload == "ffn" else "bf16")
     tdt = inputs.torch_dtype(dtype)
@@ -373,6 +382,101 @@ def main():
     ctx.close()
     for a in adams:
         a.close()
+
+
+def choose_leg(args, torch, tiling, inputs, link, steps=3):
+    """Tile-width choice, measured.  For each width n (N = M/n, d = 2) one
+    tiled linear fwd + bwd is run over `steps` steps with per-launch events;
+    the rates of its forward, dX and dW products and of its copies make the
+    planner's curve.  The step time is then taken without those events, among
+    back-to-back steps (as the planner prices a step).
+    zi_plan_choose then picks N and d from that curve and the host-link rates,
+    and its prediction for every width stands beside the measured step time.
+    Default shape: the feed-forward block's down-projection, W2[102400 x 25600]
+    fp16 at T = 32768."""
+    from offload_memory_centric_amd import zi
+    T = args.T or 32768
+    K, M = args.K or 102400, args.M or 25600
+    dtype = args.dtype or "f16"
+    tdt = inputs.torch_dtype(dtype)
+    widths = ([int(x) for x in args.widths.split(",")] if args.widths else
+              [800, 1024, 1280, 1600, 2560, 3200, 5120, 6400])
+    widths = [n for n in widths if M % n == 0 and n % 8 == 0]
+    if not widths or not link:
+        raise SystemExit("--choose needs widths that divide M and the host-link peak")
+    log("choose: T=%d K=%d M=%d %s widths %s" % (T, K, M, dtype, widths))
+    X = inputs.new((T, K), dtype, "gaussian", 0, "X", device="cuda")
+    dY = inputs.new((T, M), dtype, "gaussian", 0, "dY", device="cuda")
+    Wt = tiling.host_tensor((M, K), tdt)
+    inputs.fill_(Wt, "gaussian", 0, "W", std=0.02, device="cuda", chunk_rows=1024)
+    dWt = tiling.host_tensor((M, K), tdt)
+    dX = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    flops_step = 6.0 * T * K * M
+    rows = []
+    for n in widths:
+        plan = tiling.Plan(T, K, M, M // n, 2, dtype, Wt, dWt)
+        ctx = tiling.Context(plan)
+        Y = torch.empty((T, M), dtype=tdt, device="cuda")
+        ctx.fwd(plan, X, Y)
+        ctx.bwd(plan, X, dY, dX)
+        ctx.sync()
+        # rates of the products and copies, from per-launch events
+        ctx.set_timing(True)
+        ctx.reset_stats()
+        for _ in range(steps):
+            ctx.fwd(plan, X, Y)
+            ctx.bwd(plan, X, dY, dX)
+        ctx.sync()
+        st = ctx.stats()
+        ctx.set_timing(False)
+        # the step time among back-to-back steps, without the per-launch
+        # events: marks on the compute stream after each step, and the mean
+        # over the steps after the first two (which include the ring's fill)
+        comp = torch.cuda.ExternalStream(ctx.streams[0])
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 3)]
+        torch.cuda.synchronize()
+        marks[0].record(comp)
+        for k in range(steps + 2):
+            ctx.fwd(plan, X, Y)
+            ctx.bwd(plan, X, dY, dX)
+            marks[k + 1].record(comp)
+        ctx.sync()
+        torch.cuda.synchronize()
+        wall = marks[2].elapsed_time(marks[steps + 2]) * 1e-3 / steps
+        rate = {k[len("gemm_"):]: v["flops"] / (v["ms"] * 1e-3) for k, v in st["kinds"].items() if v["launches"]}
+        rows.append({"n": n, "N": M // n, "ms_per_step_measured": round(wall * 1e3, 3),
+                     "TFLOPs_measured": round(flops_step / wall / 1e12, 1),
+                     "fwd_TFLOPs": round(rate["fwd"] / 1e12, 1), "dx_TFLOPs": round(rate["dx"] / 1e12, 1),
+                     "dw_TFLOPs": round(rate["dw"] / 1e12, 1),
+                     "h2d_GBps": round(st["h2d_bytes"] / st["h2d_ms"] / 1e6, 2),
+                     "d2h_GBps": round(st["d2h_bytes"] / st["d2h_ms"] / 1e6, 2)})
+        log("  n=%d N=%d %.1f ms/step, fwd %.0f dx %.0f dw %.0f TFLOP/s, copies %.1f / %.1f GB/s" % (
+            n, M // n, wall * 1e3, rate["fwd"] / 1e12, rate["dx"] / 1e12, rate["dw"] / 1e12,
+            rows[-1]["h2d_GBps"], rows[-1]["d2h_GBps"]))
+        ctx.close()
+        plan.close()
+        del Y
+    prob = zi.zi_problem(T=T, K=K, M=M, N=1, d=1, dtype=zi.DTYPE_CODES[dtype], flags=0,
+                         device_budget_bytes=0, W_host=None, dW_host=None)
+    h2d, d2h = link["h2d_GBps"] * 1e9, link["d2h_GBps"] * 1e9
+    choice, table = zi.zi_plan_choose(prob, [r["n"] for r in rows], [r["fwd_TFLOPs"] * 1e12 for r in rows],
+                                      [r["dx_TFLOPs"] * 1e12 for r in rows],
+                                      [r["dw_TFLOPs"] * 1e12 for r in rows], h2d, d2h, 1, 3,
+                                      h2d=[r["h2d_GBps"] * 1e9 for r in rows],
+                                      d2h=[r["d2h_GBps"] * 1e9 for r in rows])
+    for r in rows:
+        pred = [c for c in table if c["n"] == r["n"] and c["d"] == 2][0]
+        r["ms_per_step_predicted_d2"] = round(pred["t_step_s"] * 1e3, 3)
+    best = min(rows, key=lambda r: r["ms_per_step_measured"])
+    mine = [r for r in rows if r["n"] == choice["n"]][0]
+    return {"choose": {"workload": "tiled_linear_fwd_bwd", "T": T, "K": K, "M": M, "dtype": dtype,
+                       "link": link, "widths": rows,
+                       "choice": {"N": choice["N"], "d": choice["d"], "n": choice["n"],
+                                  "ms_per_step_predicted": round(choice["t_step_s"] * 1e3, 3),
+                                  "ms_per_step_measured_d2": mine["ms_per_step_measured"]},
+                       "measured_best": {"n": best["n"], "N": best["N"],
+                                         "ms_per_step": best["ms_per_step_measured"]},
+                       "choice_vs_best": round(best["ms_per_step_measured"] / mine["ms_per_step_measured"], 4)}}
 
 
 def host_stream_GBps(torch, nelem=1 << 28, reps=3):

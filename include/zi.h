@@ -141,6 +141,60 @@ typedef struct {
 zi_status zi_plan_predict(const zi_plan *plan, int32_t backward, double flop_rate,
                           double h2d_bytes_per_s, double d2h_bytes_per_s, zi_prediction *out);
 
+/* Rates measured at a few tile widths, for one T, K and dtype: at width n[j]
+ * the forward, dX and dW products of one tile run at fwd[j], dx[j] and dw[j]
+ * FLOP/s (dx or dw NULL: fwd's rates), and one tile's host-to-device and
+ * device-to-host copies at h2d[j] and d2h[j] bytes/s (NULL: the link rates
+ * passed to zi_plan_choose).  The widths are the candidates zi_plan_choose
+ * considers; no rate is inferred between them. */
+typedef struct {
+    int32_t count;
+    const int64_t *n;
+    const double *fwd;
+    const double *dx;
+    const double *dw;
+    const double *h2d;
+    const double *d2h;
+} zi_rate_curve;
+
+/* One candidate tiling and its predicted step. */
+typedef struct {
+    int32_t N, d;          /* tile count and weight slots */
+    int64_t n;             /* tile width M / N */
+    int32_t dw_slots;      /* as zi_plan_info */
+    uint64_t ring_bytes;   /* device bytes of the ring (<= the budget) */
+    double t_fwd_s;        /* one forward pass on its own (as zi_plan_predict) */
+    double t_bwd_s;        /* one backward pass on its own (0 with backward = 0) */
+    double t_step_s;       /* a step (forward, then backward) among back-to-back
+                              steps on one ring, whose copies run ahead into the
+                              next pass: the third step's end minus the second's */
+} zi_choice;
+
+/* Choose the tile count N and the ring depth d of `problem` (its N and d are
+ * ignored) under its device budget.  The page's trade-off (transformer-math
+ * page, section "Memory-centric tiling: operators bigger than the device"):
+ * more tiles shrink the resident bytes, layer bytes / N per slot, but make
+ * each product smaller and slower; fewer tiles also lengthen the first copy,
+ * which nothing hides.  Candidates: every width n[j] of `curve` with
+ * M % n[j] == 0 and n[j] % 8 == 0, with d = 1 .. max_d, whose ring fits the
+ * budget (the rules of zi_plan_tiles; with backward > 0 as for a plan with
+ * dW_host, so gradient slots are sized in).  Each is priced with the ring's
+ * event recurrence (as zi_plan_predict) using that width's measured rates,
+ * over back-to-back steps of one forward pass plus, for backward = 1 or 2,
+ * one backward pass (2: with the forward product recomputed per tile), the
+ * ring's state carried from pass to pass.  The choice has the least t_step_s;
+ * candidates within a relative 1e-9 of it count as equal, and then the
+ * smaller ring, the smaller d and the smaller N win, in that order.
+ * table: optional array of table_cap rows that receives every candidate in
+ * the order considered (widths in curve order, d ascending); *table_len (if
+ * not NULL) is set to the number of candidates, which may exceed table_cap.
+ * ZI_ERR_ARG on a NULL problem, curve or out, non-positive or non-finite
+ * rates, a width < 1, max_d < 1, or backward outside 0..2; ZI_ERR_SHAPE if
+ * the problem's own shapes are invalid; ZI_ERR_BUDGET if no candidate fits. */
+zi_status zi_plan_choose(const zi_problem *problem, const zi_rate_curve *curve, double h2d_bytes_per_s,
+                         double d2h_bytes_per_s, int32_t backward, int32_t max_d, zi_choice *out,
+                         zi_choice *table, int32_t table_cap, int32_t *table_len);
+
 /* A context: the tile ring over caller-owned device workspace and three
  * caller-owned streams (products, host-to-device, device-to-host).  The ring
  * geometry (slot sizes, d, gradient slots) is taken from `plan`; any plan with

@@ -302,7 +302,8 @@ zi_status run_bwd(zi_ctx *c, const zi_plan *p, const void *X, const void *dY, fl
     // 2n), which halves the fp32 read-add-store passes over dX.  Tile 2j stays
     // in its slot until that launch has read it; the dW product of tile 2j + 1
     // runs after it and covers the copy of the next tile into the freed slot.
-    const bool pairs = c->dw_slots > 0 && d >= 2 && N >= 2 && n % kGemmStep == 0;
+    static_assert(kPairStep == kGemmStep, "pairs split the reduction at a GEMM step");
+    const bool pairs = pairs_apply((int)N, d, c->dw_slots, n);
     zi_status st;
     int64_t staged = std::min<int64_t>(d, N);
     for (int64_t j = 0; j < staged; ++j)

@@ -16,12 +16,18 @@ namespace zi {
 zi_status fail(zi_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 
-zi_status plan_validate_and_fill(const zi_problem *p, zi_plan_info *info);
+// with_grad: the plan will run backward passes (gradient slots are sized);
+// zi_plan_tiles passes dW_host != NULL.
+zi_status plan_validate_and_fill(const zi_problem *p, zi_plan_info *info, bool with_grad);
 
 // One pass over the ring, times in seconds per tile.
 struct PassModel {
     int N = 1, d = 1, dw_slots = 0;
     bool backward = false;
+    // backward: the dX products of tiles 2j and 2j + 1 run as one launch once
+    // both are resident (the stager does so with gradient slots, d >= 2,
+    // N >= 2 and n a multiple of the GEMM's reduction step)
+    bool pairs = false;
     double t_h2d = 0, t_d2h = 0;
     double t_fwd = 0, t_recompute = 0, t_dx = 0, t_dw = 0;
 };
@@ -29,6 +35,16 @@ struct Prediction {
     double t_pass = 0, t_compute = 0, t_link = 0, stall = 0;
 };
 Prediction simulate_pass(const PassModel &m);
+// Whether the backward pairs the dX products of tiles 2j and 2j + 1 (one
+// launch with a reduction of 2n): with gradient slots, d >= 2, N >= 2 and n a
+// multiple of the GEMM's reduction step, so that the second tile's rows start
+// on a step boundary.  The stager (zi_api.cpp) and the timing model both use it.
+constexpr int64_t kPairStep = 64;
+bool pairs_apply(int N, int d, int dw_slots, int64_t n);
+// Time of one step (the passes in order) in a run of back-to-back steps on
+// one ring: the third step's end minus the second's.  All passes share the
+// first one's d and gradient slots.
+double simulate_steady_step(const PassModel *passes, int count);
 
 // The host optimizer (zi_adam.cpp), as the context drives it.
 const zi_plan *adam_plan(const zi_adam *a);

@@ -53,6 +53,22 @@ class zi_prediction(ctypes.Structure):
                 ("d_pages", ctypes.c_int32)]
 
 
+class zi_rate_curve(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("n", ctypes.POINTER(ctypes.c_int64)),
+                ("fwd", ctypes.POINTER(ctypes.c_double)), ("dx", ctypes.POINTER(ctypes.c_double)),
+                ("dw", ctypes.POINTER(ctypes.c_double)), ("h2d", ctypes.POINTER(ctypes.c_double)),
+                ("d2h", ctypes.POINTER(ctypes.c_double))]
+
+
+class zi_choice(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("d", ctypes.c_int32), ("n", ctypes.c_int64),
+                ("dw_slots", ctypes.c_int32), ("ring_bytes", ctypes.c_uint64),
+                ("t_fwd_s", ctypes.c_double), ("t_bwd_s", ctypes.c_double), ("t_step_s", ctypes.c_double)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
 class zi_adam_hparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float)]
@@ -100,6 +116,9 @@ _sigs = {
     "zi_prefetch_depth": (ctypes.c_int32, [ctypes.c_double, ctypes.c_double]),
     "zi_plan_predict": (_S, [_P, ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                              ctypes.POINTER(zi_prediction)]),
+    "zi_plan_choose": (_S, [ctypes.POINTER(zi_problem), ctypes.POINTER(zi_rate_curve), ctypes.c_double,
+                            ctypes.c_double, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(zi_choice),
+                            ctypes.POINTER(zi_choice), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     "zi_ctx_create": (_S, [_P, _P, ctypes.c_uint64, _P, _P, _P, ctypes.POINTER(_P)]),
     "zi_ctx_destroy": (_S, [_P]),
     "zi_tiled_linear_fwd": (_S, [_P, _P, _P, _P]),
@@ -191,6 +210,32 @@ def zi_plan_predict(plan, backward: int, flop_rate: float, h2d_bytes_per_s: floa
     _check(_lib.zi_plan_predict(plan, int(backward), flop_rate, h2d_bytes_per_s, d2h_bytes_per_s,
                                 ctypes.byref(out)))
     return out
+
+
+def zi_plan_choose(problem: zi_problem, n, fwd, dx=None, dw=None, h2d_bytes_per_s: float = 0.0,
+                   d2h_bytes_per_s: float = 0.0, backward: int = 1, max_d: int = 2, h2d=None, d2h=None):
+    """(choice, table): the chosen tiling and every candidate considered, as dicts."""
+    count = len(n)
+
+    def arr(ctype, xs):
+        if xs is None:
+            return None
+        if len(xs) != count:
+            raise ValueError("every rate list needs one entry per width")
+        return (ctype * count)(*xs)
+
+    keep = [arr(ctypes.c_int64, [int(x) for x in n]), arr(ctypes.c_double, fwd),
+            arr(ctypes.c_double, dx), arr(ctypes.c_double, dw), arr(ctypes.c_double, h2d),
+            arr(ctypes.c_double, d2h)]
+    curve = zi_rate_curve(count, *keep)
+    out = zi_choice()
+    cap = max(1, count * max(1, int(max_d)))
+    table = (zi_choice * cap)()
+    length = ctypes.c_int32()
+    _check(_lib.zi_plan_choose(ctypes.byref(problem), ctypes.byref(curve), float(h2d_bytes_per_s),
+                               float(d2h_bytes_per_s), int(backward), int(max_d), ctypes.byref(out),
+                               table, cap, ctypes.byref(length)))
+    return out.as_dict(), [table[i].as_dict() for i in range(min(cap, length.value))]
 
 
 def zi_ctx_create(plan, workspace, workspace_bytes: int, compute_stream, h2d_stream, d2h_stream):

@@ -156,3 +156,150 @@ def ffn_tiled_h2d_bytes(P1: float, P2: float, bytes_per_param: int = 2) -> float
     forward, the recompute and the backward; W2 for the forward and once more
     for the recompute-plus-backward."""
     return bytes_per_param * (3 * P1 + 2 * P2)
+
+
+# --- choosing the tile width ([ZI-math] "Memory-centric tiling": resident bytes
+#     fall as layer_bytes / k while finer tiles make the products smaller and
+#     slower; [ZI-cn] "关键技术三：Overlap-Centric Design": copies overlap products)
+#
+# Our reading of the ring on one link: a pass over N tiles with d device slots
+# for weight tiles.  Tile i's copy starts once the link is free and tile i - d
+# has released its slot; its products start once the compute stream is free
+# and the copy has landed.  In the backward, the weight slot is released after
+# the products that read W (recomputed forward, then dX); dW_i is formed in a
+# separate gradient slot (free once the write-back of tile i - g is done, with
+# g gradient slots) or, with g = 0, in the weight slot itself, which then stays
+# taken until dW_i has been written back.
+
+def ring_bytes(K: int, n: int, d: int, dtype: str, budget: int, with_grad: bool, grad_f32: bool = False):
+    """(gradient slots, device bytes) of a ring of d weight slots, or None if
+    it does not fit `budget` (0 = no cap).  Slots are rounded up to 256 bytes;
+    a backward gets two gradient slots if the budget leaves room, else one,
+    else none (the gradient then needs to fit a weight slot)."""
+    def slot(b):
+        return -(-b // 256) * 256
+    w = slot(tile_bytes(K, n, dtype))
+    g = slot(K * n * (4 if grad_f32 else BYTES[dtype]))
+    if budget and d * w > budget:
+        return None
+    if not with_grad:
+        return 0, d * w
+    slots = 2 if not budget else min(2, (budget - d * w) // g)
+    if slots == 0 and g > w:
+        return None
+    return slots, d * w + slots * g
+
+
+def ring_run(N: int, d: int, passes, grad_slots: int = 0):
+    """End time of each pass when `passes` run back to back on one ring.
+
+    Every pass stages all N tiles in order; the copies of a pass start as soon
+    as the link and the slots allow, so they run ahead into the previous pass.
+    Tile g of the run (counted across passes) reuses the slot of tile g - d.
+    A pass is a dict: t_copy, and t_fwd for a forward; for a backward
+    (backward=True) t_re (recomputed forward), t_dx, t_dw, t_back (the
+    gradient's write-back) and `pairs`: the dX products of tiles 2j and 2j+1
+    of the pass run as one product once both are resident (our reading of the
+    grouping the library uses with gradient slots), which frees both slots;
+    tile 2j then runs only its recompute and dW before tile 2j+1 arrives."""
+    if any(p.get("pairs") for p in passes) and not grad_slots:
+        raise ValueError("pairs need gradient slots")
+    release = []      # release[g]: when the g-th staged tile frees its weight slot
+    grad_free = []    # grad_free[h]: when the h-th gradient frees its gradient slot
+    link = comp = back = 0.0
+    ends = []
+    for p in passes:
+        for i in range(N):
+            g = len(release)
+            link = max(link, release[g - d] if g >= d else 0.0) + p["t_copy"]
+            start = max(comp, link)
+            if not p.get("backward"):
+                comp = start + p["t_fwd"]
+                release.append(comp)
+                continue
+            h = len(grad_free)
+            if p.get("pairs") and i % 2 == 0 and i + 1 < N:
+                w_done = start + p.get("t_re", 0.0)   # no dX yet; the slot stays taken
+                release.append(None)
+            elif p.get("pairs") and i % 2 == 1:
+                w_done = start + p.get("t_re", 0.0) + 2 * p["t_dx"]
+                release[g - 1] = w_done
+                release.append(w_done)
+            else:
+                w_done = start + p.get("t_re", 0.0) + p["t_dx"]
+                if grad_slots:
+                    release.append(w_done)
+            if grad_slots:
+                comp = max(w_done, grad_free[h - grad_slots] if h >= grad_slots else 0.0) + p["t_dw"]
+                back = max(back, comp) + p["t_back"]
+            else:
+                comp = w_done + p["t_dw"]
+                back = max(back, comp) + p["t_back"]
+                release.append(back)
+            grad_free.append(back)
+        ends.append(max(comp, back))
+    return ends
+
+
+def ring_pass_time(N: int, d: int, t_copy: float, t_fwd: float = 0.0, backward: bool = False,
+                   t_re: float = 0.0, t_dx: float = 0.0, t_dw: float = 0.0, t_back: float = 0.0,
+                   grad_slots: int = 0) -> float:
+    """Time from the first copy to the last product (and write-back) of one pass."""
+    p = {"t_copy": t_copy, "t_fwd": t_fwd, "backward": backward, "t_re": t_re, "t_dx": t_dx,
+         "t_dw": t_dw, "t_back": t_back}
+    return ring_run(N, d, [p], grad_slots)[0]
+
+
+def steady_step_time(N: int, d: int, step, grad_slots: int = 0) -> float:
+    """One step (its passes in order) among back-to-back steps: the third
+    step's end minus the second's."""
+    ends = ring_run(N, d, list(step) * 3, grad_slots)
+    k = len(step)
+    return ends[3 * k - 1] - ends[2 * k - 1]
+
+
+def choose_tiling(T: int, K: int, M: int, dtype: str, budget: int, widths, r_fwd, r_dx, r_dw,
+                  h2d: float, d2h: float, backward: int, max_d: int, grad_f32: bool = False,
+                  c_h2d=None, c_d2h=None):
+    """Every candidate (width from `widths` dividing M, multiple of 8; d in
+    1..max_d; ring within the budget), priced as a step among back-to-back
+    steps of one forward pass plus, for backward 1 or 2, one backward pass (2:
+    the forward product recomputed per tile), with the measured rates of that
+    width (copy rates c_h2d / c_d2h per width, else h2d / d2h).  Returns
+    (choice, table): the candidate of least step time, where a candidate
+    within a relative 1e-9 of the best so far counts as equal and then the
+    smaller ring, the smaller d, the smaller N win; table lists every
+    candidate in the order considered, each with its passes' times on their
+    own as well."""
+    table = []
+    best = None
+    for j, n in enumerate(widths):
+        if M % n or n % 8:
+            continue
+        N = M // n
+        flops = 2.0 * T * K * n
+        for d in range(1, max_d + 1):
+            fit = ring_bytes(K, n, d, dtype, budget, backward != 0, grad_f32)
+            if fit is None:
+                continue
+            slots, nbytes = fit
+            t_copy = tile_bytes(K, n, dtype) / (c_h2d[j] if c_h2d else h2d)
+            step = [{"t_copy": t_copy, "t_fwd": flops / r_fwd[j]}]
+            if backward:
+                step.append({"t_copy": t_copy, "backward": True,
+                             "t_re": flops / r_fwd[j] if backward == 2 else 0.0,
+                             "t_dx": flops / r_dx[j], "t_dw": flops / r_dw[j],
+                             "t_back": K * n * (4 if grad_f32 else BYTES[dtype]) / (c_d2h[j] if c_d2h else d2h)})
+            if backward:
+                step[1]["pairs"] = slots > 0 and d >= 2 and N >= 2 and n % 64 == 0
+            alone = [ring_run(N, d, [p], slots)[0] for p in step]
+            c = {"N": N, "d": d, "n": n, "dw_slots": slots, "ring_bytes": nbytes,
+                 "t_fwd_s": alone[0], "t_bwd_s": alone[1] if backward else 0.0,
+                 "t_step_s": steady_step_time(N, d, step, slots)}
+            table.append(c)
+            if best is None or c["t_step_s"] < best["t_step_s"] * (1 - 1e-9):
+                best = c
+            elif c["t_step_s"] <= best["t_step_s"] * (1 + 1e-9):
+                if (c["ring_bytes"], c["d"], c["N"]) < (best["ring_bytes"], best["d"], best["N"]):
+                    best = c
+    return best, table
