@@ -63,6 +63,13 @@ def parse():
                          "once its gradient has landed, overlapped with the next tiles")
     ap.add_argument("--adam-threads", type=int, default=16,
                     help="host threads that share each tile's update (one tile at a time)")
+    ap.add_argument("--nvme", type=str, default=None, metavar="DIR",
+                    help="read the weights from files written into DIR (the NVMe tier): each tile "
+                         "goes file -> pinned staging buffer -> HBM")
+    ap.add_argument("--nvme-threads", type=int, default=8,
+                    help="threads that split each tile's file read")
+    ap.add_argument("--nvme-staging", type=int, default=3,
+                    help="pinned staging buffers per weight: how many tiles the reads may run ahead")
     ap.add_argument("--choose", action="store_true",
                     help="measure the products' rates at several tile widths, let the planner "
                          "choose N and d from them, and time every width (prints its own JSON line)")
@@ -265,6 +272,12 @@ def main():
         config = {"workload": "tiled_linear_fwd_bwd", "T": T, "K": K, "M": M, "N": N, "n": M // N,
                   "d": d, "weights": "pinned host", "dtype": dtype}
         plans = (p,)
+    sources = []
+    if args.nvme:
+        if args.adam:
+            raise SystemExit("--nvme and --adam exclude each other (the optimizer updates host memory)")
+        sources = nvme_sources(args, tiling, ctx, plans)
+        config["weights"] = "file -> pinned staging -> HBM"
     torch.cuda.synchronize()
 
     # Per-step marks: an event on the compute stream after every step (no
@@ -287,6 +300,8 @@ def main():
     ctx.sync()
     torch.cuda.synchronize()
     warm_ms = spans(wev)
+
+    src_before = [src.stats() for src, _ in sources]
 
     # ---------------- timed steps ----------------
     ctx.set_timing(True)
@@ -370,6 +385,8 @@ def main():
                      "traffic": measured_traffic(config, dom_name)},
     }
 
+    if sources:
+        result["nvme"] = nvme_report(args, tiling, sources, src_before, kinds, wall, flops_step * args.steps)
     adams = []
     if args.adam:
         result["adam"] = host_adam_leg(args, torch, tiling, ctx, plans, marked, spans, ms_step)
@@ -379,9 +396,14 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, np, torch, config, locals())
     print(json.dumps(result), flush=True)
+    for pl in plans:
+        ctx.attach_source(pl, None)
     ctx.close()
     for a in adams:
         a.close()
+    for src, path in sources:
+        src.close()
+        os.remove(path)
 
 
 def choose_leg(args, torch, tiling, inputs, link, steps=3):
@@ -477,6 +499,53 @@ def choose_leg(args, torch, tiling, inputs, link, steps=3):
                        "measured_best": {"n": best["n"], "N": best["N"],
                                          "ms_per_step": best["ms_per_step_measured"]},
                        "choice_vs_best": round(best["ms_per_step_measured"] / mine["ms_per_step_measured"], 4)}}
+
+
+def nvme_sources(args, tiling, ctx, plans):
+    """Write every plan's weight to a file under args.nvme and read the tiles
+    from there: one source per weight, args.nvme_staging staging buffers each."""
+    os.makedirs(args.nvme, exist_ok=True)
+    out = []
+    for j, pl in enumerate(plans):
+        path = os.path.join(args.nvme, "zi_weight_%d.bin" % j)
+        t0 = time.perf_counter()
+        tiling.write_weight_file(path, pl._keep[0])
+        os.sync()
+        log("wrote %s (%.1f GB) in %.1f s" % (path, pl.K * pl.M * 2 / 1e9, time.perf_counter() - t0))
+        src = tiling.FileSource(pl, path, staging=args.nvme_staging, threads=args.nvme_threads)
+        ctx.attach_source(pl, src)
+        out.append((src, path))
+    return out
+
+
+def nvme_report(args, tiling, sources, before, kinds, wall, flops):
+    """What the file tier delivered during the timed steps, beside the rate a
+    plain sequential read of one weight file reaches with the same threads,
+    and the pages' test for the tier: the step's FLOPs per byte read from the
+    files against the products' rate over that read rate."""
+    import numpy as np
+    after = [src.stats() for src, _ in sources]
+    d = {k: sum(a[k] - b[k] for a, b in zip(after, before)) for k in ("bytes", "read_s", "wait_s", "restarts")}
+    src0 = sources[0][0]
+    tile = src0.plan.info.tile_bytes
+    raw = np.empty(tile + 4096, np.uint8)  # pageable and 4096-aligned: a direct read lands in place
+    buf = raw[(-raw.ctypes.data) % 4096:][:tile]
+    reps = min(src0.plan.N, 8)
+    t0 = time.perf_counter()
+    for t in range(reps):
+        src0.read(t, buf)
+    peak = reps * tile / (time.perf_counter() - t0)
+    prod = {k: v for k, v in kinds.items() if k != "gelu_bwd"}
+    R = sum(v["flops"] for v in prod.values()) / (sum(v["ms"] for v in prod.values()) * 1e-3)
+    ait = flops / d["bytes"] if d["bytes"] else None
+    return {"direct_io": bool(after[0]["direct"]), "threads_per_read": args.nvme_threads,
+            "staging_per_weight": args.nvme_staging,
+            "bytes_read_timed": d["bytes"], "read_busy_s": round(d["read_s"], 3),
+            "pass_wait_s": round(d["wait_s"], 3), "restarts": d["restarts"],
+            "read_GBps_over_timed_steps": round(d["bytes"] / wall / 1e9, 2),
+            "read_GBps_sequential_peak": round(peak / 1e9, 2),
+            "ait_flop_per_file_byte": ait, "balance_R_over_BW": R / peak,
+            "tier_hidden": (ait >= R / peak) if ait else None}
 
 
 def host_stream_GBps(torch, nelem=1 << 28, reps=3):

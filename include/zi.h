@@ -62,7 +62,8 @@ typedef enum {
     ZI_ERR_NOT_PINNED = 4, /* host weight or gradient buffer is not page-locked */
     ZI_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned */
     ZI_ERR_HIP = 6,        /* a HIP runtime call failed (sticky on the context) */
-    ZI_ERR_STATE = 7       /* plan and context disagree, or the context is unusable */
+    ZI_ERR_STATE = 7,      /* plan and context disagree, or the context is unusable */
+    ZI_ERR_IO = 8          /* a file could not be opened or read */
 } zi_status;
 
 typedef enum { ZI_F16 = 1, ZI_BF16 = 2 } zi_dtype;
@@ -365,6 +366,52 @@ typedef struct {
     double bytes;
 } zi_adam_stats;
 zi_status zi_adam_stats_get(zi_adam *adam, zi_adam_stats *out);
+
+/* The NVMe tier: a weight read from a file on local storage instead of
+ * W_host (pwwt.cn ZeRO-Infinity article, section "关键技术三：Overlap-Centric
+ * Design": reads of later parameters from NVMe overlap the copies of nearer
+ * ones to the GPU and the compute of the current one).  The file holds W^t
+ * [M x K] of the plan's dtype from byte `offset` on, tile i at
+ * offset + i * tile_bytes.  A reader thread reads tiles ahead of the passes
+ * that use them into `staging` (>= 2) pinned buffers of one tile each, made
+ * on first use on the current device, each read split over `threads`
+ * positioned reads; with offset and tile_bytes multiples of 4096 the file is
+ * read with O_DIRECT where the file system allows it.  The read-ahead
+ * expects the tiles in ascending order, the first tile following the last
+ * (every pass walks its tiles so); a pass that asks for another tile restarts
+ * it there.  Attached to a context (zi_ctx_attach_source), every copy of the
+ * plan's tiles to the device reads from the staging buffers: the calling host
+ * thread waits, inside the pass call, until the tile's read is done (W_host
+ * may then be NULL).  A source serves one context at a time.
+ * ZI_ERR_IO if the file cannot be opened or is shorter than
+ * offset + M * K * 2 bytes; ZI_ERR_ARG on NULL arguments, staging < 2 or
+ * threads < 1.  Creating a source touches no GPU. */
+typedef struct zi_file_source zi_file_source;
+zi_status zi_file_source_create(const zi_plan *plan, const char *path, uint64_t offset, int32_t staging,
+                                int32_t threads, zi_file_source **out);
+/* Stops the reader, waits for every copy out of the staging buffers, frees
+ * them and closes the file.  Detach the source from its context first. */
+zi_status zi_file_source_destroy(zi_file_source *src);
+/* Attach `src` (or NULL: detach) to `plan` on `ctx`.  ZI_ERR_STATE if the
+ * source was made for another plan, or if an optimizer is attached to the
+ * plan (it would update W_host, which the passes would no longer read). */
+zi_status zi_ctx_attach_source(zi_ctx *ctx, const zi_plan *plan, zi_file_source *src);
+/* Read tile `tile` into host memory `dst` (tile_bytes; 4096-byte aligned for a
+ * source that reads with O_DIRECT, else ZI_ERR_ALIGN), synchronously, with the
+ * source's threads.  No GPU is involved.  ZI_ERR_IO on a failed read. */
+zi_status zi_file_source_read(zi_file_source *src, int64_t tile, void *dst);
+/* Totals since creation: tiles read ahead, restarts of the read-ahead,
+ * seconds spent reading, bytes read, seconds the passes waited for a read,
+ * and whether the file is read with O_DIRECT. */
+typedef struct {
+    int64_t tiles_read;
+    int64_t restarts;
+    double read_s;
+    double bytes;
+    double wait_s;
+    int32_t direct;
+} zi_source_stats;
+zi_status zi_file_source_stats_get(zi_file_source *src, zi_source_stats *out);
 
 /* Page-locked host memory (hipHostMalloc) for W^t / dW^t; 4096-byte aligned. */
 zi_status zi_host_alloc(uint64_t bytes, void **out);

@@ -85,9 +85,15 @@ struct zi_ctx {
     std::vector<KernelRec> krec;
     std::vector<CopyRec> crec;
     std::vector<std::pair<const zi_plan *, zi_adam *>> adams;  // optimizers attached per plan
+    std::vector<std::pair<const zi_plan *, zi_file_source *>> sources;  // file sources per plan
 
     zi_adam *adam_of(const zi_plan *p) const {
         for (const auto &e : adams)
+            if (e.first == p) return e.second;
+        return nullptr;
+    }
+    zi_file_source *source_of(const zi_plan *p) const {
+        for (const auto &e : sources)
             if (e.first == p) return e.second;
         return nullptr;
     }
@@ -164,10 +170,12 @@ zi_status check_pass(zi_ctx *c, const zi_plan *p, bool backward) {
         return fail(ZI_ERR_STATE, "plan tile of %llu B does not fit the context's %llu B slots",
                     (unsigned long long)in.tile_bytes, (unsigned long long)c->slot_bytes);
     const uint64_t wbytes = (uint64_t)pr.M * (uint64_t)pr.K * 2u;
-    if (!pr.W_host) return fail(ZI_ERR_ARG, "plan has no W_host");
-    if (!pinned_range(pr.W_host, wbytes))
-        return fail(ZI_ERR_NOT_PINNED, "W_host is not page-locked host memory over its %llu bytes",
-                    (unsigned long long)wbytes);
+    if (!c->source_of(p)) {  // with a file source the tiles come from its staging buffers
+        if (!pr.W_host) return fail(ZI_ERR_ARG, "plan has no W_host");
+        if (!pinned_range(pr.W_host, wbytes))
+            return fail(ZI_ERR_NOT_PINNED, "W_host is not page-locked host memory over its %llu bytes",
+                        (unsigned long long)wbytes);
+    }
     if (backward) {
         if (!pr.dW_host) return fail(ZI_ERR_ARG, "a backward needs a plan with dW_host");
         const uint64_t dwbytes = (uint64_t)pr.M * (uint64_t)pr.K * ((pr.flags & ZI_FLAG_F32_OUT) ? 4u : 2u);
@@ -196,13 +204,38 @@ zi_status stage(zi_ctx *c, const zi_plan *p, int64_t g, int64_t tile) {
     if (c->w_free_rec[s]) HIPCHK(c, hipStreamWaitEvent(c->h2d, c->w_free[s], 0));
     const uint64_t bytes = p->info.tile_bytes;
     const char *src = static_cast<const char *>(p->prob.W_host) + (uint64_t)tile * bytes;
+    zi_file_source *fs = c->source_of(p);
+    int fslot = -1;
+    if (fs) {  // the tile comes from the file source's staging buffer, once read
+        const void *staged = nullptr;
+        const zi_status st = source_acquire(fs, tile, &staged, &fslot);
+        if (st != ZI_OK) {  // passes already enqueued in part: the context stays failed
+            if (c->sticky == ZI_OK) {
+                c->sticky = st;
+                c->sticky_msg = zi_last_error();
+            }
+            return st;
+        }
+        src = static_cast<const char *>(staged);
+    }
     hipEvent_t ea = nullptr, eb = nullptr;
     if (c->timing) {
         zi_status st = ev_timed(c, &ea);
-        if (st != ZI_OK) return st;
+        if (st != ZI_OK) {
+            if (fs) source_abandon(fs, fslot);
+            return st;
+        }
         HIPCHK(c, hipEventRecord(ea, c->h2d));
     }
-    HIPCHK(c, hipMemcpyAsync(c->wslot(s), src, bytes, hipMemcpyHostToDevice, c->h2d));
+    {
+        hipError_t e = hipMemcpyAsync(c->wslot(s), src, bytes, hipMemcpyHostToDevice, c->h2d);
+        if (e == hipSuccess && fs) e = hipEventRecord(source_copy_event(fs, fslot), c->h2d);
+        if (e != hipSuccess) {
+            if (fs) source_abandon(fs, fslot);
+            return hip_fail(c, e, "hipMemcpyAsync(tile to device)");
+        }
+        if (fs) source_release(fs, fslot);
+    }
     if (c->timing) {
         zi_status st = ev_timed(c, &eb);
         if (st != ZI_OK) return st;
@@ -597,10 +630,30 @@ zi_status zi_tiled_linear_bwd_recompute(zi_ctx *ctx, const zi_plan *plan, const 
     return run_bwd(ctx, plan, X_dev, dY_dev, dX_dev, Yr_dev);
 }
 
+zi_status zi_ctx_attach_source(zi_ctx *ctx, const zi_plan *plan, zi_file_source *src) {
+    clear_error();
+    if (!ctx || !plan) return fail(ZI_ERR_ARG, "context and plan are required");
+    if (src && source_plan(src) != plan) return fail(ZI_ERR_STATE, "the source was made for another plan");
+    if (src && ctx->adam_of(plan))
+        return fail(ZI_ERR_STATE, "an optimizer is attached to this plan; it updates W_host, not the file");
+    for (auto it = ctx->sources.begin(); it != ctx->sources.end(); ++it) {
+        if (it->first != plan) continue;
+        if (src)
+            it->second = src;
+        else
+            ctx->sources.erase(it);
+        return ZI_OK;
+    }
+    if (src) ctx->sources.emplace_back(plan, src);
+    return ZI_OK;
+}
+
 zi_status zi_ctx_attach_adam(zi_ctx *ctx, const zi_plan *plan, zi_adam *adam) {
     clear_error();
     if (!ctx || !plan) return fail(ZI_ERR_ARG, "context and plan are required");
     if (adam && adam_plan(adam) != plan) return fail(ZI_ERR_STATE, "the optimizer was made for another plan");
+    if (adam && ctx->source_of(plan))
+        return fail(ZI_ERR_STATE, "a file source is attached to this plan; the optimizer would update W_host");
     for (auto it = ctx->adams.begin(); it != ctx->adams.end(); ++it) {
         if (it->first != plan) continue;
         if (adam)

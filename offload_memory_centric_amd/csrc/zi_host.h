@@ -1,6 +1,7 @@
 // zi_host.h -- host-side internals shared by zi_plan.cpp and zi_api.cpp.
 #pragma once
 
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 #include "../../include/zi.h"
@@ -55,5 +56,16 @@ void adam_enqueue(zi_adam *a, int64_t tile, void *landed_event);
 void adam_wait_tile(zi_adam *a, int64_t tile);
 // Block until the queue is empty; the first failure, if any.
 zi_status adam_wait_all(zi_adam *a);
+
+// The file source (zi_source.cpp), as the context drives it.
+const zi_plan *source_plan(const zi_file_source *s);
+// Block until `tile` is in a staging buffer; its host address and slot.
+zi_status source_acquire(zi_file_source *s, int64_t tile, const void **host, int *slot);
+// The event the caller records on the copy stream after the copy out of `slot`.
+hipEvent_t source_copy_event(zi_file_source *s, int slot);
+// The copy out of `slot` is enqueued and its event recorded.
+void source_release(zi_file_source *s, int slot);
+// No copy out of `slot` was enqueued after all.
+void source_abandon(zi_file_source *s, int slot);
 
 }  // namespace zi

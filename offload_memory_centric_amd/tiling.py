@@ -159,6 +159,10 @@ class Context:
         None detaches."""
         zi.zi_ctx_attach_adam(self.handle, plan.handle, None if adam is None else adam.handle)
 
+    def attach_source(self, plan: Plan, source: Optional["FileSource"]):
+        """Read `plan`'s tiles from a file source (see FileSource); None detaches."""
+        zi.zi_ctx_attach_source(self.handle, plan.handle, None if source is None else source.handle)
+
     def sync(self):
         zi.zi_sync(self.handle)
 
@@ -222,6 +226,41 @@ class Adam:
             self.close()
         except Exception:
             pass
+
+
+class FileSource:
+    """A plan's weight read from a file (zi_file_source_*): W^t [M x K] in the
+    plan's dtype from byte `offset` on, read ahead of the passes into
+    `staging` pinned tile buffers."""
+
+    def __init__(self, plan: Plan, path: str, offset: int = 0, staging: int = 3, threads: int = 4):
+        self.plan = plan
+        self.handle = zi.zi_file_source_create(plan.handle, path, offset, staging, threads)
+
+    def read(self, tile: int, dst) -> None:
+        zi.zi_file_source_read(self.handle, tile, dst)
+
+    def stats(self) -> dict:
+        return zi.zi_file_source_stats_get(self.handle)
+
+    def close(self):
+        if self.handle:
+            zi.zi_file_source_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def write_weight_file(path: str, W_host: torch.Tensor, chunk_bytes: int = 1 << 28) -> None:
+    """Write a host weight's bytes to `path` (for a FileSource), in chunks."""
+    flat = W_host.contiguous().view(torch.uint8).view(-1)
+    with open(path, "wb") as f:
+        for at in range(0, flat.numel(), chunk_bytes):
+            f.write(flat[at:at + chunk_bytes].numpy())
 
 
 def ffn_block_step(ctx: Context, p1: Plan, p2: Plan, X, A, H, Y, dY, dH, dA, dX, Yr) -> None:

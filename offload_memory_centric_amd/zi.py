@@ -15,9 +15,10 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzi.so")
 
-ZI_OK, ZI_ERR_ARG, ZI_ERR_SHAPE, ZI_ERR_BUDGET, ZI_ERR_NOT_PINNED, ZI_ERR_ALIGN, ZI_ERR_HIP, ZI_ERR_STATE = range(8)
+(ZI_OK, ZI_ERR_ARG, ZI_ERR_SHAPE, ZI_ERR_BUDGET, ZI_ERR_NOT_PINNED, ZI_ERR_ALIGN, ZI_ERR_HIP, ZI_ERR_STATE,
+ ZI_ERR_IO) = range(9)
 STATUS_NAMES = ["ZI_OK", "ZI_ERR_ARG", "ZI_ERR_SHAPE", "ZI_ERR_BUDGET", "ZI_ERR_NOT_PINNED",
-                "ZI_ERR_ALIGN", "ZI_ERR_HIP", "ZI_ERR_STATE"]
+                "ZI_ERR_ALIGN", "ZI_ERR_HIP", "ZI_ERR_STATE", "ZI_ERR_IO"]
 ZI_F16, ZI_BF16 = 1, 2
 ZI_FLAG_F32_OUT = 0x1
 DTYPE_CODES = {"f16": ZI_F16, "bf16": ZI_BF16}
@@ -76,6 +77,14 @@ class zi_adam_hparams(ctypes.Structure):
 
 class zi_adam_stats(ctypes.Structure):
     _fields_ = [("tiles_done", ctypes.c_int64), ("busy_s", ctypes.c_double), ("bytes", ctypes.c_double)]
+
+
+class zi_source_stats(ctypes.Structure):
+    _fields_ = [("tiles_read", ctypes.c_int64), ("restarts", ctypes.c_int64), ("read_s", ctypes.c_double),
+                ("bytes", ctypes.c_double), ("wait_s", ctypes.c_double), ("direct", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
 
 
 class zi_stats(ctypes.Structure):
@@ -141,6 +150,12 @@ _sigs = {
     "zi_ctx_attach_adam": (_S, [_P, _P, _P]),
     "zi_adam_wait": (_S, [_P]),
     "zi_adam_stats_get": (_S, [_P, ctypes.POINTER(zi_adam_stats)]),
+    "zi_file_source_create": (_S, [_P, ctypes.c_char_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.POINTER(_P)]),
+    "zi_file_source_destroy": (_S, [_P]),
+    "zi_ctx_attach_source": (_S, [_P, _P, _P]),
+    "zi_file_source_read": (_S, [_P, ctypes.c_int64, _P]),
+    "zi_file_source_stats_get": (_S, [_P, ctypes.POINTER(zi_source_stats)]),
     "zi_host_alloc": (_S, [ctypes.c_uint64, ctypes.POINTER(_P)]),
     "zi_host_free": (_S, [_P]),
     "zi_last_error": (ctypes.c_char_p, []),
@@ -332,6 +347,31 @@ def zi_adam_stats_get(adam) -> dict:
     s = zi_adam_stats()
     _check(_lib.zi_adam_stats_get(adam, ctypes.byref(s)))
     return {"tiles_done": s.tiles_done, "busy_s": s.busy_s, "bytes": s.bytes}
+
+
+def zi_file_source_create(plan, path: str, offset: int = 0, staging: int = 3, threads: int = 4) -> int:
+    h = _P()
+    _check(_lib.zi_file_source_create(plan, os.fsencode(path), int(offset), int(staging), int(threads),
+                                      ctypes.byref(h)))
+    return h.value
+
+
+def zi_file_source_destroy(src) -> None:
+    _check(_lib.zi_file_source_destroy(src))
+
+
+def zi_ctx_attach_source(ctx, plan, src) -> None:
+    _check(_lib.zi_ctx_attach_source(ctx, plan, src))
+
+
+def zi_file_source_read(src, tile: int, dst) -> None:
+    _check(_lib.zi_file_source_read(src, int(tile), _ptr(dst)))
+
+
+def zi_file_source_stats_get(src) -> dict:
+    s = zi_source_stats()
+    _check(_lib.zi_file_source_stats_get(src, ctypes.byref(s)))
+    return s.as_dict()
 
 
 def zi_host_alloc(nbytes: int) -> int:

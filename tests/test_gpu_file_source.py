@@ -1,0 +1,124 @@
+"""The tiled path with its weights read from files (the NVMe tier), on the
+GPU: results bit-identical to the oracle's on exact inputs, and to the same
+passes fed from pinned host memory on Gaussian ones."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from offload_memory_centric_amd import inputs
+from zi_testlib import host_bits, lib, make_linear_inputs, say
+
+pytestmark = pytest.mark.gpu
+
+
+def weight_file(tmp_path, name, W_host):
+    tiling = lib()
+    path = str(tmp_path / name)
+    tiling.write_weight_file(path, W_host)
+    return path
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("N,d,staging", [(4, 2, 2), (4, 1, 3), (8, 3, 4), (1, 1, 2)])
+def test_linear_from_file_bit_exact(tmp_path, dtype, N, d, staging):
+    # small integers: every sum exact, every stored result unique; three
+    # forward + backward steps back to back, so the read-ahead crosses passes
+    T, K, M, S = 128, 512, 2048, 3
+    tiling = lib()
+    say("case file source", dtype, "N", N, "d", d, "staging", staging)
+    X, Wt, dY = make_linear_inputs(T, K, M, dtype, "small_int", seed=7)
+    path = weight_file(tmp_path, "w.bin", Wt)
+    W_bits = host_bits(Wt).copy()
+    dWt = tiling.host_tensor((M, K), inputs.torch_dtype(dtype))
+    plan = tiling.Plan(T, K, M, N, d, dtype, None, dWt)
+    ctx = tiling.Context(plan)
+    src = tiling.FileSource(plan, path, staging=staging, threads=3)
+    ctx.attach_source(plan, src)
+    Ys = [torch.empty((T, M), dtype=inputs.torch_dtype(dtype), device="cuda") for _ in range(S)]
+    dXs = [torch.empty((T, K), dtype=torch.float32, device="cuda") for _ in range(S)]
+    torch.cuda.synchronize()
+    for s in range(S):
+        ctx.fwd(plan, X, Ys[s])
+        ctx.bwd(plan, X, dY, dXs[s])
+    ctx.sync()
+    Xb, dYb = host_bits(X), host_bits(dY)
+    Y = oracle.encode(oracle.linear_fwd(Xb, W_bits, dtype), dtype)
+    dX, dW = oracle.linear_bwd(Xb, W_bits, dYb, dtype)
+    for s in range(S):
+        assert np.array_equal(host_bits(Ys[s]), Y), "Y of step %d" % (s + 1)
+        assert np.array_equal(dXs[s].cpu().numpy().astype(np.float64), dX), "dX of step %d" % (s + 1)
+    assert np.array_equal(host_bits(dWt), oracle.encode(dW, dtype)), "dW"
+    st = src.stats()
+    say("  source", st)
+    assert st["tiles_read"] >= 2 * S * N and st["restarts"] == 0
+    ctx.attach_source(plan, None)
+    ctx.close()
+    src.close()
+    plan.close()
+
+
+def test_ffn_block_from_files_equals_host(tmp_path):
+    # the block with both weights read from files gives the same bits as the
+    # block fed from pinned host memory (same kernels, same inputs)
+    from test_gpu_ffn import ffn_setup
+    T, D, F, N1, N2, d = 96, 256, 1024, 4, 4, 2
+    say("case ffn from files")
+    tiling, ctx, p1, p2, b, h = ffn_setup(T, D, F, N1, N2, d, "f16", seed=40, w_std=0.05)
+    torch.cuda.synchronize()
+    tiling.ffn_block_step(ctx, p1, p2, b["X"], b["A"], b["H"], b["Y"], b["dY"], b["dH"], b["dA"], b["dX"], b["Yr"])
+    ctx.sync()
+    ref = {k: b[k].clone() for k in ("A", "H", "Y", "dH", "dA", "dX")}
+    ref_dw = (host_bits(h["dW1t"]).copy(), host_bits(h["dW2t"]).copy())
+    s1 = tiling.FileSource(p1, weight_file(tmp_path, "w1.bin", h["W1t"]), staging=3, threads=2)
+    s2 = tiling.FileSource(p2, weight_file(tmp_path, "w2.bin", h["W2t"]), staging=2, threads=2)
+    ctx.attach_source(p1, s1)
+    ctx.attach_source(p2, s2)
+    h["W1t"].zero_()  # the passes must not read the host copies any more
+    h["W2t"].zero_()
+    for k in ref:
+        b[k].zero_()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        tiling.ffn_block_step(ctx, p1, p2, b["X"], b["A"], b["H"], b["Y"], b["dY"], b["dH"], b["dA"], b["dX"],
+                              b["Yr"])
+    ctx.sync()
+    for k in ref:
+        assert torch.equal(b[k], ref[k]), k
+    assert np.array_equal(host_bits(h["dW1t"]), ref_dw[0]) and np.array_equal(host_bits(h["dW2t"]), ref_dw[1])
+    say("  sources", s1.stats(), s2.stats())
+    for s in (s1, s2):
+        assert s.stats()["restarts"] == 0
+    ctx.attach_source(p1, None)
+    ctx.attach_source(p2, None)
+    ctx.close()
+    s1.close()
+    s2.close()
+
+
+def test_source_and_optimizer_exclude_each_other(tmp_path):
+    T, K, M = 128, 512, 2048
+    tiling = lib()
+    X, Wt, dY = make_linear_inputs(T, K, M, "f16", "small_int", seed=8)
+    dWt = tiling.host_tensor((M, K), torch.float16)
+    plan = tiling.Plan(T, K, M, 4, 2, "f16", Wt, dWt)
+    ctx = tiling.Context(plan)
+    src = tiling.FileSource(plan, weight_file(tmp_path, "w.bin", Wt))
+    adam = tiling.Adam(plan, threads=2)
+    ctx.attach_source(plan, src)
+    from offload_memory_centric_amd import zi
+    with pytest.raises(zi.ZiError) as e:
+        ctx.attach_adam(plan, adam)
+    assert e.value.status == zi.ZI_ERR_STATE
+    ctx.attach_source(plan, None)
+    ctx.attach_adam(plan, adam)
+    with pytest.raises(zi.ZiError) as e:
+        ctx.attach_source(plan, src)
+    assert e.value.status == zi.ZI_ERR_STATE
+    ctx.attach_adam(plan, None)
+    ctx.close()
+    adam.close()
+    src.close()
+    plan.close()
