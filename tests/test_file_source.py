@@ -25,7 +25,7 @@ def aligned(nbytes, align=4096):
 @pytest.fixture
 def weight_file(tmp_path):
     def make(nbytes, offset=0, seed=0):
-        data = np.random.default_rng(seed).integers(0, 256, offset + nbytes, dtype=np.uint8)
+        data = np.frombuffer(np.random.default_rng(seed).bytes(offset + nbytes), np.uint8)
         path = str(tmp_path / ("w_%d_%d.bin" % (offset, seed)))
         data.tofile(path)
         return path, data
@@ -56,16 +56,16 @@ def test_tiles_read_back(weight_file, offset, threads):
 
 
 def test_big_tile_split_over_threads(weight_file):
-    # a 40 MiB tile: three pieces (16, 16 and 8 MiB) dealt over the threads
-    h, info = plan(K=2560, M=32768, N=4)
+    # a 20 MiB tile: two pieces (16 and 4 MiB) dealt over the threads
+    h, info = plan(K=2560, M=8192, N=2)
     try:
-        assert info.tile_bytes == 2560 * 8192 * 2
-        path, data = weight_file(info.tile_bytes * 4, 0, seed=3)
+        assert info.tile_bytes == 2560 * 4096 * 2
+        path, data = weight_file(info.tile_bytes * 2, 0, seed=3)
         src = zi.zi_file_source_create(h, path, 0, 3, 4)
         try:
             dst = aligned(info.tile_bytes)
-            zi.zi_file_source_read(src, 3, dst)
-            assert np.array_equal(dst, data[3 * info.tile_bytes:])
+            zi.zi_file_source_read(src, 1, dst)
+            assert np.array_equal(dst, data[info.tile_bytes:])
         finally:
             zi.zi_file_source_destroy(src)
     finally:
