@@ -69,7 +69,10 @@ def parse():
     ap.add_argument("--nvme-threads", type=int, default=8,
                     help="threads that split each tile's file read")
     ap.add_argument("--nvme-staging", type=int, default=3,
-                    help="pinned staging buffers per weight: how many tiles the reads may run ahead")
+                    help="pinned staging buffers per weight (with --nvme-tier: of the tier)")
+    ap.add_argument("--nvme-tier", action="store_true",
+                    help="read all weights with one reader that follows the order the first step "
+                         "used the tiles in (the warmup step is the recorded one)")
     ap.add_argument("--choose", action="store_true",
                     help="measure the products' rates at several tile widths, let the planner "
                          "choose N and d from them, and time every width (prints its own JSON line)")
@@ -272,12 +275,18 @@ def main():
         config = {"workload": "tiled_linear_fwd_bwd", "T": T, "K": K, "M": M, "N": N, "n": M // N,
                   "d": d, "weights": "pinned host", "dtype": dtype}
         plans = (p,)
-    sources = []
+    sources, tier = [], None
     if args.nvme:
         if args.adam:
             raise SystemExit("--nvme and --adam exclude each other (the optimizer updates host memory)")
-        sources = nvme_sources(args, tiling, ctx, plans)
+        sources, tier = nvme_sources(args, tiling, ctx, plans)
         config["weights"] = "file -> pinned staging -> HBM"
+        if tier is not None:
+            pass_step = step
+
+            def step():
+                pass_step()
+                tier.step()
     torch.cuda.synchronize()
 
     # Per-step marks: an event on the compute stream after every step (no
@@ -387,6 +396,8 @@ def main():
 
     if sources:
         result["nvme"] = nvme_report(args, tiling, sources, src_before, kinds, wall, flops_step * args.steps)
+        if tier is not None:
+            result["nvme"]["tier"] = tier.stats()
     adams = []
     if args.adam:
         result["adam"] = host_adam_leg(args, torch, tiling, ctx, plans, marked, spans, ms_step)
@@ -401,6 +412,8 @@ def main():
     ctx.close()
     for a in adams:
         a.close()
+    if tier is not None:
+        tier.close()
     for src, path in sources:
         src.close()
         os.remove(path)
@@ -503,9 +516,11 @@ def choose_leg(args, torch, tiling, inputs, link, steps=3):
 
 def nvme_sources(args, tiling, ctx, plans):
     """Write every plan's weight to a file under args.nvme and read the tiles
-    from there: one source per weight, args.nvme_staging staging buffers each."""
+    from there: one source per weight, args.nvme_staging staging buffers each,
+    or (--nvme-tier) all of them under one tier with that many buffers."""
     os.makedirs(args.nvme, exist_ok=True)
     out = []
+    tier = tiling.Tier(staging=args.nvme_staging, threads=args.nvme_threads) if args.nvme_tier else None
     for j, pl in enumerate(plans):
         path = os.path.join(args.nvme, "zi_weight_%d.bin" % j)
         t0 = time.perf_counter()
@@ -513,9 +528,11 @@ def nvme_sources(args, tiling, ctx, plans):
         os.sync()
         log("wrote %s (%.1f GB) in %.1f s" % (path, pl.K * pl.M * 2 / 1e9, time.perf_counter() - t0))
         src = tiling.FileSource(pl, path, staging=args.nvme_staging, threads=args.nvme_threads)
+        if tier is not None:
+            tier.add(src)
         ctx.attach_source(pl, src)
         out.append((src, path))
-    return out
+    return out, tier
 
 
 def nvme_report(args, tiling, sources, before, kinds, wall, flops):

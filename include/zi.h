@@ -390,7 +390,8 @@ typedef struct zi_file_source zi_file_source;
 zi_status zi_file_source_create(const zi_plan *plan, const char *path, uint64_t offset, int32_t staging,
                                 int32_t threads, zi_file_source **out);
 /* Stops the reader, waits for every copy out of the staging buffers, frees
- * them and closes the file.  Detach the source from its context first. */
+ * them and closes the file.  Detach the source from its context first.
+ * ZI_ERR_STATE for a source under a tier that still exists. */
 zi_status zi_file_source_destroy(zi_file_source *src);
 /* Attach `src` (or NULL: detach) to `plan` on `ctx`.  ZI_ERR_STATE if the
  * source was made for another plan, or if an optimizer is attached to the
@@ -400,7 +401,8 @@ zi_status zi_ctx_attach_source(zi_ctx *ctx, const zi_plan *plan, zi_file_source 
  * source that reads with O_DIRECT, else ZI_ERR_ALIGN), synchronously, with the
  * source's threads.  No GPU is involved.  ZI_ERR_IO on a failed read. */
 zi_status zi_file_source_read(zi_file_source *src, int64_t tile, void *dst);
-/* Totals since creation: tiles read ahead, restarts of the read-ahead,
+/* Totals since creation: tiles read for the passes, restarts of the
+ * read-ahead (with on-demand reads, counted for the tier the source is in),
  * seconds spent reading, bytes read, seconds the passes waited for a read,
  * and whether the file is read with O_DIRECT. */
 typedef struct {
@@ -412,6 +414,41 @@ typedef struct {
     int32_t direct;
 } zi_source_stats;
 zi_status zi_file_source_stats_get(zi_file_source *src, zi_source_stats *out);
+
+/* A tier of file sources read by one reader in the order the passes use
+ * them (pwwt.cn ZeRO-Infinity article, section "关键技术三：Overlap-Centric
+ * Design": the prefetcher follows the order in which the operators ran in
+ * the first iteration).  The tier owns `staging` (>= 2) pinned buffers of
+ * the largest tile of its sources and splits every read over `threads`
+ * positioned reads.  During the first step the tier records the order of
+ * the tile requests of all its sources and serves each on demand; the first
+ * zi_tier_step() call ends the recording, and from then on the reader reads
+ * ahead along that trace, across weights and across the end of a step into
+ * the next.  A request the trace does not predict restarts the read-ahead at
+ * its next place in the trace, or is read on demand.  A standalone source
+ * reads ahead with a tier of its own whose trace is its tiles in order. */
+typedef struct zi_tier zi_tier;
+zi_status zi_tier_create(int32_t staging, int32_t threads, zi_tier **out);
+/* Put `src` under the tier; before the source or the tier is first used.
+ * ZI_ERR_STATE if the source already has a tier or the tier has started. */
+zi_status zi_tier_add(zi_tier *tier, zi_file_source *src);
+/* Mark the end of a step (after its passes are enqueued).  The first call
+ * fixes the trace; later calls check that the step ended where the trace
+ * does and otherwise restart the read-ahead at the trace's start. */
+zi_status zi_tier_step(zi_tier *tier);
+/* Stops the reader, waits for every copy out of the staging buffers and
+ * frees them; the sources are then standalone again.  Detach the sources
+ * from their context first; destroy the tier before its sources. */
+zi_status zi_tier_destroy(zi_tier *tier);
+typedef struct {
+    int64_t trace_len;     /* requests per step (so far, while recording) */
+    int64_t steps;         /* zi_tier_step calls */
+    int64_t tiles_read;
+    int64_t restarts;      /* read-ahead restarted at another trace position */
+    int64_t demand_reads;  /* requests read on demand (all of the first step's) */
+    double read_s, bytes, wait_s;
+} zi_tier_stats;
+zi_status zi_tier_stats_get(zi_tier *tier, zi_tier_stats *out);
 
 /* Page-locked host memory (hipHostMalloc) for W^t / dW^t; 4096-byte aligned. */
 zi_status zi_host_alloc(uint64_t bytes, void **out);

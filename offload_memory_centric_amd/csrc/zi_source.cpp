@@ -110,43 +110,81 @@ void free_buffers(std::vector<char *> &v) {
 using namespace zi;
 
 struct zi_file_source {
-    enum State { FREE, READING, READY, IN_COPY };
-    struct Slot {
-        int64_t tile = -1;
-        State state = FREE;
-        int err = 0;        // errno of a failed read
-        hipEvent_t copied = nullptr;
-    };
-
     const zi_plan *plan = nullptr;
     int fd = -1;
     bool direct = false;
     uint64_t offset = 0, tile_bytes = 0;
     int64_t N = 0;
     int S = 2, threads = 4;
-    int device = -1;
+    zi_tier *tier = nullptr;  // the tier that reads this source's tiles
+    bool own_tier = false;    // a private tier made on first use, its trace the tiles in order
+    // statistics, under the tier's mutex
+    int64_t tiles_read = 0;
+    double read_s = 0, bytes = 0, wait_s = 0;
+};
 
-    std::vector<char *> buf;     // pinned staging buffers (hipHostMalloc), made on first use
-    std::vector<char *> bounce;  // the reader's per-thread buffers for direct reads
+// A tier of file sources: S pinned staging buffers and one reader thread that
+// reads the sources' tiles ahead of the passes, in the order of a trace.  A
+// shared tier records the order of the requests during the first step (the
+// requests are then served on demand) and replays it in every later step; a
+// standalone source gets a private tier whose trace is its tiles in order.
+struct zi_tier {
+    enum State { FREE, READING, READY, IN_COPY };
+    struct Item {
+        zi_file_source *src = nullptr;
+        int64_t tile = -1;
+        bool operator==(const Item &o) const { return src == o.src && tile == o.tile; }
+    };
+    struct Slot {
+        Item item;
+        int64_t tpos = -1;  // trace position of the item (-1: read on demand)
+        State state = FREE;
+        int err = 0;        // errno of a failed read
+        hipEvent_t copied = nullptr;
+    };
+
+    int S = 2, threads = 4;
+    bool shared = false;
+    std::vector<zi_file_source *> srcs;
+    std::vector<char *> buf;     // pinned staging buffers, made on first use
+    std::vector<char *> bounce;  // per-thread buffers for direct reads
     std::vector<Slot> slots;
+    std::vector<Item> trace, rec;
+    bool recording = false;  // a shared tier records until its first step mark
+    int64_t pos = 0;         // trace position the next request is expected at
+    int64_t rpos = 0;        // trace position the reader reads next
+    bool demand = false;     // one read the reader does before the trace's next
+    Item demand_item;
+    int next_slot = 0, cons_slot = 0;
+    uint64_t gen = 0;  // bumped when the read-ahead restarts
+    int device = -1;
+    bool started = false, stop = false;
     std::mutex mu;
     std::condition_variable cv;
     std::thread reader;
-    bool started = false, stop = false;
-    int64_t next_tile = 0;  // the reader's next tile
-    int next_slot = 0;      // the slot the reader fills next
-    int cons_slot = 0;      // the slot the next request is served from
-    uint64_t gen = 0;       // bumped when the read-ahead restarts
-    // statistics
-    int64_t tiles_read = 0, restarts = 0;
+    int64_t tiles_read = 0, restarts = 0, demand_reads = 0, steps = 0;
     double read_s = 0, bytes = 0, wait_s = 0;
+
+    bool read_ahead() const { return !recording && !trace.empty(); }
+    static bool holding(const Slot &s) { return s.state == READING || s.state == READY; }
+
+    void discard_ready() {
+        for (auto &sl : slots)
+            if (sl.state == READY) {
+                sl.state = FREE;
+                sl.item = Item{};
+                sl.tpos = -1;
+            }
+    }
 
     void run() {
         if (device >= 0) (void)hipSetDevice(device);
         std::unique_lock<std::mutex> lock(mu);
         for (;;) {
             const int k = next_slot;
-            cv.wait(lock, [&] { return stop || slots[k].state == FREE || slots[k].state == IN_COPY; });
+            cv.wait(lock, [&] {
+                return stop || ((slots[k].state == FREE || slots[k].state == IN_COPY) && (demand || read_ahead()));
+            });
             if (stop) return;
             if (slots[k].state == IN_COPY) {
                 // the staging buffer is free once the copy that reads it is done
@@ -157,29 +195,42 @@ struct zi_file_source {
                 if (slots[k].state == IN_COPY) slots[k].state = FREE;
                 continue;
             }
-            const int64_t t = next_tile;
+            Item it;
+            int64_t tp = -1;
+            if (demand) {
+                it = demand_item;
+                demand = false;
+            } else {
+                tp = rpos++;
+                it = trace[(size_t)(tp % (int64_t)trace.size())];
+            }
             const uint64_t g = gen;
-            slots[k].tile = t;
+            slots[k].item = it;
+            slots[k].tpos = tp;
             slots[k].state = READING;
             slots[k].err = 0;
-            next_tile = (t + 1) % N;
             next_slot = (k + 1) % S;
             lock.unlock();
             const auto t0 = std::chrono::steady_clock::now();
-            const int err = parallel_pread(fd, buf[k], offset + (uint64_t)t * tile_bytes, tile_bytes, threads,
-                                           direct ? bounce.data() : nullptr);
+            zi_file_source *src = it.src;
+            const int err = parallel_pread(src->fd, buf[k], src->offset + (uint64_t)it.tile * src->tile_bytes,
+                                           src->tile_bytes, threads, src->direct ? bounce.data() : nullptr);
             const double secs = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
             lock.lock();
             if (gen != g) {
                 slots[k].state = FREE;  // the read-ahead restarted meanwhile: discard
-                slots[k].tile = -1;
+                slots[k].item = Item{};
+                slots[k].tpos = -1;
             } else {
                 slots[k].state = READY;
                 slots[k].err = err;
                 if (!err) {
                     ++tiles_read;
                     read_s += secs;
-                    bytes += (double)tile_bytes;
+                    bytes += (double)src->tile_bytes;
+                    ++src->tiles_read;
+                    src->read_s += secs;
+                    src->bytes += (double)src->tile_bytes;
                 }
             }
             cv.notify_all();
@@ -191,27 +242,36 @@ namespace zi {
 
 const zi_plan *source_plan(const zi_file_source *s) { return s->plan; }
 
-// First use, on the context's device: pinned staging buffers, their events and
-// the reader thread.
-static zi_status source_start(zi_file_source *s) {
-    if (s->started) return ZI_OK;
+// First use, on the context's device: pinned staging buffers (the largest
+// tile of the tier's sources each), their events, the read buffers and the
+// reader thread.
+static zi_status tier_start(zi_tier *t) {
+    if (t->started) return ZI_OK;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(ZI_ERR_HIP, "hipGetDevice failed");
-    std::vector<char *> bufs(s->S, nullptr);
-    std::vector<hipEvent_t> evs(s->S, nullptr);
+    uint64_t bytes = 0;
+    bool direct = false;
+    for (zi_file_source *s : t->srcs) {
+        bytes = std::max(bytes, s->tile_bytes);
+        direct = direct || s->direct;
+    }
+    std::vector<char *> bufs(t->S, nullptr);
+    std::vector<hipEvent_t> evs(t->S, nullptr);
+    std::vector<char *> bb;
     auto undo = [&] {
         for (hipEvent_t e : evs)
             if (e) (void)hipEventDestroy(e);
         for (char *p : bufs)
             if (p) (void)hipHostFree(p);
+        free_buffers(bb);
     };
-    for (int k = 0; k < s->S; ++k) {
+    for (int k = 0; k < t->S; ++k) {
         void *p = nullptr;
-        hipError_t e = hipHostMalloc(&p, s->tile_bytes, hipHostMallocDefault);
+        hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocDefault);
         if (e != hipSuccess) {
             undo();
-            return fail(ZI_ERR_HIP, "hipHostMalloc of a %llu B staging buffer: %s",
-                        (unsigned long long)s->tile_bytes, hipGetErrorString(e));
+            return fail(ZI_ERR_HIP, "hipHostMalloc of a %llu B staging buffer: %s", (unsigned long long)bytes,
+                        hipGetErrorString(e));
         }
         bufs[k] = static_cast<char *>(p);
         e = hipEventCreateWithFlags(&evs[k], hipEventDisableTiming | hipEventBlockingSync);
@@ -221,93 +281,143 @@ static zi_status source_start(zi_file_source *s) {
             return fail(ZI_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
         }
     }
-    if (s->direct) {
-        s->bounce = bounce_buffers(s->threads);
-        if ((int)s->bounce.size() != s->threads) {
-            free_buffers(s->bounce);
+    if (direct) {
+        bb = bounce_buffers(t->threads);
+        if ((int)bb.size() != t->threads) {
             undo();
             return fail(ZI_ERR_ARG, "out of host memory for the read buffers");
         }
     }
-    s->device = dev;
-    s->buf = bufs;
-    for (int k = 0; k < s->S; ++k) s->slots[k].copied = evs[k];
+    t->device = dev;
+    t->buf = bufs;
+    t->bounce = bb;
+    for (int k = 0; k < t->S; ++k) t->slots[k].copied = evs[k];
     try {
-        s->reader = std::thread([s] { s->run(); });
+        t->reader = std::thread([t] { t->run(); });
     } catch (...) {
-        for (auto &sl : s->slots) sl.copied = nullptr;
-        s->buf.clear();
-        free_buffers(s->bounce);
+        for (auto &sl : t->slots) sl.copied = nullptr;
+        t->buf.clear();
+        t->bounce.clear();
         undo();
         return fail(ZI_ERR_STATE, "could not start the reader thread");
     }
-    s->started = true;
+    t->started = true;
     return ZI_OK;
 }
 
-zi_status source_acquire(zi_file_source *s, int64_t tile, const void **host, int *slot) {
-    zi_status st = source_start(s);
-    if (st != ZI_OK) return st;
-    if (tile < 0 || tile >= s->N) return fail(ZI_ERR_ARG, "tile %lld out of range", (long long)tile);
-    const auto t0 = std::chrono::steady_clock::now();
-    std::unique_lock<std::mutex> lock(s->mu);
-    const int k = s->cons_slot;
-    const bool ahead = (s->slots[k].state == zi_file_source::READING || s->slots[k].state == zi_file_source::READY) &&
-                       s->slots[k].tile == tile;
-    const bool coming = s->slots[k].state != zi_file_source::READING && s->slots[k].state != zi_file_source::READY &&
-                        s->next_slot == k && s->next_tile == tile;
-    if (!ahead && !coming) {
-        // restart the read-ahead at `tile`, from the slot the request takes
-        ++s->gen;
-        ++s->restarts;
-        for (int j = 0; j < s->S; ++j)
-            if (s->slots[j].state == zi_file_source::READY) {
-                s->slots[j].state = zi_file_source::FREE;
-                s->slots[j].tile = -1;
-            }
-        s->next_tile = tile;
-        s->next_slot = k;
-        s->cv.notify_all();
+// Stop the reader, wait for every copy out of the staging buffers, free them.
+static void tier_stop(zi_tier *t) {
+    if (!t->started) return;
+    {
+        std::lock_guard<std::mutex> lock(t->mu);
+        t->stop = true;
     }
-    s->cv.wait(lock, [&] {
-        return s->slots[k].state == zi_file_source::READY && s->slots[k].tile == tile;
-    });
-    s->wait_s += std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
-    if (s->slots[k].err) {
-        const int err = s->slots[k].err;
-        s->slots[k].state = zi_file_source::FREE;
-        s->slots[k].tile = -1;
-        s->cv.notify_all();
+    t->cv.notify_all();
+    t->reader.join();
+    for (auto &sl : t->slots)
+        if (sl.copied) {
+            (void)hipEventSynchronize(sl.copied);
+            (void)hipEventDestroy(sl.copied);
+            sl.copied = nullptr;
+        }
+    for (char *p : t->buf)
+        if (p) (void)hipHostFree(p);
+    t->buf.clear();
+    free_buffers(t->bounce);
+    t->started = false;
+}
+
+zi_status source_acquire(zi_file_source *s, int64_t tile, const void **host, int *slot) {
+    if (tile < 0 || tile >= s->N) return fail(ZI_ERR_ARG, "tile %lld out of range", (long long)tile);
+    if (!s->tier) {  // a standalone source: a private tier that reads its tiles in order
+        zi_tier *t = new (std::nothrow) zi_tier;
+        if (!t) return fail(ZI_ERR_ARG, "out of host memory");
+        t->S = s->S;
+        t->threads = s->threads;
+        t->srcs.push_back(s);
+        t->slots.assign(t->S, zi_tier::Slot{});
+        for (int64_t i = 0; i < s->N; ++i) t->trace.push_back(zi_tier::Item{s, i});
+        s->tier = t;
+        s->own_tier = true;
+    }
+    zi_tier *t = s->tier;
+    zi_status st = tier_start(t);
+    if (st != ZI_OK) return st;
+    const auto t0 = std::chrono::steady_clock::now();
+    const zi_tier::Item want{s, tile};
+    std::unique_lock<std::mutex> lock(t->mu);
+    const int k = t->cons_slot;
+    if (t->recording && t->rec.size() < (1u << 20)) t->rec.push_back(want);
+    const bool held = zi_tier::holding(t->slots[k]) && t->slots[k].item == want;
+    const bool coming = !zi_tier::holding(t->slots[k]) && t->next_slot == k && !t->demand && t->read_ahead() &&
+                        t->trace[(size_t)(t->rpos % (int64_t)t->trace.size())] == want;
+    if (!held && !coming) {
+        // serve this request next, from the slot it takes: restart the read-ahead
+        // at its next place in the trace, or read it on demand
+        ++t->gen;
+        t->discard_ready();
+        t->next_slot = k;
+        int64_t q = -1;
+        if (t->read_ahead()) {
+            const int64_t L = (int64_t)t->trace.size();
+            for (int64_t j = 0; j < L && q < 0; ++j)
+                if (t->trace[(size_t)((t->pos + j) % L)] == want) q = t->pos + j;
+        }
+        if (q >= 0) {
+            ++t->restarts;
+            t->rpos = q;
+            t->demand = false;
+        } else {
+            ++t->demand_reads;
+            t->demand = true;
+            t->demand_item = want;
+        }
+        t->cv.notify_all();
+    }
+    t->cv.wait(lock, [&] { return t->slots[k].state == zi_tier::READY && t->slots[k].item == want; });
+    const double waited = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+    t->wait_s += waited;
+    s->wait_s += waited;
+    if (t->slots[k].tpos >= 0) t->pos = t->slots[k].tpos + 1;
+    if (t->slots[k].err) {
+        const int err = t->slots[k].err;
+        t->slots[k].state = zi_tier::FREE;
+        t->slots[k].item = zi_tier::Item{};
+        t->cv.notify_all();
         return fail(ZI_ERR_IO, "reading tile %lld: %s", (long long)tile, strerror(err));
     }
-    *host = s->buf[k];
+    *host = t->buf[k];
     *slot = k;
     return ZI_OK;
 }
 
-hipEvent_t source_copy_event(zi_file_source *s, int slot) { return s->slots[slot].copied; }
+hipEvent_t source_copy_event(zi_file_source *s, int slot) { return s->tier->slots[slot].copied; }
 
 void source_release(zi_file_source *s, int slot) {
+    zi_tier *t = s->tier;
     {
-        std::lock_guard<std::mutex> lock(s->mu);
-        s->slots[slot].state = zi_file_source::IN_COPY;
-        s->cons_slot = (slot + 1) % s->S;
+        std::lock_guard<std::mutex> lock(t->mu);
+        t->slots[slot].state = zi_tier::IN_COPY;
+        t->cons_slot = (slot + 1) % t->S;
     }
-    s->cv.notify_all();
+    t->cv.notify_all();
 }
 
 // A request that fails after source_acquire (the copy could not be enqueued)
-// gives the buffer back unread by any copy.
+// gives the buffer back unread by any copy; the next request restarts the
+// read-ahead from this slot.
 void source_abandon(zi_file_source *s, int slot) {
+    zi_tier *t = s->tier;
     {
-        std::lock_guard<std::mutex> lock(s->mu);
-        s->slots[slot].state = zi_file_source::FREE;
-        s->slots[slot].tile = -1;
-        ++s->gen;
-        s->next_slot = slot;
-        s->cons_slot = slot;
+        std::lock_guard<std::mutex> lock(t->mu);
+        t->slots[slot].state = zi_tier::FREE;
+        t->slots[slot].item = zi_tier::Item{};
+        ++t->gen;
+        t->discard_ready();
+        t->next_slot = slot;
+        t->cons_slot = slot;
     }
-    s->cv.notify_all();
+    t->cv.notify_all();
 }
 
 }  // namespace zi
@@ -352,7 +462,6 @@ zi_status zi_file_source_create(const zi_plan *plan, const char *path, uint64_t 
     s->N = plan->prob.N;
     s->S = staging;
     s->threads = threads;
-    s->slots.assign(staging, zi_file_source::Slot{});
     *out = s;
     return ZI_OK;
 }
@@ -360,22 +469,10 @@ zi_status zi_file_source_create(const zi_plan *plan, const char *path, uint64_t 
 zi_status zi_file_source_destroy(zi_file_source *s) {
     clear_error();
     if (!s) return ZI_OK;
-    if (s->started) {
-        {
-            std::lock_guard<std::mutex> lock(s->mu);
-            s->stop = true;
-        }
-        s->cv.notify_all();
-        s->reader.join();
-        // no copy may still read a staging buffer when it is freed
-        for (auto &sl : s->slots)
-            if (sl.copied) {
-                (void)hipEventSynchronize(sl.copied);
-                (void)hipEventDestroy(sl.copied);
-            }
-        for (char *p : s->buf)
-            if (p) (void)hipHostFree(p);
-        free_buffers(s->bounce);
+    if (s->tier && !s->own_tier) return fail(ZI_ERR_STATE, "the source belongs to a tier: destroy the tier first");
+    if (s->own_tier) {
+        tier_stop(s->tier);
+        delete s->tier;
     }
     close(s->fd);
     delete s;
@@ -405,13 +502,96 @@ zi_status zi_file_source_read(zi_file_source *s, int64_t tile, void *dst) {
 zi_status zi_file_source_stats_get(zi_file_source *s, zi_source_stats *out) {
     clear_error();
     if (!s || !out) return fail(ZI_ERR_ARG, "source and out are required");
-    std::lock_guard<std::mutex> lock(s->mu);
+    out->direct = s->direct ? 1 : 0;
+    if (!s->tier) {
+        out->tiles_read = out->restarts = 0;
+        out->read_s = out->bytes = out->wait_s = 0.0;
+        return ZI_OK;
+    }
+    std::lock_guard<std::mutex> lock(s->tier->mu);
     out->tiles_read = s->tiles_read;
-    out->restarts = s->restarts;
+    out->restarts = s->tier->restarts + s->tier->demand_reads;
     out->read_s = s->read_s;
     out->bytes = s->bytes;
     out->wait_s = s->wait_s;
-    out->direct = s->direct ? 1 : 0;
+    return ZI_OK;
+}
+
+zi_status zi_tier_create(int32_t staging, int32_t threads, zi_tier **out) {
+    clear_error();
+    if (!out) return fail(ZI_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    if (staging < 2) return fail(ZI_ERR_ARG, "at least two staging buffers (got %d)", staging);
+    if (threads < 1) return fail(ZI_ERR_ARG, "threads must be >= 1 (got %d)", threads);
+    zi_tier *t = new (std::nothrow) zi_tier;
+    if (!t) return fail(ZI_ERR_ARG, "out of host memory");
+    t->S = staging;
+    t->threads = threads;
+    t->shared = true;
+    t->recording = true;
+    t->slots.assign(staging, zi_tier::Slot{});
+    *out = t;
+    return ZI_OK;
+}
+
+zi_status zi_tier_add(zi_tier *t, zi_file_source *s) {
+    clear_error();
+    if (!t || !s) return fail(ZI_ERR_ARG, "tier and source are required");
+    if (s->tier) return fail(ZI_ERR_STATE, "the source is already read by a tier (or has been used on its own)");
+    std::lock_guard<std::mutex> lock(t->mu);
+    if (t->started) return fail(ZI_ERR_STATE, "the tier is in use: add every source before the first pass");
+    t->srcs.push_back(s);
+    s->tier = t;
+    return ZI_OK;
+}
+
+zi_status zi_tier_step(zi_tier *t) {
+    clear_error();
+    if (!t) return fail(ZI_ERR_ARG, "tier is NULL");
+    {
+        std::lock_guard<std::mutex> lock(t->mu);
+        ++t->steps;
+        if (t->recording) {
+            t->trace = t->rec;
+            t->rec.clear();
+            t->recording = false;
+            t->pos = t->rpos = 0;
+        } else if (!t->trace.empty()) {
+            const int64_t L = (int64_t)t->trace.size();
+            if (t->pos % L == 0) return ZI_OK;  // in step with the trace
+            ++t->restarts;  // the step ended elsewhere: start the next one at the trace's start
+            t->pos = t->rpos = (t->pos + L - 1) / L * L;
+        }
+        ++t->gen;
+        t->discard_ready();
+        t->demand = false;
+        t->next_slot = t->cons_slot;
+    }
+    t->cv.notify_all();
+    return ZI_OK;
+}
+
+zi_status zi_tier_destroy(zi_tier *t) {
+    clear_error();
+    if (!t) return ZI_OK;
+    tier_stop(t);
+    for (zi_file_source *s : t->srcs) s->tier = nullptr;
+    delete t;
+    return ZI_OK;
+}
+
+zi_status zi_tier_stats_get(zi_tier *t, zi_tier_stats *out) {
+    clear_error();
+    if (!t || !out) return fail(ZI_ERR_ARG, "tier and out are required");
+    std::lock_guard<std::mutex> lock(t->mu);
+    out->trace_len = (int64_t)(t->recording ? t->rec.size() : t->trace.size());
+    out->steps = t->steps;
+    out->tiles_read = t->tiles_read;
+    out->restarts = t->restarts;
+    out->demand_reads = t->demand_reads;
+    out->read_s = t->read_s;
+    out->bytes = t->bytes;
+    out->wait_s = t->wait_s;
     return ZI_OK;
 }
 

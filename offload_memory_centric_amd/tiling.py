@@ -255,6 +255,37 @@ class FileSource:
             pass
 
 
+class Tier:
+    """File sources read by one reader along the order the first step used
+    them (zi_tier_*): add every source, run the steps, and call step() after
+    each step's passes are enqueued."""
+
+    def __init__(self, staging: int = 4, threads: int = 8):
+        self.handle = zi.zi_tier_create(staging, threads)
+        self.sources = []
+
+    def add(self, source: FileSource) -> None:
+        zi.zi_tier_add(self.handle, source.handle)
+        self.sources.append(source)
+
+    def step(self) -> None:
+        zi.zi_tier_step(self.handle)
+
+    def stats(self) -> dict:
+        return zi.zi_tier_stats_get(self.handle)
+
+    def close(self):
+        if self.handle:
+            zi.zi_tier_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def write_weight_file(path: str, W_host: torch.Tensor, chunk_bytes: int = 1 << 28) -> None:
     """Write a host weight's bytes to `path` (for a FileSource), in chunks."""
     flat = W_host.contiguous().view(torch.uint8).view(-1)

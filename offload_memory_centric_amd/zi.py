@@ -87,6 +87,15 @@ class zi_source_stats(ctypes.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+class zi_tier_stats(ctypes.Structure):
+    _fields_ = [("trace_len", ctypes.c_int64), ("steps", ctypes.c_int64), ("tiles_read", ctypes.c_int64),
+                ("restarts", ctypes.c_int64), ("demand_reads", ctypes.c_int64), ("read_s", ctypes.c_double),
+                ("bytes", ctypes.c_double), ("wait_s", ctypes.c_double)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
 class zi_stats(ctypes.Structure):
     _fields_ = [("kind_count", ctypes.c_int32), ("kind_name", (ctypes.c_char * 24) * 8),
                 ("launches", ctypes.c_int64 * 8), ("kernel_ms", ctypes.c_double * 8),
@@ -156,6 +165,11 @@ _sigs = {
     "zi_ctx_attach_source": (_S, [_P, _P, _P]),
     "zi_file_source_read": (_S, [_P, ctypes.c_int64, _P]),
     "zi_file_source_stats_get": (_S, [_P, ctypes.POINTER(zi_source_stats)]),
+    "zi_tier_create": (_S, [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_P)]),
+    "zi_tier_add": (_S, [_P, _P]),
+    "zi_tier_step": (_S, [_P]),
+    "zi_tier_destroy": (_S, [_P]),
+    "zi_tier_stats_get": (_S, [_P, ctypes.POINTER(zi_tier_stats)]),
     "zi_host_alloc": (_S, [ctypes.c_uint64, ctypes.POINTER(_P)]),
     "zi_host_free": (_S, [_P]),
     "zi_last_error": (ctypes.c_char_p, []),
@@ -371,6 +385,30 @@ def zi_file_source_read(src, tile: int, dst) -> None:
 def zi_file_source_stats_get(src) -> dict:
     s = zi_source_stats()
     _check(_lib.zi_file_source_stats_get(src, ctypes.byref(s)))
+    return s.as_dict()
+
+
+def zi_tier_create(staging: int = 4, threads: int = 8) -> int:
+    h = _P()
+    _check(_lib.zi_tier_create(int(staging), int(threads), ctypes.byref(h)))
+    return h.value
+
+
+def zi_tier_add(tier, src) -> None:
+    _check(_lib.zi_tier_add(tier, src))
+
+
+def zi_tier_step(tier) -> None:
+    _check(_lib.zi_tier_step(tier))
+
+
+def zi_tier_destroy(tier) -> None:
+    _check(_lib.zi_tier_destroy(tier))
+
+
+def zi_tier_stats_get(tier) -> dict:
+    s = zi_tier_stats()
+    _check(_lib.zi_tier_stats_get(tier, ctypes.byref(s)))
     return s.as_dict()
 
 

@@ -105,3 +105,36 @@ def test_errors(weight_file, tmp_path):
             zi.zi_file_source_destroy(src)
     finally:
         zi.zi_plan_destroy(h)
+
+
+def test_tier_bookkeeping_without_a_gpu(weight_file):
+    h, info = plan()
+    try:
+        p1, _ = weight_file(info.tile_bytes * 4, seed=5)
+        p2, _ = weight_file(info.tile_bytes * 4, seed=6)
+        with pytest.raises(zi.ZiError) as e:
+            zi.zi_tier_create(1, 4)
+        assert e.value.status == zi.ZI_ERR_ARG
+        tier = zi.zi_tier_create(3, 4)
+        s1 = zi.zi_file_source_create(h, p1, 0, 2, 2)
+        s2 = zi.zi_file_source_create(h, p2, 0, 2, 2)
+        zi.zi_tier_add(tier, s1)
+        zi.zi_tier_add(tier, s2)
+        with pytest.raises(zi.ZiError) as e:  # a source has one tier
+            zi.zi_tier_add(tier, s1)
+        assert e.value.status == zi.ZI_ERR_STATE
+        with pytest.raises(zi.ZiError) as e:  # the tier goes first
+            zi.zi_file_source_destroy(s1)
+        assert e.value.status == zi.ZI_ERR_STATE
+        st = zi.zi_tier_stats_get(tier)
+        assert st["trace_len"] == 0 and st["steps"] == 0 and st["tiles_read"] == 0
+        zi.zi_tier_step(tier)
+        assert zi.zi_tier_stats_get(tier)["steps"] == 1
+        # synchronous reads go straight to the file, tier or not
+        dst = aligned(info.tile_bytes)
+        zi.zi_file_source_read(s2, 2, dst)
+        zi.zi_tier_destroy(tier)
+        zi.zi_file_source_destroy(s1)
+        zi.zi_file_source_destroy(s2)
+    finally:
+        zi.zi_plan_destroy(h)

@@ -122,3 +122,85 @@ def test_source_and_optimizer_exclude_each_other(tmp_path):
     adam.close()
     src.close()
     plan.close()
+
+
+def run_block(tiling, ctx, p1, p2, b, forward_only=False, w2_first=False):
+    if w2_first:  # the down-projection's forward alone (an order the trace does not know)
+        ctx.fwd(p2, b["H"], b["Y"])
+        return
+    if forward_only:
+        ctx.fwd_gelu(p1, b["X"], b["A"], b["H"])
+        ctx.fwd(p2, b["H"], b["Y"])
+        return
+    tiling.ffn_block_step(ctx, p1, p2, b["X"], b["A"], b["H"], b["Y"], b["dY"], b["dH"], b["dA"], b["dX"], b["Yr"])
+
+
+def test_ffn_block_through_one_tier(tmp_path):
+    # both weights under one tier: the first step is recorded and read on
+    # demand, the next ones read ahead along the trace; steps in another order
+    # restart the read-ahead.  Every step gives the host-fed block's bits.
+    from test_gpu_ffn import ffn_setup
+    T, D, F, N1, N2, d = 96, 256, 1024, 4, 4, 2
+    say("case ffn through a tier")
+    tiling, ctx, p1, p2, b, h = ffn_setup(T, D, F, N1, N2, d, "f16", seed=41, w_std=0.05)
+    torch.cuda.synchronize()
+    run_block(tiling, ctx, p1, p2, b)
+    ctx.sync()
+    keys = ("A", "H", "Y", "dH", "dA", "dX")
+    ref = {k: b[k].clone() for k in keys}
+    ref_dw = (host_bits(h["dW1t"]).copy(), host_bits(h["dW2t"]).copy())
+    tier = tiling.Tier(staging=3, threads=2)
+    s1 = tiling.FileSource(p1, weight_file(tmp_path, "w1.bin", h["W1t"]))
+    s2 = tiling.FileSource(p2, weight_file(tmp_path, "w2.bin", h["W2t"]))
+    tier.add(s1)
+    tier.add(s2)
+    ctx.attach_source(p1, s1)
+    ctx.attach_source(p2, s2)
+    h["W1t"].zero_()
+    h["W2t"].zero_()
+
+    def check(what):
+        ctx.sync()
+        for k in keys:
+            assert torch.equal(b[k], ref[k]), (what, k)
+            b[k].zero_()
+        assert np.array_equal(host_bits(h["dW1t"]), ref_dw[0]), what
+        assert np.array_equal(host_bits(h["dW2t"]), ref_dw[1]), what
+
+    per_step = 3 * N1 + 2 * N2
+    run_block(tiling, ctx, p1, p2, b)        # recorded, read on demand
+    tier.step()
+    check("recorded step")
+    st = tier.stats()
+    say("  after the recorded step", st)
+    assert st["trace_len"] == per_step and st["demand_reads"] == per_step and st["restarts"] == 0
+    for n in range(2):                       # replayed
+        run_block(tiling, ctx, p1, p2, b)
+        tier.step()
+        check("replayed step %d" % n)
+    st = tier.stats()
+    say("  after two replayed steps", st)
+    assert st["demand_reads"] == per_step and st["restarts"] == 0
+    assert st["tiles_read"] >= 3 * per_step
+    # a forward-only step ends inside the trace: the next step starts over
+    run_block(tiling, ctx, p1, p2, b, forward_only=True)
+    tier.step()
+    ctx.sync()
+    assert torch.equal(b["Y"], ref["Y"])
+    run_block(tiling, ctx, p1, p2, b)
+    tier.step()
+    check("step after a forward-only one")
+    # a request out of the trace's order restarts the read-ahead where it is
+    run_block(tiling, ctx, p1, p2, b, w2_first=True)
+    run_block(tiling, ctx, p1, p2, b)
+    tier.step()
+    check("step after an unpredicted pass")
+    st = tier.stats()
+    say("  at the end", st)
+    assert st["restarts"] >= 2
+    ctx.attach_source(p1, None)
+    ctx.attach_source(p2, None)
+    ctx.close()
+    tier.close()
+    s1.close()
+    s2.close()
