@@ -181,11 +181,14 @@ struct zi_tier {
         if (device >= 0) (void)hipSetDevice(device);
         std::unique_lock<std::mutex> lock(mu);
         for (;;) {
-            const int k = next_slot;
+            // next_slot is read afresh on every wake-up: a request that restarts
+            // the read-ahead may move it while the reader waits
             cv.wait(lock, [&] {
-                return stop || ((slots[k].state == FREE || slots[k].state == IN_COPY) && (demand || read_ahead()));
+                const Slot &sl = slots[next_slot];
+                return stop || ((sl.state == FREE || sl.state == IN_COPY) && (demand || read_ahead()));
             });
             if (stop) return;
+            const int k = next_slot;
             if (slots[k].state == IN_COPY) {
                 // the staging buffer is free once the copy that reads it is done
                 hipEvent_t ev = slots[k].copied;
