@@ -138,6 +138,7 @@ struct zi_tier {
     struct Slot {
         Item item;
         int64_t tpos = -1;  // trace position of the item (-1: read on demand)
+        uint64_t gen = 0;   // the read-ahead generation the read belongs to
         State state = FREE;
         int err = 0;        // errno of a failed read
         hipEvent_t copied = nullptr;
@@ -210,6 +211,7 @@ struct zi_tier {
             const uint64_t g = gen;
             slots[k].item = it;
             slots[k].tpos = tp;
+            slots[k].gen = g;
             slots[k].state = READING;
             slots[k].err = 0;
             next_slot = (k + 1) % S;
@@ -351,7 +353,9 @@ zi_status source_acquire(zi_file_source *s, int64_t tile, const void **host, int
     std::unique_lock<std::mutex> lock(t->mu);
     const int k = t->cons_slot;
     if (t->recording && t->rec.size() < (1u << 20)) t->rec.push_back(want);
-    const bool held = zi_tier::holding(t->slots[k]) && t->slots[k].item == want;
+    // a read still running for an earlier generation will be discarded: it
+    // does not count, even if it is for the same tile
+    const bool held = zi_tier::holding(t->slots[k]) && t->slots[k].gen == t->gen && t->slots[k].item == want;
     const bool coming = !zi_tier::holding(t->slots[k]) && t->next_slot == k && !t->demand && t->read_ahead() &&
                         t->trace[(size_t)(t->rpos % (int64_t)t->trace.size())] == want;
     if (!held && !coming) {
@@ -377,7 +381,9 @@ zi_status source_acquire(zi_file_source *s, int64_t tile, const void **host, int
         }
         t->cv.notify_all();
     }
-    t->cv.wait(lock, [&] { return t->slots[k].state == zi_tier::READY && t->slots[k].item == want; });
+    t->cv.wait(lock, [&] {
+        return t->slots[k].state == zi_tier::READY && t->slots[k].gen == t->gen && t->slots[k].item == want;
+    });
     const double waited = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
     t->wait_s += waited;
     s->wait_s += waited;
