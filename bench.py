@@ -403,6 +403,8 @@ def main():
         result["adam"] = host_adam_leg(args, torch, tiling, ctx, plans, marked, spans, ms_step)
         adams = result["adam"].pop("_objs")
 
+    result["machine"] = machine_info(torch)
+
     # ---------------- CPU baseline (oracle, after the GPU timing) ----------------
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, np, torch, config, locals())
@@ -626,6 +628,33 @@ def host_adam_leg(args, torch, tiling, ctx, plans, marked, spans, ms_without):
                      "bytes_per_param": 28, "peak_kind": "measured a += b on the host"},
         "_objs": adams,
     }
+
+
+def machine_info(torch):
+    """The facts a reader needs to place the figures: device, runtime, host
+    cores and memory nodes, the copy-engine switch and the clocks the driver
+    reports (where rocm-smi is there to read them)."""
+    import glob
+    import subprocess
+    props = torch.cuda.get_device_properties(0)
+    info = {"device": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hbm_bytes": props.total_memory,
+            "hip_runtime": torch.version.hip, "HSA_ENABLE_SDMA": os.environ.get("HSA_ENABLE_SDMA"),
+            "host_cores": len(os.sched_getaffinity(0)),
+            "host_numa_nodes": len(glob.glob("/sys/devices/system/node/node[0-9]*"))}
+    try:
+        with open("/proc/cpuinfo") as f:
+            info["host_cpu"] = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        if r.returncode == 0:
+            card = next(iter(json.loads(r.stdout).values()))
+            info["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()}
+    except Exception:
+        pass
+    return info
 
 
 def _bits(torch, np, t):
