@@ -204,3 +204,32 @@ def test_ffn_block_through_one_tier(tmp_path):
     tier.close()
     s1.close()
     s2.close()
+
+
+def test_read_error_fails_the_pass_and_sticks(tmp_path):
+    # the file loses its second half after the source was made: the pass that
+    # needs tile 2 reports ZI_ERR_IO, the context keeps the error, and closing
+    # it waits for the work already enqueued
+    T, K, M, N = 128, 512, 2048, 4
+    tiling = lib()
+    from offload_memory_centric_amd import zi
+    say("case file read error")
+    X, Wt, dY = make_linear_inputs(T, K, M, "f16", "small_int", seed=9)
+    path = weight_file(tmp_path, "w.bin", Wt)
+    plan = tiling.Plan(T, K, M, N, 2, "f16", None, None)
+    ctx = tiling.Context(plan)
+    src = tiling.FileSource(plan, path, staging=2, threads=2)
+    os.truncate(path, 2 * plan.info.tile_bytes)
+    ctx.attach_source(plan, src)
+    Y = torch.empty((T, M), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+    with pytest.raises(zi.ZiError) as e:
+        ctx.fwd(plan, X, Y)
+    assert e.value.status == zi.ZI_ERR_IO
+    with pytest.raises(zi.ZiError) as e:
+        ctx.sync()
+    assert e.value.status == zi.ZI_ERR_IO
+    ctx.attach_source(plan, None)
+    ctx.close()
+    src.close()
+    plan.close()
