@@ -271,6 +271,19 @@ typedef struct {
     double compute_busy_ms;      /* sum of all kernel durations */
 } zi_stats;
 zi_status zi_ctx_set_timing(zi_ctx *ctx, int32_t enable);
+
+/* Debug aids for testing the ring's ordering and its stall accounting.
+ * ZI_DEBUG_POISON: every weight slot is filled with 0xFF bytes (a NaN in
+ * fp16, bf16 and fp32) on the copy stream just before a new tile is copied
+ * into it, and every gradient slot on the product stream just before a new
+ * dW is formed in it; a product that still read a released slot, or a
+ * write-back that still read a gradient slot, would then see NaNs.
+ * copy_delay_us: a host function on the copy stream sleeps that long before
+ * every tile copy (at most 10 s), which slows the host link as far as the
+ * ring can tell.  Both cost time; they are for tests.  ZI_ERR_ARG on unknown
+ * flags or a longer delay. */
+#define ZI_DEBUG_POISON 0x1u
+zi_status zi_ctx_set_debug(zi_ctx *ctx, uint32_t flags, uint32_t copy_delay_us);
 zi_status zi_ctx_reset_stats(zi_ctx *ctx);
 zi_status zi_ctx_stats(zi_ctx *ctx, zi_stats *out);
 

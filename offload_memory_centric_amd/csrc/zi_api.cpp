@@ -23,6 +23,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+#include <unistd.h>
 
 #include <algorithm>
 #include <mutex>
@@ -80,6 +81,8 @@ struct zi_ctx {
     zi_status sticky = ZI_OK;
     std::string sticky_msg;
     bool timing = false;
+    uint32_t debug = 0;     // ZI_DEBUG_* flags
+    uint32_t delay_us = 0;  // host-side delay before every tile copy
     std::vector<hipEvent_t> pool;
     size_t pool_used = 0;
     std::vector<KernelRec> krec;
@@ -123,6 +126,9 @@ zi_status hip_fail(zi_ctx *c, hipError_t e, const char *what) {
     } while (0)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Host function of the copy-delay debug aid: holds its stream for `arg` us.
+void sleep_us(void *arg) { usleep((useconds_t)(uintptr_t)arg); }
 
 bool pinned_range(const void *p, uint64_t bytes) {
     if (!p || !bytes) return false;
@@ -202,6 +208,9 @@ zi_status stage(zi_ctx *c, const zi_plan *p, int64_t g, int64_t tile) {
     if (zi_adam *a = c->adam_of(p)) adam_wait_tile(a, tile);
     const int s = (int)(g % c->d);
     if (c->w_free_rec[s]) HIPCHK(c, hipStreamWaitEvent(c->h2d, c->w_free[s], 0));
+    if (c->debug & ZI_DEBUG_POISON)  // a reader still using the slot would now see NaNs
+        HIPCHK(c, hipMemsetAsync(c->wslot(s), 0xFF, c->slot_bytes, c->h2d));
+    if (c->delay_us) HIPCHK(c, hipLaunchHostFunc(c->h2d, sleep_us, reinterpret_cast<void *>((uintptr_t)c->delay_us)));
     const uint64_t bytes = p->info.tile_bytes;
     const char *src = static_cast<const char *>(p->prob.W_host) + (uint64_t)tile * bytes;
     zi_file_source *fs = c->source_of(p);
@@ -404,6 +413,8 @@ zi_status run_bwd(zi_ctx *c, const zi_plan *p, const void *X, const void *dY, fl
             ready = c->dw_ready[s];
             done = c->w_free[s];
         }
+        if (c->debug & ZI_DEBUG_POISON)  // a write-back still reading the slot would copy NaNs
+            HIPCHK(c, hipMemsetAsync(dst, 0xFF, in.dw_tile_bytes, c->comp));
         {  // dW_i^t[m][k] = sum_t dY[t][i n + m] X[t][k]
             GemmArgs a{};
             a.Q = X;
@@ -705,6 +716,16 @@ zi_status zi_sync(zi_ctx *ctx) {
         if (st != ZI_OK) return st;
     }
     if (ctx->sticky != ZI_OK) return fail(ctx->sticky, "%s", ctx->sticky_msg.c_str());
+    return ZI_OK;
+}
+
+zi_status zi_ctx_set_debug(zi_ctx *ctx, uint32_t flags, uint32_t copy_delay_us) {
+    clear_error();
+    if (!ctx) return fail(ZI_ERR_ARG, "context is NULL");
+    if (flags & ~ZI_DEBUG_POISON) return fail(ZI_ERR_ARG, "unknown debug flags 0x%x", flags);
+    if (copy_delay_us > 10000000u) return fail(ZI_ERR_ARG, "copy delay above 10 s");
+    ctx->debug = flags;
+    ctx->delay_us = copy_delay_us;
     return ZI_OK;
 }
 

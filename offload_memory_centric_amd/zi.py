@@ -146,6 +146,7 @@ _sigs = {
     "zi_gelu_bwd": (_S, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_int64]),
     "zi_sync": (_S, [_P]),
     "zi_ctx_set_timing": (_S, [_P, ctypes.c_int32]),
+    "zi_ctx_set_debug": (_S, [_P, ctypes.c_uint32, ctypes.c_uint32]),
     "zi_ctx_reset_stats": (_S, [_P]),
     "zi_ctx_stats": (_S, [_P, ctypes.POINTER(zi_stats)]),
     "zi_stream_create": (_S, [ctypes.POINTER(_P)]),
@@ -316,6 +317,13 @@ def zi_stream_destroy(stream) -> None:
 
 def zi_sync(ctx) -> None:
     _check(_lib.zi_sync(ctx))
+
+
+ZI_DEBUG_POISON = 0x1
+
+
+def zi_ctx_set_debug(ctx, flags: int = 0, copy_delay_us: int = 0) -> None:
+    _check(_lib.zi_ctx_set_debug(ctx, int(flags), int(copy_delay_us)))
 
 
 def zi_ctx_set_timing(ctx, enable: bool) -> None:
