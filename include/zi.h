@@ -268,9 +268,22 @@ typedef struct {
     double h2d_ms, d2h_ms;       /* sums of event-measured copy durations */
     double h2d_bytes, d2h_bytes;
     double span_ms;              /* first timed event -> last timed event */
-    double compute_busy_ms;      /* sum of all kernel durations */
+    double compute_busy_ms;      /* time some kernel ran: the union of their intervals */
 } zi_stats;
 zi_status zi_ctx_set_timing(zi_ctx *ctx, int32_t enable);
+
+/* A second product stream (caller-owned, default priority, distinct from the
+ * context's three; NULL: none).  A forward pass then launches the products of
+ * its odd tiles on it and of its even tiles on the first: the tiles' outputs
+ * are disjoint, and the next tile's workgroups fill the compute units that the
+ * last, partial wave of the previous tile's leaves idle.  Backward passes keep
+ * all their products on the first stream.  The second stream waits for
+ * everything enqueued before
+ * the pass, and the first stream waits for the second at the pass's end, so
+ * the context's ordering toward later calls is unchanged.  With timing on,
+ * kernel durations of overlapping products include the time they share the
+ * device; compute_busy_ms counts the union of the kernels' intervals. */
+zi_status zi_ctx_set_second_stream(zi_ctx *ctx, void *stream);
 
 /* Debug aids for testing the ring's ordering and its stall accounting.
  * ZI_DEBUG_POISON: every weight slot is filled with 0xFF bytes (a NaN in

@@ -71,6 +71,10 @@ using namespace zi;
 struct zi_ctx {
     int device = 0;
     hipStream_t comp = nullptr, h2d = nullptr, d2h = nullptr;
+    // optional second product stream: a forward pass alternates its tiles'
+    // products between comp and comp2 (forked from and joined back into comp)
+    hipStream_t comp2 = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
     char *ws = nullptr;
     uint64_t ws_bytes = 0;
     int d = 1, dw_slots = 0;
@@ -277,19 +281,21 @@ zi_status write_back(zi_ctx *c, const zi_plan *p, int64_t tile, const void *src,
     return ZI_OK;
 }
 
-zi_status gemm(zi_ctx *c, int kind, GemmOp op, int dtype, const GemmArgs &a, double flops) {
+zi_status gemm(zi_ctx *c, int kind, GemmOp op, int dtype, const GemmArgs &a, double flops,
+               hipStream_t stream = nullptr) {
+    if (!stream) stream = c->comp;
     hipEvent_t ea = nullptr, eb = nullptr;
     if (c->timing) {
         zi_status st = ev_timed(c, &ea);
         if (st != ZI_OK) return st;
-        HIPCHK(c, hipEventRecord(ea, c->comp));
+        HIPCHK(c, hipEventRecord(ea, stream));
     }
-    hipError_t e = launch_gemm(op, dtype, a, c->comp);
+    hipError_t e = launch_gemm(op, dtype, a, stream);
     if (e != hipSuccess) return hip_fail(c, e, kKindNames[kind]);
     if (c->timing) {
         zi_status st = ev_timed(c, &eb);
         if (st != ZI_OK) return st;
-        HIPCHK(c, hipEventRecord(eb, c->comp));
+        HIPCHK(c, hipEventRecord(eb, stream));
         c->krec.push_back(KernelRec{kind, flops, ea, eb});
     }
     return ZI_OK;
@@ -304,11 +310,21 @@ zi_status run_fwd(zi_ctx *c, const zi_plan *p, const void *X, void *Y, void *H) 
     const int64_t base = c->seq;
     const double tile_flops = 2.0 * (double)pr.T * (double)pr.K * (double)n;
     zi_status st;
+    // The tiles' products are independent (disjoint output columns), so with a
+    // second product stream they alternate between the two: the next tile's
+    // workgroups take the compute units that the last wave of the previous
+    // tile's leaves idle.  comp2 first waits for everything before this pass
+    // on comp, and comp waits for comp2 at its end.
+    if (c->comp2) {
+        HIPCHK(c, hipEventRecord(c->fork, c->comp));
+        HIPCHK(c, hipStreamWaitEvent(c->comp2, c->fork, 0));
+    }
     for (int64_t j = 0; j < std::min<int64_t>(d, N); ++j)
         if ((st = stage(c, p, base + j, j)) != ZI_OK) return st;
     for (int64_t i = 0; i < N; ++i) {
         const int s = (int)((base + i) % d);
-        HIPCHK(c, hipStreamWaitEvent(c->comp, c->w_ready[s], 0));
+        hipStream_t ks = (c->comp2 && (i & 1)) ? c->comp2 : c->comp;
+        HIPCHK(c, hipStreamWaitEvent(ks, c->w_ready[s], 0));
         GemmArgs a{};
         a.Q = c->wslot(s);
         a.ldq = pr.K;
@@ -321,11 +337,15 @@ zi_status run_fwd(zi_ctx *c, const zi_plan *p, const void *X, void *Y, void *H) 
         a.cols = n;
         a.red = pr.K;
         a.out_f32 = f32 ? 1 : 0;
-        st = gemm(c, H ? K_FWD_GELU : K_FWD, H ? GemmOp::FwdGelu : GemmOp::Fwd, pr.dtype, a, tile_flops);
+        st = gemm(c, H ? K_FWD_GELU : K_FWD, H ? GemmOp::FwdGelu : GemmOp::Fwd, pr.dtype, a, tile_flops, ks);
         if (st != ZI_OK) return st;
-        HIPCHK(c, hipEventRecord(c->w_free[s], c->comp));
+        HIPCHK(c, hipEventRecord(c->w_free[s], ks));
         c->w_free_rec[s] = 1;
         if (i + d < N && (st = stage(c, p, base + i + d, i + d)) != ZI_OK) return st;
+    }
+    if (c->comp2) {
+        HIPCHK(c, hipEventRecord(c->join, c->comp2));
+        HIPCHK(c, hipStreamWaitEvent(c->comp, c->join, 0));
     }
     c->seq += N;
     return ZI_OK;
@@ -347,6 +367,9 @@ zi_status run_bwd(zi_ctx *c, const zi_plan *p, const void *X, const void *dY, fl
     static_assert(kPairStep == kGemmStep, "pairs split the reduction at a GEMM step");
     const bool pairs = pairs_apply((int)N, d, c->dw_slots, n);
     zi_status st;
+    // The products of a backward pass stay on one stream: running the
+    // recomputed forward beside the previous tile's dW on the second stream
+    // was measured slower (452 -> 478 ms for the block's down-projection).
     int64_t staged = std::min<int64_t>(d, N);
     for (int64_t j = 0; j < staged; ++j)
         if ((st = stage(c, p, base + j, j)) != ZI_OK) return st;
@@ -587,6 +610,7 @@ zi_status zi_ctx_destroy(zi_ctx *c) {
     clear_error();
     if (!c) return ZI_OK;
     if (c->comp || c->h2d || c->d2h) {
+        if (c->comp2) (void)hipStreamSynchronize(c->comp2);
         (void)hipStreamSynchronize(c->comp);
         (void)hipStreamSynchronize(c->h2d);
         (void)hipStreamSynchronize(c->d2h);
@@ -594,6 +618,8 @@ zi_status zi_ctx_destroy(zi_ctx *c) {
     for (auto *v : {&c->w_ready, &c->w_free, &c->dw_ready, &c->dw_free, &c->pool})
         for (hipEvent_t e : *v)
             if (e) (void)hipEventDestroy(e);
+    if (c->fork) (void)hipEventDestroy(c->fork);
+    if (c->join) (void)hipEventDestroy(c->join);
     delete c;
     return ZI_OK;
 }
@@ -705,6 +731,10 @@ zi_status zi_gelu_bwd(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const voi
 zi_status zi_sync(zi_ctx *ctx) {
     clear_error();
     if (!ctx) return fail(ZI_ERR_ARG, "context is NULL");
+    if (ctx->comp2) {
+        const hipError_t e0 = hipStreamSynchronize(ctx->comp2);
+        if (e0 != hipSuccess) return hip_fail(ctx, e0, "hipStreamSynchronize(second compute)");
+    }
     hipError_t e1 = hipStreamSynchronize(ctx->comp);
     hipError_t e2 = hipStreamSynchronize(ctx->h2d);
     hipError_t e3 = hipStreamSynchronize(ctx->d2h);
@@ -716,6 +746,23 @@ zi_status zi_sync(zi_ctx *ctx) {
         if (st != ZI_OK) return st;
     }
     if (ctx->sticky != ZI_OK) return fail(ctx->sticky, "%s", ctx->sticky_msg.c_str());
+    return ZI_OK;
+}
+
+zi_status zi_ctx_set_second_stream(zi_ctx *ctx, void *stream) {
+    clear_error();
+    zi_status st = check_ctx(ctx);
+    if (st != ZI_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (s && (s == ctx->comp || s == ctx->h2d || s == ctx->d2h))
+        return fail(ZI_ERR_ARG, "the second product stream must be a stream of its own");
+    if (s && !ctx->fork) {
+        HIPCHK(ctx, hipEventCreateWithFlags(&ctx->fork, hipEventDisableTiming));
+        HIPCHK(ctx, hipEventCreateWithFlags(&ctx->join, hipEventDisableTiming));
+    }
+    // work already on the old second stream must be done before it is let go
+    if (ctx->comp2) HIPCHK(ctx, hipStreamSynchronize(ctx->comp2));
+    ctx->comp2 = s;
     return ZI_OK;
 }
 
@@ -766,15 +813,31 @@ zi_status zi_ctx_stats(zi_ctx *ctx, zi_stats *out) {
         any = true;
         return ZI_OK;
     };
+    std::vector<std::pair<double, double>> busy;  // kernel intervals, ms after the first event
     for (const KernelRec &r : ctx->krec) {
-        float ms = 0;
+        float ms = 0, t0 = 0;
         HIPCHK(ctx, hipEventElapsedTime(&ms, r.a, r.b));
+        HIPCHK(ctx, hipEventElapsedTime(&t0, ref, r.a));
         out->launches[r.kind] += 1;
         out->kernel_ms[r.kind] += ms;
         out->flops[r.kind] += r.flops;
-        out->compute_busy_ms += ms;
+        busy.emplace_back(t0, (double)t0 + ms);
         if ((st = span(r.a, r.b)) != ZI_OK) return st;
     }
+    // time the compute units had work: the union of the kernel intervals
+    // (kernels on the two product streams may overlap)
+    std::sort(busy.begin(), busy.end());
+    double cur_lo = 0, cur_hi = -1;
+    for (const auto &b : busy) {
+        if (b.first > cur_hi) {
+            if (cur_hi > cur_lo) out->compute_busy_ms += cur_hi - cur_lo;
+            cur_lo = b.first;
+            cur_hi = b.second;
+        } else if (b.second > cur_hi) {
+            cur_hi = b.second;
+        }
+    }
+    if (cur_hi > cur_lo) out->compute_busy_ms += cur_hi - cur_lo;
     for (const CopyRec &r : ctx->crec) {
         float ms = 0;
         HIPCHK(ctx, hipEventElapsedTime(&ms, r.a, r.b));

@@ -147,6 +147,7 @@ _sigs = {
     "zi_sync": (_S, [_P]),
     "zi_ctx_set_timing": (_S, [_P, ctypes.c_int32]),
     "zi_ctx_set_debug": (_S, [_P, ctypes.c_uint32, ctypes.c_uint32]),
+    "zi_ctx_set_second_stream": (_S, [_P, _P]),
     "zi_ctx_reset_stats": (_S, [_P]),
     "zi_ctx_stats": (_S, [_P, ctypes.POINTER(zi_stats)]),
     "zi_stream_create": (_S, [ctypes.POINTER(_P)]),
@@ -317,6 +318,10 @@ def zi_stream_destroy(stream) -> None:
 
 def zi_sync(ctx) -> None:
     _check(_lib.zi_sync(ctx))
+
+
+def zi_ctx_set_second_stream(ctx, stream) -> None:
+    _check(_lib.zi_ctx_set_second_stream(ctx, _stream(stream)))
 
 
 ZI_DEBUG_POISON = 0x1
