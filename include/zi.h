@@ -452,7 +452,13 @@ zi_status zi_file_source_stats_get(zi_file_source *src, zi_source_stats *out);
  * ahead along that trace, across weights and across the end of a step into
  * the next.  A request the trace does not predict restarts the read-ahead at
  * its next place in the trace, or is read on demand.  A standalone source
- * reads ahead with a tier of its own whose trace is its tiles in order. */
+ * reads ahead with a tier of its own whose trace is its tiles in order.
+ * The buffers also cache the files in host memory: a tile a buffer still
+ * holds is served without a read.  A read takes a buffer no pending request
+ * waits for, preferring an empty one, else the one whose tile the trace needs
+ * again latest (the eviction that keeps the fewest reads when the order of
+ * future requests is known; Belady, 1966).  With as many buffers as a source
+ * has tiles, its weight is read once and then served from host memory. */
 typedef struct zi_tier zi_tier;
 zi_status zi_tier_create(int32_t staging, int32_t threads, zi_tier **out);
 /* Put `src` under the tier; before the source or the tier is first used.
@@ -472,6 +478,7 @@ typedef struct {
     int64_t tiles_read;
     int64_t restarts;      /* read-ahead restarted at another trace position */
     int64_t demand_reads;  /* requests read on demand (all of the first step's) */
+    int64_t hits;          /* requests served by a buffer that still held the tile */
     double read_s, bytes, wait_s;
 } zi_tier_stats;
 zi_status zi_tier_stats_get(zi_tier *tier, zi_tier_stats *out);

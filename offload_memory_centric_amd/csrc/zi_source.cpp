@@ -28,6 +28,7 @@
 #include <algorithm>
 #include <chrono>
 #include <condition_variable>
+#include <deque>
 #include <mutex>
 #include <new>
 #include <string>
@@ -123,120 +124,173 @@ struct zi_file_source {
     double read_s = 0, bytes = 0, wait_s = 0;
 };
 
-// A tier of file sources: S pinned staging buffers and one reader thread that
+// A tier of file sources: S pinned tile buffers and one reader thread that
 // reads the sources' tiles ahead of the passes, in the order of a trace.  A
 // shared tier records the order of the requests during the first step (the
 // requests are then served on demand) and replays it in every later step; a
 // standalone source gets a private tier whose trace is its tiles in order.
+//
+// The buffers are also a cache of the file in host memory: a tile still held
+// by a buffer is served again without a read.  When the reader needs a buffer
+// for a read, it takes one that no pending request is waiting for, preferring
+// one that holds nothing, else the one whose tile the trace needs again
+// latest (with the order of future requests known, that choice keeps the
+// fewest reads of any eviction order, as Belady showed for page replacement).
 struct zi_tier {
-    enum State { FREE, READING, READY, IN_COPY };
+    enum State { FREE, READING, READY };
     struct Item {
         zi_file_source *src = nullptr;
         int64_t tile = -1;
         bool operator==(const Item &o) const { return src == o.src && tile == o.tile; }
     };
-    struct Slot {
-        Item item;
-        int64_t tpos = -1;  // trace position of the item (-1: read on demand)
-        uint64_t gen = 0;   // the read-ahead generation the read belongs to
-        State state = FREE;
-        int err = 0;        // errno of a failed read
+    struct Buf {
+        Item item;            // the tile the buffer holds or is reading
+        State state = FREE;   // FREE: holds nothing valid
+        int err = 0;          // errno of a failed read
+        bool held = false;    // handed to a request whose copy is not enqueued yet
+        uint64_t copies = 0;  // copies out of it enqueued ('copied' recorded after each)
+        uint64_t synced = 0;  // copies known to be done
         hipEvent_t copied = nullptr;
     };
 
     int S = 2, threads = 4;
     bool shared = false;
     std::vector<zi_file_source *> srcs;
-    std::vector<char *> buf;     // pinned staging buffers, made on first use
+    std::vector<char *> buf;     // pinned tile buffers, made on first use
     std::vector<char *> bounce;  // per-thread buffers for direct reads
-    std::vector<Slot> slots;
+    std::vector<Buf> bufs;
     std::vector<Item> trace, rec;
-    bool recording = false;  // a shared tier records until its first step mark
-    int64_t pos = 0;         // trace position the next request is expected at
-    int64_t rpos = 0;        // trace position the reader reads next
-    bool demand = false;     // one read the reader does before the trace's next
+    bool recording = false;      // a shared tier records until its first step mark
+    int64_t pos = 0;             // trace position the next request is expected at
+    int64_t rpos = 0;            // first trace position without a buffer yet
+    std::deque<int> assigned;    // buffer of each trace position in [pos, rpos)
+    bool demand = false;         // a request off the trace, read before the trace's next
     Item demand_item;
-    int next_slot = 0, cons_slot = 0;
-    uint64_t gen = 0;  // bumped when the read-ahead restarts
     int device = -1;
     bool started = false, stop = false;
     std::mutex mu;
     std::condition_variable cv;
     std::thread reader;
-    int64_t tiles_read = 0, restarts = 0, demand_reads = 0, steps = 0;
+    int64_t tiles_read = 0, hits = 0, restarts = 0, demand_reads = 0, steps = 0;
     double read_s = 0, bytes = 0, wait_s = 0;
 
     bool read_ahead() const { return !recording && !trace.empty(); }
-    static bool holding(const Slot &s) { return s.state == READING || s.state == READY; }
+    const Item &at(int64_t q) const { return trace[(size_t)(q % (int64_t)trace.size())]; }
 
-    void discard_ready() {
-        for (auto &sl : slots)
-            if (sl.state == READY) {
-                sl.state = FREE;
-                sl.item = Item{};
-                sl.tpos = -1;
+    int holding(const Item &it) const {  // buffer holding or reading `it`, or -1
+        for (int b = 0; b < S; ++b)
+            if (bufs[b].state != FREE && bufs[b].item == it) return b;
+        return -1;
+    }
+
+    bool pending(int b) const {
+        for (int x : assigned)
+            if (x == b) return true;
+        return false;
+    }
+
+    // Trace distance from rpos to the next request for `it` (L + 1: none).
+    int64_t next_use(const Item &it) const {
+        const int64_t L = (int64_t)trace.size();
+        if (!read_ahead()) return L + 1;
+        for (int64_t j = 0; j < L; ++j)
+            if (at(rpos + j) == it) return j;
+        return L + 1;
+    }
+
+    // A buffer the reader may overwrite, or -1.
+    int victim() const {
+        int best = -1;
+        int64_t far = -1;
+        for (int b = 0; b < S; ++b) {
+            const Buf &x = bufs[b];
+            if (x.state == READING || x.held || pending(b)) continue;
+            if (x.state == FREE) return b;
+            const int64_t d = next_use(x.item);
+            if (d > far) {
+                far = d;
+                best = b;
             }
+        }
+        return best;
     }
 
     void run() {
         if (device >= 0) (void)hipSetDevice(device);
         std::unique_lock<std::mutex> lock(mu);
         for (;;) {
-            // next_slot is read afresh on every wake-up: a request that restarts
-            // the read-ahead may move it while the reader waits
-            cv.wait(lock, [&] {
-                const Slot &sl = slots[next_slot];
-                return stop || ((sl.state == FREE || sl.state == IN_COPY) && (demand || read_ahead()));
-            });
             if (stop) return;
-            const int k = next_slot;
-            if (slots[k].state == IN_COPY) {
-                // the staging buffer is free once the copy that reads it is done
-                hipEvent_t ev = slots[k].copied;
+            // what to read next: an off-trace request first, then the trace
+            Item want;
+            bool have = false, for_trace = false;
+            if (demand) {
+                if (holding(demand_item) >= 0) {
+                    demand = false;  // served from a buffer meanwhile
+                } else {
+                    want = demand_item;
+                    have = true;
+                }
+            }
+            if (!have && read_ahead() && rpos - pos < S) {
+                const Item &it = at(rpos);
+                const int b = holding(it);
+                if (b >= 0) {  // already held: no read
+                    assigned.push_back(b);
+                    ++rpos;
+                    ++hits;
+                    cv.notify_all();
+                    continue;
+                }
+                want = it;
+                have = true;
+                for_trace = true;
+            }
+            if (!have) {
+                cv.wait(lock);
+                continue;
+            }
+            const int k = victim();
+            if (k < 0) {
+                cv.wait(lock);
+                continue;
+            }
+            if (bufs[k].synced < bufs[k].copies) {
+                // the buffer is free once the copies that read it are done (the
+                // event was recorded after the last one before its count rose)
+                const uint64_t upto = bufs[k].copies;
+                hipEvent_t ev = bufs[k].copied;
                 lock.unlock();
                 (void)hipEventSynchronize(ev);
                 lock.lock();
-                if (slots[k].state == IN_COPY) slots[k].state = FREE;
-                continue;
+                bufs[k].synced = std::max(bufs[k].synced, upto);
+                continue;  // the plan may have changed meanwhile
             }
-            Item it;
-            int64_t tp = -1;
-            if (demand) {
-                it = demand_item;
-                demand = false;
+            bufs[k].item = want;
+            bufs[k].state = READING;
+            bufs[k].err = 0;
+            if (for_trace) {
+                assigned.push_back(k);
+                ++rpos;
             } else {
-                tp = rpos++;
-                it = trace[(size_t)(tp % (int64_t)trace.size())];
+                demand = false;
+                ++demand_reads;
             }
-            const uint64_t g = gen;
-            slots[k].item = it;
-            slots[k].tpos = tp;
-            slots[k].gen = g;
-            slots[k].state = READING;
-            slots[k].err = 0;
-            next_slot = (k + 1) % S;
             lock.unlock();
             const auto t0 = std::chrono::steady_clock::now();
-            zi_file_source *src = it.src;
-            const int err = parallel_pread(src->fd, buf[k], src->offset + (uint64_t)it.tile * src->tile_bytes,
+            zi_file_source *src = want.src;
+            const int err = parallel_pread(src->fd, buf[k], src->offset + (uint64_t)want.tile * src->tile_bytes,
                                            src->tile_bytes, threads, src->direct ? bounce.data() : nullptr);
             const double secs = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
             lock.lock();
-            if (gen != g) {
-                slots[k].state = FREE;  // the read-ahead restarted meanwhile: discard
-                slots[k].item = Item{};
-                slots[k].tpos = -1;
-            } else {
-                slots[k].state = READY;
-                slots[k].err = err;
-                if (!err) {
-                    ++tiles_read;
-                    read_s += secs;
-                    bytes += (double)src->tile_bytes;
-                    ++src->tiles_read;
-                    src->read_s += secs;
-                    src->bytes += (double)src->tile_bytes;
-                }
+            bufs[k].state = READY;
+            bufs[k].err = err;
+            if (!err) {
+                ++tiles_read;
+                read_s += secs;
+                bytes += (double)src->tile_bytes;
+                ++src->tiles_read;
+                src->read_s += secs;
+                src->bytes += (double)src->tile_bytes;
             }
             cv.notify_all();
         }
@@ -296,11 +350,11 @@ static zi_status tier_start(zi_tier *t) {
     t->device = dev;
     t->buf = bufs;
     t->bounce = bb;
-    for (int k = 0; k < t->S; ++k) t->slots[k].copied = evs[k];
+    for (int k = 0; k < t->S; ++k) t->bufs[k].copied = evs[k];
     try {
         t->reader = std::thread([t] { t->run(); });
     } catch (...) {
-        for (auto &sl : t->slots) sl.copied = nullptr;
+        for (auto &sl : t->bufs) sl.copied = nullptr;
         t->buf.clear();
         t->bounce.clear();
         undo();
@@ -319,7 +373,7 @@ static void tier_stop(zi_tier *t) {
     }
     t->cv.notify_all();
     t->reader.join();
-    for (auto &sl : t->slots)
+    for (auto &sl : t->bufs)
         if (sl.copied) {
             (void)hipEventSynchronize(sl.copied);
             (void)hipEventDestroy(sl.copied);
@@ -340,7 +394,7 @@ zi_status source_acquire(zi_file_source *s, int64_t tile, const void **host, int
         t->S = s->S;
         t->threads = s->threads;
         t->srcs.push_back(s);
-        t->slots.assign(t->S, zi_tier::Slot{});
+        t->bufs.assign(t->S, zi_tier::Buf{});
         for (int64_t i = 0; i < s->N; ++i) t->trace.push_back(zi_tier::Item{s, i});
         s->tier = t;
         s->own_tier = true;
@@ -351,80 +405,81 @@ zi_status source_acquire(zi_file_source *s, int64_t tile, const void **host, int
     const auto t0 = std::chrono::steady_clock::now();
     const zi_tier::Item want{s, tile};
     std::unique_lock<std::mutex> lock(t->mu);
-    const int k = t->cons_slot;
     if (t->recording && t->rec.size() < (1u << 20)) t->rec.push_back(want);
-    // a read still running for an earlier generation will be discarded: it
-    // does not count, even if it is for the same tile
-    const bool held = zi_tier::holding(t->slots[k]) && t->slots[k].gen == t->gen && t->slots[k].item == want;
-    const bool coming = !zi_tier::holding(t->slots[k]) && t->next_slot == k && !t->demand && t->read_ahead() &&
-                        t->trace[(size_t)(t->rpos % (int64_t)t->trace.size())] == want;
-    if (!held && !coming) {
-        // serve this request next, from the slot it takes: restart the read-ahead
-        // at its next place in the trace, or read it on demand
-        ++t->gen;
-        t->discard_ready();
-        t->next_slot = k;
-        int64_t q = -1;
-        if (t->read_ahead()) {
-            const int64_t L = (int64_t)t->trace.size();
-            for (int64_t j = 0; j < L && q < 0; ++j)
-                if (t->trace[(size_t)((t->pos + j) % L)] == want) q = t->pos + j;
-        }
-        if (q >= 0) {
-            ++t->restarts;
-            t->rpos = q;
-            t->demand = false;
-        } else {
-            ++t->demand_reads;
-            t->demand = true;
-            t->demand_item = want;
-        }
+    bool on_trace = t->read_ahead() && t->at(t->pos) == want;
+    if (!on_trace && t->read_ahead()) {
+        // restart the read-ahead at the request's next place in the trace
+        const int64_t L = (int64_t)t->trace.size();
+        for (int64_t j = 1; j < L && !on_trace; ++j)
+            if (t->at(t->pos + j) == want) {
+                ++t->restarts;
+                t->assigned.clear();
+                t->pos = t->rpos = t->pos + j;
+                on_trace = true;
+            }
         t->cv.notify_all();
     }
-    t->cv.wait(lock, [&] {
-        return t->slots[k].state == zi_tier::READY && t->slots[k].gen == t->gen && t->slots[k].item == want;
-    });
+    int b;
+    if (on_trace) {
+        t->cv.wait(lock, [&] { return !t->assigned.empty() && t->bufs[t->assigned.front()].state == zi_tier::READY; });
+        b = t->assigned.front();
+        t->assigned.pop_front();
+        ++t->pos;
+    } else {
+        // off the trace (or while recording): a buffer that holds it, else a read on demand
+        b = t->holding(want);
+        if (b >= 0 && t->bufs[b].state == zi_tier::READY) {
+            ++t->hits;
+        } else if (b < 0) {
+            t->demand = true;
+            t->demand_item = want;
+            t->cv.notify_all();
+        }
+        t->cv.wait(lock, [&] {
+            const int h = t->holding(want);
+            return h >= 0 && t->bufs[h].state == zi_tier::READY;
+        });
+        b = t->holding(want);
+    }
+    t->cv.notify_all();  // the reader may run further ahead now
     const double waited = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
     t->wait_s += waited;
     s->wait_s += waited;
-    if (t->slots[k].tpos >= 0) t->pos = t->slots[k].tpos + 1;
-    if (t->slots[k].err) {
-        const int err = t->slots[k].err;
-        t->slots[k].state = zi_tier::FREE;
-        t->slots[k].item = zi_tier::Item{};
+    if (t->bufs[b].err) {
+        const int err = t->bufs[b].err;
+        t->bufs[b].state = zi_tier::FREE;
+        t->bufs[b].item = zi_tier::Item{};
+        // later positions may have been given the same buffer: plan them again
+        t->assigned.clear();
+        t->rpos = t->pos;
         t->cv.notify_all();
         return fail(ZI_ERR_IO, "reading tile %lld: %s", (long long)tile, strerror(err));
     }
-    *host = t->buf[k];
-    *slot = k;
+    t->bufs[b].held = true;
+    *host = t->buf[b];
+    *slot = b;
     return ZI_OK;
 }
 
-hipEvent_t source_copy_event(zi_file_source *s, int slot) { return s->tier->slots[slot].copied; }
+hipEvent_t source_copy_event(zi_file_source *s, int slot) { return s->tier->bufs[slot].copied; }
 
 void source_release(zi_file_source *s, int slot) {
     zi_tier *t = s->tier;
     {
         std::lock_guard<std::mutex> lock(t->mu);
-        t->slots[slot].state = zi_tier::IN_COPY;
-        t->cons_slot = (slot + 1) % t->S;
+        t->bufs[slot].held = false;
+        ++t->bufs[slot].copies;
     }
     t->cv.notify_all();
 }
 
 // A request that fails after source_acquire (the copy could not be enqueued)
-// gives the buffer back unread by any copy; the next request restarts the
-// read-ahead from this slot.
+// gives the buffer back; its tile stays cached.
 void source_abandon(zi_file_source *s, int slot) {
     zi_tier *t = s->tier;
     {
         std::lock_guard<std::mutex> lock(t->mu);
-        t->slots[slot].state = zi_tier::FREE;
-        t->slots[slot].item = zi_tier::Item{};
-        ++t->gen;
-        t->discard_ready();
-        t->next_slot = slot;
-        t->cons_slot = slot;
+        t->bufs[slot].held = false;
     }
     t->cv.notify_all();
 }
@@ -538,7 +593,7 @@ zi_status zi_tier_create(int32_t staging, int32_t threads, zi_tier **out) {
     t->threads = threads;
     t->shared = true;
     t->recording = true;
-    t->slots.assign(staging, zi_tier::Slot{});
+    t->bufs.assign(staging, zi_tier::Buf{});
     *out = t;
     return ZI_OK;
 }
@@ -565,16 +620,14 @@ zi_status zi_tier_step(zi_tier *t) {
             t->rec.clear();
             t->recording = false;
             t->pos = t->rpos = 0;
+            t->assigned.clear();
         } else if (!t->trace.empty()) {
             const int64_t L = (int64_t)t->trace.size();
             if (t->pos % L == 0) return ZI_OK;  // in step with the trace
             ++t->restarts;  // the step ended elsewhere: start the next one at the trace's start
             t->pos = t->rpos = (t->pos + L - 1) / L * L;
+            t->assigned.clear();
         }
-        ++t->gen;
-        t->discard_ready();
-        t->demand = false;
-        t->next_slot = t->cons_slot;
     }
     t->cv.notify_all();
     return ZI_OK;
@@ -598,6 +651,7 @@ zi_status zi_tier_stats_get(zi_tier *t, zi_tier_stats *out) {
     out->tiles_read = t->tiles_read;
     out->restarts = t->restarts;
     out->demand_reads = t->demand_reads;
+    out->hits = t->hits;
     out->read_s = t->read_s;
     out->bytes = t->bytes;
     out->wait_s = t->wait_s;

@@ -89,7 +89,8 @@ class zi_source_stats(ctypes.Structure):
 
 class zi_tier_stats(ctypes.Structure):
     _fields_ = [("trace_len", ctypes.c_int64), ("steps", ctypes.c_int64), ("tiles_read", ctypes.c_int64),
-                ("restarts", ctypes.c_int64), ("demand_reads", ctypes.c_int64), ("read_s", ctypes.c_double),
+                ("restarts", ctypes.c_int64), ("demand_reads", ctypes.c_int64), ("hits", ctypes.c_int64),
+                ("read_s", ctypes.c_double),
                 ("bytes", ctypes.c_double), ("wait_s", ctypes.c_double)]
 
     def as_dict(self) -> dict:

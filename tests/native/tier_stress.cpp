@@ -1,9 +1,10 @@
-// Stress test of the file tier's read-ahead, on the CPU: zi_source.cpp is
-// compiled with host stand-ins for the HIP calls it makes (aligned malloc for
-// page-locked memory, events that are always complete).  A consumer stages
-// tiles as the passes do, in order and out of order, restarting the
-// read-ahead and abandoning requests at random, and checks every staged
-// buffer against the file's bytes.  Usage: tier_stress DIR
+// Stress test of the file tier's read-ahead and cache, on the CPU:
+// zi_source.cpp is compiled with host stand-ins for the HIP calls it makes
+// (aligned malloc for page-locked memory, events that are always complete).
+// A consumer stages tiles as the passes do, in order and out of order,
+// restarting the read-ahead and abandoning requests at random, and checks
+// every staged buffer against the file's bytes; with as many buffers as
+// tiles, every tile must be read exactly once.  Usage: tier_stress DIR
 #include "../../offload_memory_centric_amd/csrc/zi_source.cpp"
 #include <random>
 #include <stdarg.h>
@@ -61,6 +62,17 @@ int main(int argc, char **argv) {
             for (int t = 0; t < N; ++t) serve(s, 0, t, true);
         zi_source_stats st; zi_file_source_stats_get(s, &st);
         printf("standalone: restarts %lld tiles_read %lld\n", (long long)st.restarts, (long long)st.tiles_read);
+        zi_file_source_destroy(s);
+    }
+    // 1b. as many buffers as tiles: every tile is read once, then served from memory
+    {
+        zi_file_source *s = nullptr;
+        zi_file_source_create(&plan, paths[1], 0, N, 2, &s);
+        for (int pass = 0; pass < 30; ++pass)
+            for (int t = 0; t < N; ++t) serve(s, 1, t, false);
+        zi_source_stats st; zi_file_source_stats_get(s, &st);
+        printf("cached: tiles_read %lld\n", (long long)st.tiles_read);
+        if (st.tiles_read != N) ++bad;
         zi_file_source_destroy(s);
     }
     // 2. a shared tier over three sources: a recorded step, then replays with perturbations

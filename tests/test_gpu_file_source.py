@@ -53,7 +53,14 @@ def test_linear_from_file_bit_exact(tmp_path, dtype, N, d, staging):
     assert np.array_equal(host_bits(dWt), oracle.encode(dW, dtype)), "dW"
     st = src.stats()
     say("  source", st)
-    assert st["tiles_read"] >= 2 * S * N and st["restarts"] == 0
+    assert st["restarts"] == 0
+    # every tile is read at least once, and no request more than once (the
+    # read-ahead may run a few tiles past the last pass); with a buffer per
+    # tile exactly once: the buffers then hold the whole weight
+    if staging >= N:
+        assert st["tiles_read"] == N
+    else:
+        assert N <= st["tiles_read"] <= 2 * S * N + staging
     ctx.attach_source(plan, None)
     ctx.close()
     src.close()
@@ -173,15 +180,18 @@ def test_ffn_block_through_one_tier(tmp_path):
     check("recorded step")
     st = tier.stats()
     say("  after the recorded step", st)
-    assert st["trace_len"] == per_step and st["demand_reads"] == per_step and st["restarts"] == 0
+    # the recorded step is served on demand, or from a buffer that still holds the tile
+    assert st["trace_len"] == per_step and 0 < st["demand_reads"] <= per_step
+    assert st["restarts"] == 0
+    recorded_demand = st["demand_reads"]
     for n in range(2):                       # replayed
         run_block(tiling, ctx, p1, p2, b)
         tier.step()
         check("replayed step %d" % n)
     st = tier.stats()
     say("  after two replayed steps", st)
-    assert st["demand_reads"] == per_step and st["restarts"] == 0
-    assert st["tiles_read"] >= 3 * per_step
+    assert st["demand_reads"] == recorded_demand and st["restarts"] == 0
+    assert st["tiles_read"] + st["hits"] >= 3 * per_step
     # a forward-only step ends inside the trace: the next step starts over
     run_block(tiling, ctx, p1, p2, b, forward_only=True)
     tier.step()
