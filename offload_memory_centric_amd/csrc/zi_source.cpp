@@ -148,6 +148,7 @@ struct zi_tier {
         State state = FREE;   // FREE: holds nothing valid
         int err = 0;          // errno of a failed read
         bool held = false;    // handed to a request whose copy is not enqueued yet
+        bool reserved = false;// read on demand for a request that has not taken it yet
         uint64_t copies = 0;  // copies out of it enqueued ('copied' recorded after each)
         uint64_t synced = 0;  // copies known to be done
         hipEvent_t copied = nullptr;
@@ -204,7 +205,7 @@ struct zi_tier {
         int64_t far = -1;
         for (int b = 0; b < S; ++b) {
             const Buf &x = bufs[b];
-            if (x.state == READING || x.held || pending(b)) continue;
+            if (x.state == READING || x.held || x.reserved || pending(b)) continue;
             if (x.state == FREE) return b;
             const int64_t d = next_use(x.item);
             if (d > far) {
@@ -271,8 +272,9 @@ struct zi_tier {
             if (for_trace) {
                 assigned.push_back(k);
                 ++rpos;
-            } else {
+            } else {  // kept for the waiting request until it takes the buffer
                 demand = false;
+                bufs[k].reserved = true;
                 ++demand_reads;
             }
             lock.unlock();
@@ -449,6 +451,7 @@ zi_status source_acquire(zi_file_source *s, int64_t tile, const void **host, int
         const int err = t->bufs[b].err;
         t->bufs[b].state = zi_tier::FREE;
         t->bufs[b].item = zi_tier::Item{};
+        t->bufs[b].reserved = false;
         // later positions may have been given the same buffer: plan them again
         t->assigned.clear();
         t->rpos = t->pos;
@@ -456,6 +459,8 @@ zi_status source_acquire(zi_file_source *s, int64_t tile, const void **host, int
         return fail(ZI_ERR_IO, "reading tile %lld: %s", (long long)tile, strerror(err));
     }
     t->bufs[b].held = true;
+    for (auto &x : t->bufs)  // an on-demand read of this tile is no longer waited for
+        if (x.item == want) x.reserved = false;
     *host = t->buf[b];
     *slot = b;
     return ZI_OK;

@@ -101,6 +101,25 @@ int main(int argc, char **argv) {
         zi_tier_destroy(tier);
         for (int i = 0; i < 3; ++i) zi_file_source_destroy(s[i]);
     }
+    // 3. few buffers and requests off the trace: an on-demand read must not be
+    //    evicted by the read-ahead before its request takes it
+    {
+        zi_tier *tier = nullptr; zi_tier_create(2, 2, &tier);
+        zi_file_source *s[3];
+        for (int i = 0; i < 3; ++i) { zi_file_source_create(&plan, paths[i], 0, 2, 2, &s[i]); zi_tier_add(tier, s[i]); }
+        for (int t = 0; t < N; ++t) serve(s[0], 0, t, false);
+        for (int t = 0; t < N; ++t) serve(s[1], 1, t, false);
+        zi_tier_step(tier);
+        for (int k = 0; k < 300; ++k) {
+            const int t = (int)(rng() % N);
+            if (rng() % 3 == 0) serve(s[2], 2, t, false);  // never in the trace
+            serve(s[k % 2], k % 2, (k / 2) % N, false);
+        }
+        zi_tier_stats ts; zi_tier_stats_get(tier, &ts);
+        printf("off-trace: demand %lld restarts %lld\n", (long long)ts.demand_reads, (long long)ts.restarts);
+        zi_tier_destroy(tier);
+        for (int i = 0; i < 3; ++i) zi_file_source_destroy(s[i]);
+    }
     for (auto p : paths) remove(p);
     printf("served %d bad %d\n", served, bad);
     return bad != 0;
