@@ -58,8 +58,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--d2h-cus", type=int, default=None,
                     help="compute units of the device-to-host copy stream (0: unrestricted)")
-    ap.add_argument("--overlap", action="store_true",
-                    help="a second product stream: forward tiles alternate between two streams")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="no second product stream (few-wave forward tiles then run on one stream too)")
     ap.add_argument("--adam", action="store_true",
                     help="attach the host Adam to every weight: each tile is updated on the host "
                          "once its gradient has landed, overlapped with the next tiles")
@@ -217,8 +217,8 @@ def main():
     seed = 0
 
     ctx_kw = {} if args.d2h_cus is None else {"d2h_cus": args.d2h_cus}
-    if args.overlap:
-        ctx_kw["overlap"] = True
+    if args.no_overlap:
+        ctx_kw["overlap"] = False
 
     # ---------------- workload ----------------
     if args.workload == "ffn":

@@ -273,10 +273,12 @@ typedef struct {
 zi_status zi_ctx_set_timing(zi_ctx *ctx, int32_t enable);
 
 /* A second product stream (caller-owned, default priority, distinct from the
- * context's three; NULL: none).  A forward pass then launches the products of
- * its odd tiles on it and of its even tiles on the first: the tiles' outputs
- * are disjoint, and the next tile's workgroups fill the compute units that the
- * last, partial wave of the previous tile's leaves idle.  Backward passes keep
+ * context's three; NULL: none).  A forward pass whose tile products take
+ * fewer than 8 waves of workgroups (one 256 x 256 output block per compute
+ * unit and wave) then launches the products of its odd tiles on it and of
+ * its even tiles on the first: the tiles' outputs are disjoint, and the next
+ * tile's workgroups fill the compute units that the last, partial wave of the
+ * previous tile's leaves idle.  Backward passes keep
  * all their products on the first stream.  The second stream waits for
  * everything enqueued before
  * the pass, and the first stream waits for the second at the pass's end, so

@@ -99,15 +99,15 @@ class Context:
     By default the context creates its own three streams, one after another, so
     that they sit on distinct hardware queues (see zi_stream_create): products,
     host-to-device copies, and device-to-host copies confined to ``d2h_cus``
-    compute units (0: unconfined).  With ``overlap`` it also makes a second
-    product stream, on which the forward passes run every other tile's
-    product.  The products do not run on torch's current stream: inputs
+    compute units (0: unconfined).  With ``overlap`` (the default) it also
+    makes a second product stream, on which forward passes whose tiles take
+    few workgroup waves run every other tile's product.  The products do not run on torch's current stream: inputs
     must be complete before a call (torch.cuda.synchronize()), and outputs are
     ready once sync() returns.
     """
 
     def __init__(self, plan: Plan, device: str = "cuda", workspace_bytes: Optional[int] = None,
-                 streams=None, d2h_cus: int = D2H_CUS, overlap: bool = False):
+                 streams=None, d2h_cus: int = D2H_CUS, overlap: bool = True):
         nbytes = int(workspace_bytes if workspace_bytes is not None else plan.info.ring_bytes)
         self.handle = None
         self._own_streams = []
