@@ -120,6 +120,52 @@ int main(int argc, char **argv) {
         zi_tier_destroy(tier);
         for (int i = 0; i < 3; ++i) zi_file_source_destroy(s[i]);
     }
+    // 4. the cache against the offline optimum: a block-like step (source 0's
+    //    tiles three times, source 1's twice) under C buffers reads no fewer
+    //    tiles per step than Belady's eviction with C slots (no policy can),
+    //    and with a buffer per distinct tile nothing after the first step
+    for (int C : {2, 3, 5, 8}) {
+        zi_tier *tier = nullptr; zi_tier_create(C, 2, &tier);
+        zi_file_source *s[2];
+        for (int i = 0; i < 2; ++i) { zi_file_source_create(&plan, paths[i], 0, 2, 2, &s[i]); zi_tier_add(tier, s[i]); }
+        std::vector<std::pair<int, int>> step;
+        for (int pass : {0, 1, 0, 1, 0})
+            for (int t = 0; t < N; ++t) step.push_back({pass, t});
+        auto run_step = [&] { for (auto &r : step) serve(s[r.first], r.first, r.second, false); };
+        run_step();
+        zi_tier_step(tier);
+        const int steps = 6;
+        zi_tier_stats a; zi_tier_stats_get(tier, &a);
+        for (int k = 0; k < steps; ++k) { run_step(); zi_tier_step(tier); }
+        zi_tier_stats b; zi_tier_stats_get(tier, &b);
+        // Belady with C slots over the same steps (steady state: after a first step)
+        std::vector<std::pair<int, int>> seq;
+        for (int k = 0; k < steps + 2; ++k) seq.insert(seq.end(), step.begin(), step.end());
+        std::vector<std::pair<int, int>> cache;
+        long misses = 0;
+        for (size_t i = 0; i < seq.size(); ++i) {
+            bool hit = false;
+            for (auto &c : cache) hit = hit || c == seq[i];
+            if (hit) continue;
+            if (i >= step.size() && i < step.size() * (steps + 1)) ++misses;
+            if ((int)cache.size() == C) {
+                size_t far = 0, vi = 0;
+                for (size_t c = 0; c < cache.size(); ++c) {
+                    size_t j = i + 1;
+                    while (j < seq.size() && !(seq[j] == cache[c])) ++j;
+                    if (j >= far) { far = j; vi = c; }
+                }
+                cache.erase(cache.begin() + vi);
+            }
+            cache.push_back(seq[i]);
+        }
+        const long got = (long)(b.tiles_read - a.tiles_read);
+        printf("cache C=%d: reads %ld over %d steps, Belady %ld\n", C, got, steps, misses);
+        if (got < misses || got > (long)(steps * step.size() + C)) ++bad;
+        if (C >= 2 * N && got != 0) ++bad;
+        zi_tier_destroy(tier);
+        for (int i = 0; i < 2; ++i) zi_file_source_destroy(s[i]);
+    }
     for (auto p : paths) remove(p);
     printf("served %d bad %d\n", served, bad);
     return bad != 0;
