@@ -196,7 +196,7 @@ def main():
     import numpy as np
     import torch
 
-    from offload_memory_centric_amd import inputs, tiling
+    from offload_memory_centric_amd import inputs, tiling, zi
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -402,6 +402,18 @@ def main():
         result["nvme"] = nvme_report(args, tiling, sources, src_before, kinds, wall, flops_step * args.steps)
         if tier is not None:
             result["nvme"]["tier"] = tier.stats()
+            # the tier's buffer policy on its recorded trace, without files or
+            # threads, with the read-ahead 1, 2 or every buffer ahead of the
+            # requests (a reader held back by the disk runs one or two ahead)
+            trace = zi.zi_tier_trace_get(tier.handle)
+            tile = plans[0].info.tile_bytes
+            assert all(p.info.tile_bytes == tile for p in plans), "reads are counted in tiles of one size"
+            S = args.nvme_staging
+            result["nvme"]["predicted_GB_read_per_step"] = {
+                str(w): round(zi.zi_tier_simulate_reads(trace, S, 4, w)[-1] * tile / 1e9, 2)
+                for w in sorted({1, min(2, S), S})}
+            result["nvme"]["measured_GB_read_per_step"] = round(
+                result["nvme"]["bytes_read_timed"] / args.steps / 1e9, 2)
     adams = []
     if args.adam:
         result["adam"] = host_adam_leg(args, torch, tiling, ctx, plans, marked, spans, ms_step)

@@ -484,6 +484,24 @@ typedef struct {
     double read_s, bytes, wait_s;
 } zi_tier_stats;
 zi_status zi_tier_stats_get(zi_tier *tier, zi_tier_stats *out);
+/* The recorded trace, one id per request: (index of the source in the order
+ * it was added) << 32 | tile.  *len receives the trace's length; up to cap
+ * ids are written (ids may be NULL to ask for the length).  ZI_ERR_STATE
+ * while the first step is still being recorded. */
+zi_status zi_tier_trace_get(zi_tier *tier, int64_t *ids, int64_t cap, int64_t *len);
+/* The tier's buffer policy applied to a trace of item ids without files or
+ * threads, for choosing a buffer count: before each request the read-ahead
+ * fills its window (up to `window` requests ahead, 1 <= window <= buffers; a
+ * tile a buffer holds is assigned without a read, else it is read into the
+ * buffer the policy picks), then the request takes its buffer.
+ * reads_per_step[k] receives the reads of step k (steps entries; step 0
+ * starts empty).  The tier's reads run at most `buffers` requests ahead; a
+ * reader held back by the disk runs only one or two ahead and keeps the other
+ * buffers as cache, and window = 1 gives the offline optimum of buffers - 1
+ * slots or better.  No GPU is involved.  ZI_ERR_ARG on an empty trace,
+ * buffers < 2, a window outside 1..buffers or steps < 1. */
+zi_status zi_tier_simulate_reads(const int64_t *trace, int64_t len, int32_t buffers, int32_t window, int32_t steps,
+                                 int64_t *reads_per_step);
 
 /* Page-locked host memory (hipHostMalloc) for W^t / dW^t; 4096-byte aligned. */
 zi_status zi_host_alloc(uint64_t bytes, void **out);

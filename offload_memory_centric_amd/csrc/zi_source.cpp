@@ -489,9 +489,89 @@ void source_abandon(zi_file_source *s, int slot) {
     t->cv.notify_all();
 }
 
+// The tier's buffer policy run without threads or files on a trace of item
+// ids: before each request the reader fills its window (up to W positions
+// ahead, W <= S; a held tile assigned without a read, else a read into the
+// buffer the policy picks), then the request takes its position's buffer.
+// Returns the reads attributed to each step (by the position read).
+static std::vector<int64_t> tier_simulate(const std::vector<int64_t> &trace, int S, int W, int steps) {
+    const int64_t L = (int64_t)trace.size();
+    std::vector<int64_t> reads(steps, 0);
+    std::vector<int64_t> item(S, -1);
+    std::deque<int> pend;
+    int64_t pos = 0, rpos = 0;
+    auto at = [&](int64_t q) { return trace[(size_t)(q % L)]; };
+    auto next_use = [&](int64_t it) -> int64_t {
+        for (int64_t j = 0; j < L; ++j)
+            if (at(rpos + j) == it) return j;
+        return L + 1;
+    };
+    for (int64_t r = 0; r < (int64_t)steps * L; ++r) {
+        while (rpos - pos < W && rpos < (int64_t)steps * L) {
+            const int64_t it = at(rpos);
+            int b = -1;
+            for (int k = 0; k < S && b < 0; ++k)
+                if (item[k] == it) b = k;
+            if (b < 0) {
+                int64_t far = -1;
+                for (int k = 0; k < S; ++k) {
+                    bool p = false;
+                    for (int x : pend) p = p || x == k;
+                    if (p) continue;
+                    if (item[k] < 0) {
+                        b = k;
+                        break;
+                    }
+                    const int64_t d = next_use(item[k]);
+                    if (d > far) {
+                        far = d;
+                        b = k;
+                    }
+                }
+                if (b < 0) break;  // every buffer waits for a pending request
+                item[b] = it;
+                ++reads[(size_t)(rpos / L)];
+            }
+            pend.push_back(b);
+            ++rpos;
+        }
+        pend.pop_front();  // request r (= pos) takes its buffer
+        ++pos;
+    }
+    return reads;
+}
+
 }  // namespace zi
 
 extern "C" {
+
+zi_status zi_tier_simulate_reads(const int64_t *trace, int64_t len, int32_t buffers, int32_t window, int32_t steps,
+                                 int64_t *reads_per_step) {
+    clear_error();
+    if (!trace || !reads_per_step || len < 1) return fail(ZI_ERR_ARG, "a trace of at least one request is required");
+    if (buffers < 2) return fail(ZI_ERR_ARG, "at least two buffers (got %d)", buffers);
+    if (window < 1 || window > buffers) return fail(ZI_ERR_ARG, "window must be in 1..buffers (got %d)", window);
+    if (steps < 1) return fail(ZI_ERR_ARG, "steps must be >= 1");
+    const std::vector<int64_t> t(trace, trace + len);
+    const std::vector<int64_t> r = tier_simulate(t, buffers, window, steps);
+    for (int k = 0; k < steps; ++k) reads_per_step[k] = r[(size_t)k];
+    return ZI_OK;
+}
+
+zi_status zi_tier_trace_get(zi_tier *t, int64_t *ids, int64_t cap, int64_t *len) {
+    clear_error();
+    if (!t || !len) return fail(ZI_ERR_ARG, "tier and len are required");
+    std::lock_guard<std::mutex> lock(t->mu);
+    if (t->recording) return fail(ZI_ERR_STATE, "the trace is still being recorded (no zi_tier_step yet)");
+    *len = (int64_t)t->trace.size();
+    for (int64_t k = 0; k < *len && k < cap && ids; ++k) {
+        const zi_tier::Item &it = t->trace[(size_t)k];
+        int64_t s = 0;
+        while (s < (int64_t)t->srcs.size() && t->srcs[(size_t)s] != it.src) ++s;
+        ids[k] = (s << 32) | it.tile;
+    }
+    return ZI_OK;
+}
 
 zi_status zi_file_source_create(const zi_plan *plan, const char *path, uint64_t offset, int32_t staging,
                                 int32_t threads, zi_file_source **out) {

@@ -173,6 +173,9 @@ _sigs = {
     "zi_tier_step": (_S, [_P]),
     "zi_tier_destroy": (_S, [_P]),
     "zi_tier_stats_get": (_S, [_P, ctypes.POINTER(zi_tier_stats)]),
+    "zi_tier_trace_get": (_S, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
+    "zi_tier_simulate_reads": (_S, [ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
     "zi_host_alloc": (_S, [ctypes.c_uint64, ctypes.POINTER(_P)]),
     "zi_host_free": (_S, [_P]),
     "zi_last_error": (ctypes.c_char_p, []),
@@ -424,6 +427,22 @@ def zi_tier_stats_get(tier) -> dict:
     s = zi_tier_stats()
     _check(_lib.zi_tier_stats_get(tier, ctypes.byref(s)))
     return s.as_dict()
+
+
+def zi_tier_trace_get(tier) -> list:
+    n = ctypes.c_int64()
+    _check(_lib.zi_tier_trace_get(tier, None, 0, ctypes.byref(n)))
+    ids = (ctypes.c_int64 * max(1, n.value))()
+    _check(_lib.zi_tier_trace_get(tier, ids, n.value, ctypes.byref(n)))
+    return list(ids[:n.value])
+
+
+def zi_tier_simulate_reads(trace, buffers: int, steps: int, window: int = 0) -> list:
+    """Reads per step of the tier's policy on `trace`; window 0 means `buffers`."""
+    t = (ctypes.c_int64 * max(1, len(trace)))(*[int(x) for x in trace])
+    out = (ctypes.c_int64 * max(1, int(steps)))()
+    _check(_lib.zi_tier_simulate_reads(t, len(trace), int(buffers), int(window or buffers), int(steps), out))
+    return list(out[:int(steps)])
 
 
 def zi_host_alloc(nbytes: int) -> int:

@@ -303,3 +303,74 @@ def choose_tiling(T: int, K: int, M: int, dtype: str, budget: int, widths, r_fwd
                 if (c["ring_bytes"], c["d"], c["N"]) < (best["ring_bytes"], best["d"], best["N"]):
                     best = c
     return best, table
+
+
+# --- the file tier's buffers as a cache (our reading R30 of the pages' CPU
+#     memory in front of NVMe; [ZI-cn] "关键技术三：Overlap-Centric Design")
+
+def belady_reads(trace, capacity: int, steps: int):
+    """Reads per step of the offline optimum (Belady): a cache of `capacity`
+    items over `steps` repetitions of `trace`, evicting on a miss the item
+    whose next request is farthest away (never requested again counts as
+    farthest).  No policy reads fewer."""
+    seq = list(trace) * steps
+    L = len(trace)
+    held = set()
+    reads = [0] * steps
+    for i, x in enumerate(seq):
+        if x in held:
+            continue
+        reads[i // L] += 1
+        if len(held) == capacity:
+            def nxt(y):
+                for j in range(i + 1, len(seq)):
+                    if seq[j] == y:
+                        return j
+                return len(seq) + 1
+            held.remove(max(held, key=nxt))
+        held.add(x)
+    return reads
+
+
+def tier_policy_reads(trace, buffers: int, steps: int, window: int = 0):
+    """Reads per step of the tier's policy with its read-ahead `window`
+    requests ahead (0: as far as it may, `buffers`): before each request the
+    reader walks the trace from its position until `window` requests are
+    waiting; a tile some buffer
+    holds is given that buffer without a read; otherwise the tile is read into
+    a buffer no waiting request needs, an empty one first, else the one whose
+    tile is next wanted latest (counted from the reader's position along the
+    repeating trace).  Then the request takes the first waiting buffer."""
+    L = len(trace)
+    total = steps * L
+    tiles = [None] * buffers          # what each buffer holds
+    waiting = []                      # buffer of each request read ahead for, in order
+    reads = [0] * steps
+    ahead = 0                         # next position the reader looks at
+    window = window or buffers
+    for _ in range(total):
+        while len(waiting) < window and ahead < total:
+            want = trace[ahead % L]
+            if want in tiles:
+                waiting.append(tiles.index(want))
+                ahead += 1
+                continue
+            free = [b for b in range(buffers) if b not in waiting]
+            if not free:
+                break
+            empty = [b for b in free if tiles[b] is None]
+            if empty:
+                b = empty[0]
+            else:
+                def wanted_in(b):
+                    for j in range(L):
+                        if trace[(ahead + j) % L] == tiles[b]:
+                            return j
+                    return L + 1
+                b = max(free, key=lambda c: (wanted_in(c), -c))
+            tiles[b] = want
+            reads[ahead // L] += 1
+            waiting.append(b)
+            ahead += 1
+        waiting.pop(0)
+    return reads
