@@ -184,6 +184,12 @@ def test_ffn_block_through_one_tier(tmp_path):
     assert st["trace_len"] == per_step and 0 < st["demand_reads"] <= per_step
     assert st["restarts"] == 0
     recorded_demand = st["demand_reads"]
+    # the recorded order, as (source index << 32 | tile): W1 forward, W2
+    # forward, W1 recomputed, W2 backward, W1 backward, each tile ascending
+    from offload_memory_centric_amd import zi
+    order = [(0, t) for t in range(N1)] + [(1, t) for t in range(N2)] + [(0, t) for t in range(N1)] + \
+        [(1, t) for t in range(N2)] + [(0, t) for t in range(N1)]
+    assert zi.zi_tier_trace_get(tier.handle) == [(s << 32) | t for s, t in order]
     for n in range(2):                       # replayed
         run_block(tiling, ctx, p1, p2, b)
         tier.step()
