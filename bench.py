@@ -185,8 +185,8 @@ def link_peak_in_child():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the tiled path runs on a single device and has no "
+              "multi-GPU form (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     link = None
     if not args.no_link_peak and not args.link_peak_only and not args.copy_probe:
