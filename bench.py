@@ -691,8 +691,8 @@ def cpu_baseline(args, np, torch, config, env):
         X, dY, W1t, W2t = (_bits(torch, np, env[k]) for k in ("X", "dY", "W1t", "W2t"))
         T, D, F = config["T"], config["d_model"], config["d_ff"]
         rng = np.random.default_rng(0)
-        nt = 8
-        nf = 16
+        nt = 32
+        nf = 64
         t_rows = np.sort(rng.choice(T, nt, replace=False))
         f_cols = np.sort(rng.choice(F, nf, replace=False))
         d2 = np.sort(rng.choice(D, 2, replace=False))
