@@ -199,6 +199,22 @@ struct zi_tier {
         return L + 1;
     }
 
+    // An off-trace request has found every buffer kept for upcoming trace
+    // positions: give back read-ahead buffers from the farthest position
+    // down, until one may be overwritten.  A buffer given back keeps its tile
+    // (the cache may still serve it when the read-ahead comes back there).
+    // Returns whether anything was given back.
+    bool trim_read_ahead() {
+        bool any = false;
+        while (!assigned.empty() && victim() < 0) {
+            if (bufs[assigned.back()].state == READING) break;
+            assigned.pop_back();
+            --rpos;
+            any = true;
+        }
+        return any;
+    }
+
     // A buffer the reader may overwrite, or -1.
     int victim() const {
         int best = -1;
@@ -252,6 +268,10 @@ struct zi_tier {
             }
             const int k = victim();
             if (k < 0) {
+                // only the consumer frees a held buffer; buffers kept for the
+                // trace are given back to a request the trace does not hold,
+                // which would otherwise wait for them forever
+                if (!for_trace && trim_read_ahead()) continue;
                 cv.wait(lock);
                 continue;
             }

@@ -6,7 +6,11 @@
 // every staged buffer against the file's bytes; with as many buffers as
 // tiles, every tile must be read exactly once.  Usage: tier_stress DIR
 #include "../../offload_memory_centric_amd/csrc/zi_source.cpp"
+#include <unistd.h>
+
+#include <chrono>
 #include <random>
+#include <thread>
 #include <stdarg.h>
 extern "C" {
 hipError_t hipGetDevice(int *d) { *d = 0; return hipSuccess; }
@@ -165,6 +169,28 @@ int main(int argc, char **argv) {
         if (C >= 2 * N && got != 0) ++bad;
         zi_tier_destroy(tier);
         for (int i = 0; i < 2; ++i) zi_file_source_destroy(s[i]);
+    }
+    // 5. an off-trace request after the read-ahead has taken every buffer for
+    //    upcoming trace positions: the reader must give one of them back for
+    //    the read on demand (a hang here is caught by the alarm)
+    for (int round = 0; round < 3; ++round) {
+        alarm(60);
+        zi_tier *tier = nullptr; zi_tier_create(2, 2, &tier);
+        zi_file_source *s[2];
+        for (int i = 0; i < 2; ++i) { zi_file_source_create(&plan, paths[i], 0, 2, 2, &s[i]); zi_tier_add(tier, s[i]); }
+        for (int t = 0; t < N; ++t) serve(s[0], 0, t, false);
+        zi_tier_step(tier);
+        serve(s[0], 0, 0, false);
+        std::this_thread::sleep_for(std::chrono::milliseconds(200));  // both buffers now hold trace tiles 1, 2
+        serve(s[1], 1, round % N, false);                             // never in the trace
+        for (int t = 1; t < N; ++t) serve(s[0], 0, t, false);         // the trace goes on
+        serve(s[0], 0, 0, false);
+        zi_tier_stats ts; zi_tier_stats_get(tier, &ts);
+        printf("read-ahead given back: demand %lld restarts %lld\n", (long long)ts.demand_reads, (long long)ts.restarts);
+        if (ts.demand_reads < 1) ++bad;
+        zi_tier_destroy(tier);
+        for (int i = 0; i < 2; ++i) zi_file_source_destroy(s[i]);
+        alarm(0);
     }
     for (auto p : paths) remove(p);
     printf("served %d bad %d\n", served, bad);
