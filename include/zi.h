@@ -111,6 +111,14 @@ typedef struct zi_plan zi_plan; /* library-owned, immutable after creation */
 typedef struct zi_ctx zi_ctx;   /* library-owned: ring over caller workspace, events */
 
 /* Plan the tiling of one linear operator.
+ * The split is the method's core step (pwwt.cn article, section
+ * "关键技术一：Memory-centric tiling", core idea and its worked example of a
+ * 64K x 256K layer in N = 16 tiles: W is cut along its output dimension into N
+ * tiles W_1..W_N of M/N columns, each small enough to sit in device memory on
+ * its own); the working-memory figures follow the transformer-math page,
+ * section "Memory-centric tiling: operators bigger than the device" (the layer's
+ * bytes divided by the tile count for one resident tile, twice that with one
+ * tile in flight beside it).
  * Validates the shapes (N | M, K % 8 == 0, n % 8 == 0, T >= 1), the dtype,
  * and the budget: the forward needs d weight slots; the backward additionally
  * needs somewhere to form dW_i -- up to two separate gradient slots if the
@@ -216,14 +224,30 @@ zi_status zi_ctx_destroy(zi_ctx *ctx);
 /* Forward: Y[:, i*n:(i+1)*n] = RNE(X W_i) for i = 0..N-1, tiles in ascending
  * order, fp32 accumulation, one rounding into the input format (or fp32 with
  * ZI_FLAG_F32_OUT).  X [T x K] and Y [T x M] (ldc = M) are device pointers,
- * 16-byte aligned. */
+ * 16-byte aligned.
+ * This is the forward of the pages' tiled operator: each tile is brought into
+ * device memory, multiplies X into its own output slice, and is released before
+ * the next one needs its buffer (pwwt.cn article, section "关键技术一：Memory-
+ * centric tiling", worked example: load W_i, compute Y_i, free W_i, go on with
+ * W_{i+1}); the column slices need no communication between tiles and their
+ * concatenation is Y (transformer-math page, section "Memory-centric tiling:
+ * operators bigger than the device").  The copy of tile i + d runs under the
+ * products of tile i (the same page, section "Prefetch depth: how far ahead the
+ * pipeline must run").  ZI_ERR_ARG / ZI_ERR_ALIGN on NULL or misaligned
+ * pointers, ZI_ERR_STATE when the plan does not fit the context,
+ * ZI_ERR_NOT_PINNED when W_host is not page-locked; nothing is enqueued then. */
 zi_status zi_tiled_linear_fwd(zi_ctx *ctx, const zi_plan *plan, const void *X_dev, void *Y_dev);
 
 /* Forward with the GeLU of the feed-forward block fused into the epilogue
  * (the 1T model's FFN, transformer-math page, section "Memory-centric
  * tiling"): A = RNE(X W) and H = RNE(GeLU(A)), GeLU in the exact erf form
- * evaluated in fp32 on the stored (rounded) A.  A and H are [T x M] device
- * buffers in the input format.  Not available with ZI_FLAG_F32_OUT. */
+ * evaluated in fp64 on the stored (rounded) A and rounded once into the input
+ * format, so H is the correctly rounded GeLU of A (the epilogue reads it from
+ * a per-device table over every 16-bit A).  A and H are [T x M] device
+ * buffers in the input format.  With ZI_FLAG_F32_OUT, A is written in fp32
+ * instead (the fp32 accumulator itself: A_dev then holds 4-byte elements)
+ * while H is still GeLU of A rounded to the input format, exactly as without
+ * the flag. */
 zi_status zi_tiled_linear_fwd_gelu(zi_ctx *ctx, const zi_plan *plan, const void *X_dev,
                                    void *A_dev, void *H_dev);
 
@@ -233,7 +257,16 @@ zi_status zi_tiled_linear_fwd_gelu(zi_ctx *ctx, const zi_plan *plan, const void 
  *                                        input format, or fp32 with ZI_FLAG_F32_OUT),
  * and dW_i is copied to dW_host rows [i*n, (i+1)*n) on the write-back stream.
  * dX_dev: fp32 [T x K].  Requires a plan with dW_host.  dW_host must not be
- * read before zi_sync(). */
+ * read before zi_sync().
+ * The backward stages every tile a second time (transformer-math page, section
+ * "The FLOPs-per-byte test every tier must pass": the parameters climb to the
+ * device once for the forward and once more for the backward), and each
+ * tile's gradient leaves for host memory while the next tiles' products run
+ * (pwwt.cn article, section "关键技术三：Overlap-Centric Design": the gradient
+ * copies to the CPU overlap the backward's compute).  dX is summed over the
+ * tiles in fp32, in ascending tile order.  Errors as zi_tiled_linear_fwd,
+ * plus ZI_ERR_ARG without dW_host and ZI_ERR_NOT_PINNED when it is not
+ * page-locked. */
 zi_status zi_tiled_linear_bwd(zi_ctx *ctx, const zi_plan *plan, const void *X_dev,
                               const void *dY_dev, float *dX_dev);
 
@@ -246,18 +279,46 @@ zi_status zi_tiled_linear_bwd_recompute(zi_ctx *ctx, const zi_plan *plan, const 
                                         const void *dY_dev, float *dX_dev, void *Yr_dev);
 
 /* dA = RNE(dH * GeLU'(A)) elementwise on the compute stream, GeLU'(a) =
- * Phi(a) + a phi(a) evaluated in fp32 on the stored A.  dH: fp32 device,
- * A and dA: device, input format `dtype`; `count` elements each. */
+ * Phi(a) + a phi(a) evaluated in fp32 on the stored A (the chain rule through
+ * the block's GeLU; transformer-math page, section "Memory-centric tiling":
+ * the 1T model's FFN).  dH: fp32 device, A and dA: device, input format
+ * `dtype`; `count` elements each, 16-byte aligned pointers. */
 zi_status zi_gelu_bwd(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const void *A_dev,
                       void *dA_dev, int64_t count);
 
-/* Wait for everything enqueued on the context's three streams; return the
- * first error (sticky). */
+/* The same product left in fp32: dA_dev[i] = dH[i] * GeLU'(A[i]), the value
+ * that zi_gelu_bwd rounds once into the input format (the form in which the
+ * result can be compared without that rounding).  dA_dev: fp32 device. */
+zi_status zi_gelu_bwd_f32(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const void *A_dev,
+                          float *dA_dev, int64_t count);
+
+/* Wait for everything enqueued on the context's three streams (and the
+ * second product stream, if set) and for the host optimizers attached to it;
+ * return the first error, which stays with the context (sticky).  The passes
+ * only enqueue work so that the copies of later tiles run ahead of the
+ * products (transformer-math page, section "Prefetch depth: how far ahead the
+ * pipeline must run"; pwwt.cn article, section "关键技术三：Overlap-Centric
+ * Design"); this is the one point at which the host waits for them.  After
+ * ZI_OK every output of the enqueued passes, device and host, may be read. */
 zi_status zi_sync(zi_ctx *ctx);
 
 /* Per-context timing (off by default).  When on, every kernel launch and
  * every copy is bracketed by timing events; zi_ctx_stats() (after zi_sync)
  * reports the totals since the last reset. */
+#define ZI_STATS_KERNELS 16
+/* One kernel: a product (or the GeLU backward) at one launch shape.  Launches
+ * of different roles that run the same kernel on the same shape (a forward
+ * product and its recomputation, for instance) share an entry. */
+typedef struct {
+    char name[24];               /* "gemm_fwd", "gemm_fwd_gelu", "gemm_dx", "gemm_dw", "gelu_bwd" */
+    int64_t rows, cols, red;     /* output rows and columns and reduction length of one launch
+                                    (gelu_bwd: rows = elements, cols = red = 1) */
+    int64_t launches;
+    double ms;                   /* sum of event-measured durations of all launches */
+    double flops;                /* algorithmic FLOPs of those launches (gelu_bwd: elements) */
+    int64_t solo_launches;       /* launches no other kernel of the context overlapped */
+    double solo_ms;              /* their summed durations: the kernel's time on its own */
+} zi_kernel_stats;
 typedef struct {
     int32_t kind_count;          /* number of valid entries below */
     char kind_name[8][24];       /* "gemm_fwd", "gemm_fwd_gelu", "gemm_dx", "gemm_dw", ... */
@@ -269,6 +330,9 @@ typedef struct {
     double h2d_bytes, d2h_bytes;
     double span_ms;              /* first timed event -> last timed event */
     double compute_busy_ms;      /* time some kernel ran: the union of their intervals */
+    int32_t kernel_count;        /* valid entries of kernel[] (launch shapes beyond the
+                                    table's size are counted in the per-kind totals only) */
+    zi_kernel_stats kernel[ZI_STATS_KERNELS];
 } zi_stats;
 zi_status zi_ctx_set_timing(zi_ctx *ctx, int32_t enable);
 

@@ -57,6 +57,8 @@ struct KernelRec {
     int kind;
     double flops;
     hipEvent_t a, b;
+    int op;                    // kernel identity: GemmOp (or -1: GeLU backward) and launch shape
+    int64_t rows, cols, red;
 };
 struct CopyRec {
     int d2h;
@@ -297,7 +299,7 @@ zi_status gemm(zi_ctx *c, int kind, GemmOp op, int dtype, const GemmArgs &a, dou
         zi_status st = ev_timed(c, &eb);
         if (st != ZI_OK) return st;
         HIPCHK(c, hipEventRecord(eb, stream));
-        c->krec.push_back(KernelRec{kind, flops, ea, eb});
+        c->krec.push_back(KernelRec{kind, flops, ea, eb, (int)op, a.rows, a.cols, a.red});
     }
     return ZI_OK;
 }
@@ -645,8 +647,6 @@ zi_status zi_tiled_linear_fwd_gelu(zi_ctx *ctx, const zi_plan *plan, const void 
     clear_error();
     zi_status st = check_pass(ctx, plan, false);
     if (st != ZI_OK) return st;
-    if (plan->prob.flags & ZI_FLAG_F32_OUT)
-        return fail(ZI_ERR_ARG, "the GeLU forward stores A and H in the input format only");
     if ((st = check_dev_ptr(X_dev, "X")) != ZI_OK || (st = check_dev_ptr(A_dev, "A")) != ZI_OK ||
         (st = check_dev_ptr(H_dev, "H")) != ZI_OK)
         return st;
@@ -711,8 +711,8 @@ zi_status zi_ctx_attach_adam(zi_ctx *ctx, const zi_plan *plan, zi_adam *adam) {
     return ZI_OK;
 }
 
-zi_status zi_gelu_bwd(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const void *A_dev, void *dA_dev,
-                      int64_t count) {
+static zi_status gelu_bwd(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const void *A_dev, void *dA_dev,
+                          int64_t count, bool out_f32) {
     clear_error();
     zi_status st = check_ctx(ctx);
     if (st != ZI_OK) return st;
@@ -726,14 +726,24 @@ zi_status zi_gelu_bwd(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const voi
         if ((st = ev_timed(ctx, &ea)) != ZI_OK) return st;
         HIPCHK(ctx, hipEventRecord(ea, ctx->comp));
     }
-    hipError_t e = launch_gelu_bwd(dtype, dH_dev, A_dev, dA_dev, count, ctx->comp);
+    hipError_t e = launch_gelu_bwd(dtype, dH_dev, A_dev, dA_dev, count, out_f32, ctx->comp);
     if (e != hipSuccess) return hip_fail(ctx, e, "gelu_bwd");
     if (ctx->timing) {
         if ((st = ev_timed(ctx, &eb)) != ZI_OK) return st;
         HIPCHK(ctx, hipEventRecord(eb, ctx->comp));
-        ctx->krec.push_back(KernelRec{K_GELU_BWD, (double)count, ea, eb});
+        ctx->krec.push_back(KernelRec{K_GELU_BWD, (double)count, ea, eb, -1, count, 1, 1});
     }
     return ZI_OK;
+}
+
+zi_status zi_gelu_bwd(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const void *A_dev, void *dA_dev,
+                      int64_t count) {
+    return gelu_bwd(ctx, dtype, dH_dev, A_dev, dA_dev, count, false);
+}
+
+zi_status zi_gelu_bwd_f32(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const void *A_dev, float *dA_dev,
+                          int64_t count) {
+    return gelu_bwd(ctx, dtype, dH_dev, A_dev, dA_dev, count, true);
 }
 
 zi_status zi_sync(zi_ctx *ctx) {
@@ -822,6 +832,7 @@ zi_status zi_ctx_stats(zi_ctx *ctx, zi_stats *out) {
         return ZI_OK;
     };
     std::vector<std::pair<double, double>> busy;  // kernel intervals, ms after the first event
+    std::vector<double> dur;                        // per launch, in krec order
     for (const KernelRec &r : ctx->krec) {
         float ms = 0, t0 = 0;
         HIPCHK(ctx, hipEventElapsedTime(&ms, r.a, r.b));
@@ -830,7 +841,59 @@ zi_status zi_ctx_stats(zi_ctx *ctx, zi_stats *out) {
         out->kernel_ms[r.kind] += ms;
         out->flops[r.kind] += r.flops;
         busy.emplace_back(t0, (double)t0 + ms);
+        dur.push_back(ms);
         if ((st = span(r.a, r.b)) != ZI_OK) return st;
+    }
+    // Per kernel (product and launch shape): totals, and the launches that ran
+    // alone.  A launch ran alone when no other launch's interval reaches into
+    // it; intervals that only touch (within 2 us, the events' resolution on one
+    // stream) do not count as overlapping.
+    {
+        const size_t n = busy.size();
+        std::vector<size_t> order(n);
+        for (size_t i = 0; i < n; ++i) order[i] = i;
+        std::sort(order.begin(), order.end(), [&](size_t x, size_t y) { return busy[x] < busy[y]; });
+        std::vector<char> solo(n, 1);
+        constexpr double eps = 2e-3;
+        double reach = -1e300;  // latest end among the launches started so far
+        size_t reach_of = n;
+        for (size_t j = 0; j < n; ++j) {
+            const size_t i = order[j];
+            if (busy[i].first < reach - eps) {
+                solo[i] = 0;
+                if (reach_of < n) solo[reach_of] = 0;
+            }
+            if (busy[i].second > reach) {
+                reach = busy[i].second;
+                reach_of = i;
+            }
+        }
+        for (size_t i = 0; i < n; ++i) {
+            const KernelRec &r = ctx->krec[i];
+            int e = 0;
+            while (e < out->kernel_count &&
+                   !(out->kernel[e].rows == r.rows && out->kernel[e].cols == r.cols && out->kernel[e].red == r.red &&
+                     strcmp(out->kernel[e].name, kKindNames[r.op == -1 ? K_GELU_BWD : r.op]) == 0))
+                ++e;
+            if (e == out->kernel_count) {
+                if (e == ZI_STATS_KERNELS) continue;
+                ++out->kernel_count;
+                zi_kernel_stats &k = out->kernel[e];
+                // the name of the product, whichever pass launched it
+                snprintf(k.name, sizeof(k.name), "%s", kKindNames[r.op == -1 ? K_GELU_BWD : r.op]);
+                k.rows = r.rows;
+                k.cols = r.cols;
+                k.red = r.red;
+            }
+            zi_kernel_stats &k = out->kernel[e];
+            k.launches += 1;
+            k.ms += dur[i];
+            k.flops += r.flops;
+            if (solo[i]) {
+                k.solo_launches += 1;
+                k.solo_ms += dur[i];
+            }
+        }
     }
     // time the compute units had work: the union of the kernel intervals
     // (kernels on the two product streams may overlap)

@@ -11,7 +11,7 @@ namespace zi {
 // contiguous; "Q" is the operand indexed by q, "P" the operand indexed by p.
 enum class GemmOp : int {
     Fwd = 0,      // Y_i[t][m]  = sum_k X[t][k] W^t_i[m][k]      (Q = W slot, P = X)
-    FwdGelu = 1,  // same product; stores A = RNE(acc) and H = RNE(GeLU(A))
+    FwdGelu = 1,  // same product; stores A = RNE(acc) (fp32 acc with out_f32) and H = RNE(GeLU(RNE(acc)))
     Dx = 2,       // dX[t][k]  (+)= sum_r dY[t][i*n+r] W^t_i[r][k] (Q = W slot^T, P = dY)
     Dw = 3,       // dW^t_i[m][k] = sum_t dY[t][i*n+m] X[t][k]    (Q = X^T,      P = dY^T)
 };
@@ -28,7 +28,7 @@ struct GemmArgs {
     int64_t cols;   // extent of q (multiple of 8)
     int64_t red;    // reduction length
     int accumulate; // Dx only: 0 = overwrite, 1 = add into C
-    int out_f32;    // Fwd / Dw: write fp32 instead of the 16-bit format
+    int out_f32;    // Fwd / Dw: write fp32 instead of the 16-bit format; FwdGelu: A in fp32
     // Dx only: reduction rows k >= qsplit of Q come from Q2 (row k - qsplit), so
     // one launch can consume two weight tiles held in different ring slots.
     // qsplit = 0: no split.  Otherwise a multiple of the kernel's step (64).
@@ -43,9 +43,10 @@ hipError_t launch_gemm(GemmOp op, int dtype, const GemmArgs &a, hipStream_t stre
 // and bf16) that the forward GeLU epilogue reads; enqueued on `stream`.
 hipError_t build_gelu_tables(hipStream_t stream);
 
-// dA[i] = RNE(dH[i] * GeLU'(A[i])), i < count.
+// dA[i] = RNE(dH[i] * GeLU'(A[i])), i < count; with out_f32 the fp32 product
+// itself (dA then holds fp32 elements).
 hipError_t launch_gelu_bwd(int dtype, const float *dH, const void *A, void *dA, int64_t count,
-                           hipStream_t stream);
+                           bool out_f32, hipStream_t stream);
 
 // Macro-tile of the GEMM kernels (rows of p, columns of q per workgroup).
 constexpr int kTileP = 256;

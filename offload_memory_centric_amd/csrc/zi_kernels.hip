@@ -64,7 +64,9 @@ constexpr int kUnitBytes = 256 * BK * 2;        // 32 KiB: one operand, one step
 constexpr int kUnits = 5;                       // ring of operand units: 160 KiB of LDS
 constexpr int kLdsBytes = kUnits * kUnitBytes;
 
-enum Epi { EPI_LP = 0, EPI_F32 = 1, EPI_GELU = 2, EPI_ACC = 3 };
+// Epilogues: RNE to 16 bits; fp32; GeLU (A and H = GeLU(A) in 16 bits);
+// accumulate into fp32 C; GeLU with A kept in fp32 (H still from the 16-bit A).
+enum Epi { EPI_LP = 0, EPI_F32 = 1, EPI_GELU = 2, EPI_ACC = 3, EPI_GELU_F32A = 4 };
 
 __device__ __forceinline__ uint32_t lds_addr(const char *p) { return (uint32_t)(uintptr_t)p; }
 
@@ -612,7 +614,7 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue.
-    if constexpr (EPI == EPI_GELU) {
+    if constexpr (EPI == EPI_GELU || EPI == EPI_GELU_F32A) {
         // H = table[A]: the GeLU table of this type goes into the now idle LDS
         // (128 KiB: 32 one-KiB copies per wave).  Every wave's copies of the
         // main loop must have landed before the table overwrites the ring.
@@ -642,15 +644,18 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
             } else if constexpr (EPI == EPI_LP) {
                 u32x2 o = {bits16<T>(v[0]) | (bits16<T>(v[1]) << 16), bits16<T>(v[2]) | (bits16<T>(v[3]) << 16)};
                 *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.C) + off) = o;
-            } else {  // EPI_GELU: A = RNE(acc); H = RNE(GeLU(A)) from the table
+            } else {  // A = RNE(acc) (or acc itself in fp32); H = RNE(GeLU(RNE(acc))) from the table
                 uint32_t b[4], h[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     b[e] = bits16<T>(v[e]);
                     h[e] = gtab[b[e]];
                 }
-                *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.C) + off) =
-                    u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+                if constexpr (EPI == EPI_GELU)
+                    *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.C) + off) =
+                        u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+                else
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(a.C) + off) = v;
                 *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(a.C2) + off) =
                     u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
             }
@@ -660,29 +665,44 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
 
 // ---- dA = RNE(dH * GeLU'(A)) ----------------------------------------------------------
 
-template <typename T>
+// OUT_F32: dA is written as the fp32 product itself, the value the 16-bit
+// form rounds once.
+template <typename T, bool OUT_F32>
 __global__ __launch_bounds__(256) void gelu_bwd_kernel(const float *__restrict__ dH,
                                                        const uint16_t *__restrict__ A,
-                                                       uint16_t *__restrict__ dA, int64_t count) {
+                                                       void *__restrict__ dA, int64_t count) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x * 8;
+    uint16_t *dA16 = static_cast<uint16_t *>(dA);
+    float *dA32 = static_cast<float *>(dA);
     for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < count; i += stride) {
         if (i + 8 <= count) {
             const f32x4 g0 = *reinterpret_cast<const f32x4 *>(dH + i);
             const f32x4 g1 = *reinterpret_cast<const f32x4 *>(dH + i + 4);
             const u32x4 av = *reinterpret_cast<const u32x4 *>(A + i);
             const float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-            u32x4 o;
+            float r[8];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const float a0 = value16<T>(av[w] & 0xffffu);
-                const float a1 = value16<T>(av[w] >> 16);
-                o[w] = bits16<T>(g[2 * w] * gelu_grad_f32(a0)) |
-                       (bits16<T>(g[2 * w + 1] * gelu_grad_f32(a1)) << 16);
+                r[2 * w] = g[2 * w] * gelu_grad_f32(value16<T>(av[w] & 0xffffu));
+                r[2 * w + 1] = g[2 * w + 1] * gelu_grad_f32(value16<T>(av[w] >> 16));
             }
-            *reinterpret_cast<u32x4 *>(dA + i) = o;
+            if constexpr (OUT_F32) {
+                *reinterpret_cast<f32x4 *>(dA32 + i) = f32x4{r[0], r[1], r[2], r[3]};
+                *reinterpret_cast<f32x4 *>(dA32 + i + 4) = f32x4{r[4], r[5], r[6], r[7]};
+            } else {
+                u32x4 o;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) o[w] = bits16<T>(r[2 * w]) | (bits16<T>(r[2 * w + 1]) << 16);
+                *reinterpret_cast<u32x4 *>(dA16 + i) = o;
+            }
         } else {
-            for (int64_t e = i; e < count; ++e)
-                dA[e] = (uint16_t)bits16<T>(dH[e] * gelu_grad_f32(value16<T>(A[e])));
+            for (int64_t e = i; e < count; ++e) {
+                const float r = dH[e] * gelu_grad_f32(value16<T>(A[e]));
+                if constexpr (OUT_F32)
+                    dA32[e] = r;
+                else
+                    dA16[e] = (uint16_t)bits16<T>(r);
+            }
         }
     }
 }
@@ -711,7 +731,7 @@ hipError_t dispatch(GemmOp op, const GemmArgs &a, hipStream_t s) {
         case GemmOp::Fwd:
             return a.out_f32 ? run<T, false, false, EPI_F32>(a, s) : run<T, false, false, EPI_LP>(a, s);
         case GemmOp::FwdGelu:
-            return run<T, false, false, EPI_GELU>(a, s);
+            return a.out_f32 ? run<T, false, false, EPI_GELU_F32A>(a, s) : run<T, false, false, EPI_GELU>(a, s);
         case GemmOp::Dx:
             return run<T, true, false, EPI_ACC>(a, s);
         case GemmOp::Dw:
@@ -737,19 +757,21 @@ hipError_t build_gelu_tables(hipStream_t stream) {
 }
 
 hipError_t launch_gelu_bwd(int dtype, const float *dH, const void *A, void *dA, int64_t count,
-                           hipStream_t stream) {
+                           bool out_f32, hipStream_t stream) {
     if (count <= 0) return hipSuccess;
     const int64_t threads = (count + 7) / 8;
     int64_t blocks = (threads + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     const uint16_t *a16 = static_cast<const uint16_t *>(A);
-    uint16_t *d16 = static_cast<uint16_t *>(dA);
-    if (dtype == 1)
-        hipLaunchKernelGGL(gelu_bwd_kernel<_Float16>, dim3((unsigned)blocks), dim3(256), 0, stream, dH,
-                           a16, d16, count);
+    const dim3 g((unsigned)blocks), b(256);
+    if (dtype == 1 && !out_f32)
+        hipLaunchKernelGGL((gelu_bwd_kernel<_Float16, false>), g, b, 0, stream, dH, a16, dA, count);
+    else if (dtype == 1)
+        hipLaunchKernelGGL((gelu_bwd_kernel<_Float16, true>), g, b, 0, stream, dH, a16, dA, count);
+    else if (dtype == 2 && !out_f32)
+        hipLaunchKernelGGL((gelu_bwd_kernel<__bf16, false>), g, b, 0, stream, dH, a16, dA, count);
     else if (dtype == 2)
-        hipLaunchKernelGGL(gelu_bwd_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, stream, dH,
-                           a16, d16, count);
+        hipLaunchKernelGGL((gelu_bwd_kernel<__bf16, true>), g, b, 0, stream, dH, a16, dA, count);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

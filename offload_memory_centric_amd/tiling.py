@@ -130,8 +130,9 @@ class Context:
         zi.zi_tiled_linear_fwd(self.handle, plan.handle, X, Y)
 
     def fwd_gelu(self, plan: Plan, X, A, H):
+        """A = X W (RNE, or fp32 for an f32_out plan), H = RNE(GeLU(RNE(A)))."""
         _need(X, plan.T * plan.K, _lp(plan), "X")
-        _need(A, plan.T * plan.M, _lp(plan), "A")
+        _need(A, plan.T * plan.M, _out(plan), "A")
         _need(H, plan.T * plan.M, _lp(plan), "H")
         zi.zi_tiled_linear_fwd_gelu(self.handle, plan.handle, X, A, H)
 
@@ -154,11 +155,15 @@ class Context:
         zi.zi_tiled_linear_bwd_recompute(self.handle, plan.handle, X, dY, dX, Yr)
 
     def gelu_bwd(self, dtype: str, dH, A, dA, count: int):
+        """dA = RNE(dH * GeLU'(A)); an fp32 dA receives the product unrounded."""
         lp = (torch.float16,) if dtype == "f16" else (torch.bfloat16,)
         _need(dH, count, (torch.float32,), "dH")
         _need(A, count, lp, "A")
-        _need(dA, count, lp, "dA")
-        zi.zi_gelu_bwd(self.handle, zi.DTYPE_CODES[dtype], dH, A, dA, count)
+        _need(dA, count, lp + (torch.float32,), "dA")
+        if dA.dtype == torch.float32:
+            zi.zi_gelu_bwd_f32(self.handle, zi.DTYPE_CODES[dtype], dH, A, dA, count)
+        else:
+            zi.zi_gelu_bwd(self.handle, zi.DTYPE_CODES[dtype], dH, A, dA, count)
 
     def attach_adam(self, plan: Plan, adam: Optional["Adam"]):
         """Update each tile of `plan` on the host as its gradient lands (see Adam);

@@ -97,6 +97,20 @@ class zi_tier_stats(ctypes.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+ZI_STATS_KERNELS = 16
+
+
+class zi_kernel_stats(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 24), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("red", ctypes.c_int64), ("launches", ctypes.c_int64), ("ms", ctypes.c_double),
+                ("flops", ctypes.c_double), ("solo_launches", ctypes.c_int64), ("solo_ms", ctypes.c_double)]
+
+    def as_dict(self) -> dict:
+        d = {k: getattr(self, k) for k, _ in self._fields_}
+        d["name"] = bytes(self.name).split(b"\0", 1)[0].decode()
+        return d
+
+
 class zi_stats(ctypes.Structure):
     _fields_ = [("kind_count", ctypes.c_int32), ("kind_name", (ctypes.c_char * 24) * 8),
                 ("launches", ctypes.c_int64 * 8), ("kernel_ms", ctypes.c_double * 8),
@@ -104,7 +118,8 @@ class zi_stats(ctypes.Structure):
                 ("d2h_copies", ctypes.c_int64), ("h2d_ms", ctypes.c_double),
                 ("d2h_ms", ctypes.c_double), ("h2d_bytes", ctypes.c_double),
                 ("d2h_bytes", ctypes.c_double), ("span_ms", ctypes.c_double),
-                ("compute_busy_ms", ctypes.c_double)]
+                ("compute_busy_ms", ctypes.c_double), ("kernel_count", ctypes.c_int32),
+                ("kernel", zi_kernel_stats * ZI_STATS_KERNELS)]
 
     def as_dict(self):
         kinds = {}
@@ -114,7 +129,8 @@ class zi_stats(ctypes.Structure):
         return {"kinds": kinds, "h2d_copies": self.h2d_copies, "d2h_copies": self.d2h_copies,
                 "h2d_ms": self.h2d_ms, "d2h_ms": self.d2h_ms, "h2d_bytes": self.h2d_bytes,
                 "d2h_bytes": self.d2h_bytes, "span_ms": self.span_ms,
-                "compute_busy_ms": self.compute_busy_ms}
+                "compute_busy_ms": self.compute_busy_ms,
+                "kernels": [self.kernel[i].as_dict() for i in range(self.kernel_count)]}
 
 
 if not os.path.exists(LIB_PATH):
@@ -145,6 +161,7 @@ _sigs = {
     "zi_tiled_linear_bwd": (_S, [_P, _P, _P, _P, _P]),
     "zi_tiled_linear_bwd_recompute": (_S, [_P, _P, _P, _P, _P, _P]),
     "zi_gelu_bwd": (_S, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_int64]),
+    "zi_gelu_bwd_f32": (_S, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_int64]),
     "zi_sync": (_S, [_P]),
     "zi_ctx_set_timing": (_S, [_P, ctypes.c_int32]),
     "zi_ctx_set_debug": (_S, [_P, ctypes.c_uint32, ctypes.c_uint32]),
@@ -302,6 +319,10 @@ def zi_tiled_linear_bwd_recompute(ctx, plan, X, dY, dX, Yr) -> None:
 
 def zi_gelu_bwd(ctx, dtype: int, dH, A, dA, count: int) -> None:
     _check(_lib.zi_gelu_bwd(ctx, int(dtype), _ptr(dH), _ptr(A), _ptr(dA), int(count)))
+
+
+def zi_gelu_bwd_f32(ctx, dtype: int, dH, A, dA, count: int) -> None:
+    _check(_lib.zi_gelu_bwd_f32(ctx, int(dtype), _ptr(dH), _ptr(A), _ptr(dA), int(count)))
 
 
 def zi_stream_create() -> int:

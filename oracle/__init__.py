@@ -294,7 +294,9 @@ def ffn_fwd_bwd(X, W1t, W2t, dY, dtype: str, round_intermediates: bool = True) -
     dY [T x D2].  With ``round_intermediates`` the stored activations A, H and
     the stored gradient dA are rounded once (RNE) into ``dtype``, as the method
     stores them; dH stays unrounded (it is accumulated in fp32 across tiles).
-    Returns A, H (rounded values), Y, dH, dA (rounded), dX, dW1t, dW2t (fp64).
+    Returns A, H (rounded values), Y, dH, dA (rounded), dX, dW1t, dW2t (fp64),
+    and the two quantities the method rounds before storing them, unrounded:
+    A_exact = X W1 and dA_exact = dH * GeLU'(A) (with A the rounded value).
     """
     T, D = X.shape
     F = W1t.shape[0]
@@ -324,7 +326,7 @@ def ffn_fwd_bwd(X, W1t, W2t, dY, dtype: str, round_intermediates: bool = True) -
         dX = matmul_nt(dA_r, W1d_T)
         dW1t = matmul_nt(np.ascontiguousarray(dA_r.T), np.ascontiguousarray(Xd.T))
     return {"A": A_r, "H": H_r, "Y": Y, "dH": dH, "dA": dA_r,
-            "dX": dX, "dW1t": dW1t, "dW2t": dW2t}
+            "dX": dX, "dW1t": dW1t, "dW2t": dW2t, "A_exact": A, "dA_exact": dA}
 
 
 def ffn_sample(X, W1t, W2t, dY, dtype: str, t_rows, f_cols, d2_cols, d_cols,

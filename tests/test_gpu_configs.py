@@ -134,7 +134,7 @@ def test_ffn_first_matrix_two_tile_budget():
     assert torch.equal(Y1, Y2) and torch.equal(dX1, dX2) and torch.equal(dW1, dW2)
 
 
-def ffn_case(T, seed, nt=8, nf=16):
+def ffn_case(T, seed, nt=34, nf=18):
     D, F, N1, N2, d = 25600, 102400, 16, 16, 2
     release_pinned()
     tiling = lib()
@@ -168,10 +168,14 @@ def ffn_case(T, seed, nt=8, nf=16):
     assert torch.equal(A, A0) and torch.equal(H, H0), "recomputed activations differ"
     assert torch.equal(Y, Yr), "recomputed W2 product differs"
     say("  oracle on samples")
+    # every internal tile edge of both weights (i n - 1, i n) besides the
+    # random rows and columns, the first and the last
     t_rows = sample_indices(T, nt - 2, seed + 10)
-    f_cols = sample_indices(F, nf - 2, seed + 11, must=[6400 - 1, 6400, F - 6400])
-    d2_cols = sample_indices(D, nf - 2, seed + 12, must=[1600 - 1, 1600, D - 1600])
+    f_cols = sample_indices(F, nf - 2, seed + 11, must=tile_edges(F, F // N1))
+    d2_cols = sample_indices(D, nf - 2, seed + 12, must=tile_edges(D, D // N2))
     d_cols = sample_indices(D, nf - 2, seed + 13)
+    assert set(tile_edges(F, F // N1)) <= set(f_cols.tolist()) and len(t_rows) >= 32
+    assert set(tile_edges(D, D // N2)) <= set(d2_cols.tolist())
     ref = oracle.ffn_sample(host_bits(X), host_bits(W1t), host_bits(W2t), host_bits(dY), "f16",
                             t_rows, f_cols, d2_cols, d_cols, chunk=4096)
     tr, fc, d2c, dc = (torch.as_tensor(v) for v in (t_rows, f_cols, d2_cols, d_cols))
@@ -195,7 +199,17 @@ def test_ffn_block_T512():
     ffn_case(512, seed=40)
 
 
+def test_ffn_block_T2048():
+    say("case ffn block T=2048")
+    ffn_case(2048, seed=44)
+
+
+def test_ffn_block_T8192():
+    say("case ffn block T=8192")
+    ffn_case(8192, seed=48)
+
+
 def test_ffn_block_T32768_bench_configuration():
     # the benchmark's own configuration: T = 32768, N = 16 + 16, d = 2
     say("case ffn block T=32768")
-    ffn_case(32768, seed=50, nt=6, nf=10)
+    ffn_case(32768, seed=50)

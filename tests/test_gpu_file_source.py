@@ -1,6 +1,7 @@
 """The tiled path with its weights read from files (the NVMe tier), on the
-GPU: results bit-identical to the oracle's on exact inputs, and to the same
-passes fed from pinned host memory on Gaussian ones."""
+GPU: results bit-identical to the oracle's on exact inputs; on Gaussian ones
+bit-identical to the same passes fed from pinned host memory and within the
+2e-3 bar of the oracle."""
 import os
 
 import numpy as np
@@ -9,7 +10,7 @@ import torch
 
 import oracle
 from offload_memory_centric_amd import inputs
-from zi_testlib import host_bits, lib, make_linear_inputs, say
+from zi_testlib import assert_close, host_bits, lib, make_linear_inputs, say, values
 
 pytestmark = pytest.mark.gpu
 
@@ -156,6 +157,9 @@ def test_ffn_block_through_one_tier(tmp_path):
     keys = ("A", "H", "Y", "dH", "dA", "dX")
     ref = {k: b[k].clone() for k in keys}
     ref_dw = (host_bits(h["dW1t"]).copy(), host_bits(h["dW2t"]).copy())
+    # the oracle's block on the same weights, for the tier-fed steps below
+    r = oracle.ffn_fwd_bwd(host_bits(b["X"]), host_bits(h["W1t"]).copy(), host_bits(h["W2t"]).copy(),
+                           host_bits(b["dY"]), "f16")
     tier = tiling.Tier(staging=3, threads=2)
     s1 = tiling.FileSource(p1, weight_file(tmp_path, "w1.bin", h["W1t"]))
     s2 = tiling.FileSource(p2, weight_file(tmp_path, "w2.bin", h["W2t"]))
@@ -166,8 +170,13 @@ def test_ffn_block_through_one_tier(tmp_path):
     h["W1t"].zero_()
     h["W2t"].zero_()
 
-    def check(what):
+    def check(what, with_oracle=False):
         ctx.sync()
+        if with_oracle:  # the tier-fed outputs themselves against the oracle
+            for k in keys:
+                assert_close(values(b[k], "f16"), r[k], "%s %s" % (what, k))
+            assert_close(values(h["dW1t"], "f16"), r["dW1t"], what + " dW1")
+            assert_close(values(h["dW2t"], "f16"), r["dW2t"], what + " dW2")
         for k in keys:
             assert torch.equal(b[k], ref[k]), (what, k)
             b[k].zero_()
@@ -177,7 +186,7 @@ def test_ffn_block_through_one_tier(tmp_path):
     per_step = 3 * N1 + 2 * N2
     run_block(tiling, ctx, p1, p2, b)        # recorded, read on demand
     tier.step()
-    check("recorded step")
+    check("recorded step", with_oracle=True)
     st = tier.stats()
     say("  after the recorded step", st)
     # the recorded step is served on demand, or from a buffer that still holds the tile
@@ -193,7 +202,7 @@ def test_ffn_block_through_one_tier(tmp_path):
     for n in range(2):                       # replayed
         run_block(tiling, ctx, p1, p2, b)
         tier.step()
-        check("replayed step %d" % n)
+        check("replayed step %d" % n, with_oracle=(n == 1))
     st = tier.stats()
     say("  after two replayed steps", st)
     assert st["demand_reads"] == recorded_demand and st["restarts"] == 0
@@ -210,7 +219,7 @@ def test_ffn_block_through_one_tier(tmp_path):
     run_block(tiling, ctx, p1, p2, b, w2_first=True)
     run_block(tiling, ctx, p1, p2, b)
     tier.step()
-    check("step after an unpredicted pass")
+    check("step after an unpredicted pass", with_oracle=True)
     st = tier.stats()
     say("  at the end", st)
     assert st["restarts"] >= 2

@@ -59,6 +59,30 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str, tol: float = TOL):
     assert err <= tol * scale, "%s: max|err| %.3e > %.1e * max|ref| %.3e" % (what, err, tol, scale)
 
 
+def ulp(x: float, dtype: str) -> float:
+    """Spacing of the 16-bit format at |x| (its binade's unit in the last place)."""
+    mant = 10 if dtype == "f16" else 7
+    x = abs(float(x))
+    if x == 0.0:
+        return 0.0
+    return 2.0 ** (np.floor(np.log2(x)) - mant)
+
+
+def stored_tol(ref: np.ndarray, dtype: str, ulps: float) -> float:
+    """Relative bound for a value the method stores in 16 bits, compared with
+    the oracle's chain.  fp16: the 2e-3 bar (its half-ulp is at most 4.9e-4 of
+    the maximum).  bf16: 2e-3 for the fp32 arithmetic plus `ulps` units in the
+    last place at max|ref|: 1/2 for the method's own rounding of a value the
+    oracle keeps unrounded (Y, dW); 1 where both round the same quantity and
+    may take neighbouring values when it lies within the fp32 sum's error of a
+    rounding boundary (A); 1 + 1.13 where the input was such a neighbour too
+    (H = GeLU(A), |GeLU'| <= 1.13)."""
+    if dtype == "f16":
+        return TOL
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    return TOL + (ulps * ulp(scale, dtype) / scale if scale else 0.0)
+
+
 def make_linear_inputs(T, K, M, dtype, kind, seed, device="cuda", w_std=0.02, gen_device=None,
                        chunk_rows=0):
     """X [T,K] and dY [T,M] on `device`; W^t [M,K] in pinned host memory."""
