@@ -182,6 +182,113 @@ def link_peak_in_child():
     return json.loads(r.stdout.decode().strip().splitlines()[-1])
 
 
+class ClockSampler:
+    """Samples the shader clock (and board power, where the driver reports it)
+    every `period` seconds on a host thread, and notes when each marked step's
+    end event completes, so that every timed step gets the clock it ran at.
+    Reads the AMD SMI library when it is importable, else the driver's
+    pp_dpm_sclk file; with neither it records nothing."""
+
+    def __init__(self, period=0.02):
+        import threading
+        self.period = period
+        self.samples = []        # (host time, sclk MHz, power W or None)
+        self.ends = {}           # step index -> host time its end event was seen complete
+        self.events, self.recorded = [], 0
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = self._reader()
+
+    def _reader(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+
+            def read():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                clk = m.get("current_gfxclk")
+                if not isinstance(clk, (int, float)) or clk <= 0 or clk == 0xFFFF:
+                    clk = m.get("average_gfxclk_frequency")
+                pw = m.get("current_socket_power")
+                if not isinstance(pw, (int, float)) or pw <= 0 or pw == 0xFFFF:
+                    pw = m.get("average_socket_power")
+                return (float(clk) if isinstance(clk, (int, float)) else None,
+                        float(pw) if isinstance(pw, (int, float)) and pw != 0xFFFF else None)
+            read()
+            self.source = "amdsmi gpu_metrics (current_gfxclk, current_socket_power)"
+            return read
+        except Exception as e:  # no SMI library on this host: the driver's file
+            self.error = "amdsmi: %s" % (e,)
+        import glob
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            try:
+                open(path).read()
+            except OSError:
+                continue
+
+            def read(path=path):
+                for line in open(path):
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz")), None
+                return None, None
+            self.source = path
+            return read
+        self.source = None
+        return None
+
+    def watch(self, events):
+        """Step i ends at events[i + 1]; call recorded(i) after recording it."""
+        self.events = events
+        self.recorded = 0
+
+    def mark_recorded(self, n):
+        self.recorded = n
+
+    def _run(self):
+        while not self._stop.is_set():
+            t = time.perf_counter()
+            if self._read is not None:
+                try:
+                    clk, pw = self._read()
+                    self.samples.append((t, clk, pw))
+                except Exception as e:
+                    self.error = str(e)
+                    self._read = None
+            for j in range(1, self.recorded + 1):
+                if j not in self.ends and self.events[j].query():
+                    self.ends[j] = time.perf_counter()
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def per_step(self, t_start, n):
+        """Mean sclk and power over each step's host interval (step 0 from t_start)."""
+        out = []
+        prev = t_start
+        for j in range(1, n + 1):
+            end = self.ends.get(j)
+            if end is None:
+                out.append(None)
+                continue
+            sel = [x for x in self.samples if prev <= x[0] <= end]
+            clk = [x[1] for x in sel if x[1]]
+            pw = [x[2] for x in sel if x[2]]
+            out.append({"sclk_MHz": round(statistics.mean(clk), 1) if clk else None,
+                        "power_W": round(statistics.mean(pw), 1) if pw else None, "samples": len(sel)})
+            prev = end
+        return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -297,12 +404,16 @@ def main():
     # host synchronisation, so the ring's prefetch still crosses steps).
     comp = torch.cuda.ExternalStream(ctx.streams[0])
 
-    def marked(n):
+    def marked(n, sampler=None):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        if sampler is not None:
+            sampler.watch(ev)
         ev[0].record(comp)
         for i in range(n):
             step()
             ev[i + 1].record(comp)
+            if sampler is not None:
+                sampler.mark_recorded(i + 1)
         return ev
 
     def spans(ev):
@@ -319,13 +430,18 @@ def main():
     # ---------------- timed steps ----------------
     ctx.set_timing(True)
     ctx.reset_stats()
+    sampler = ClockSampler()
+    sampler.start()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    tev = marked(args.steps)
+    tev = marked(args.steps, sampler)
     ctx.sync()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    time.sleep(2 * sampler.period)  # the sampler notes the last step's end
+    sampler.stop()
     step_ms = spans(tev)
+    step_clock = sampler.per_step(t0, args.steps)
     st = ctx.stats()
     ctx.set_timing(False)
 
@@ -337,36 +453,48 @@ def main():
     d2h_rate = st["d2h_bytes"] / (st["d2h_ms"] * 1e-3) if st["d2h_ms"] > 0 else 0.0
 
     kinds = {k: v for k, v in st["kinds"].items() if v["launches"]}
-    dom = max(kinds.items(), key=lambda kv: kv[1]["ms"])
-    dom_name, dom_v = dom
-    avg_ms = dom_v["ms"] / dom_v["launches"]
-    flops_launch = dom_v["flops"] / dom_v["launches"]
-    achieved = flops_launch / (avg_ms * 1e-3) / 1e12
-    kernel_table = {k: {"launches": v["launches"], "avg_ms": v["ms"] / v["launches"],
-                        "total_ms_per_step": v["ms"] / args.steps,
-                        "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if k != "gelu_bwd" else None}
-                    for k, v in kinds.items()}
+    # Per kernel (product and launch shape).  A launch that another kernel
+    # overlapped (the two-stream forward passes) has a duration that includes
+    # the time the two shared the device; a kernel's own rate comes from the
+    # launches that ran alone, and its time per step is that rate applied to
+    # all of its launches.
+    kernel_table = []
+    for k in st["kernels"]:
+        fl = k["flops"] / k["launches"]
+        solo = k["solo_launches"] > 0
+        avg = (k["solo_ms"] / k["solo_launches"]) if solo else k["ms"] / k["launches"]
+        kernel_table.append({
+            "kernel": "%s %dx%dx%d" % (k["name"], k["rows"], k["cols"], k["red"]),
+            "launches": k["launches"], "solo_launches": k["solo_launches"],
+            "avg_ms": round(avg, 4), "avg_ms_all_launches": round(k["ms"] / k["launches"], 4),
+            "ms_per_step": round(avg * k["launches"] / args.steps, 3),
+            "tflops": round(fl / (avg * 1e-3) / 1e12, 1) if k["name"] != "gelu_bwd" else None,
+            "flops_per_launch": fl if k["name"] != "gelu_bwd" else None})
+    kernel_table.sort(key=lambda r: -r["ms_per_step"])
+    dom = next(r for r in kernel_table if r["flops_per_launch"])
+    achieved = dom["tflops"]
+    kinds_table = {k: {"launches": v["launches"], "avg_ms": v["ms"] / v["launches"],
+                       "total_ms_per_step": v["ms"] / args.steps}
+                   for k, v in kinds.items()}
 
-    # model prediction of the stall with the measured rates
+    # The hidden-tier rule with the measured rates: the step can go no faster
+    # than its kernels (the path's FLOPs over the time some kernel ran) or its
+    # host-to-device bytes over the measured link.
     pred = None
-    if link:
-        try:
-            R = sum(v["flops"] for k, v in kinds.items() if k != "gelu_bwd") / (
-                sum(v["ms"] for k, v in kinds.items() if k != "gelu_bwd") * 1e-3)
-            ait = flops_step / h2d_bytes_step
-            link_roof = ait * link["h2d_GBps"] * 1e9
-            # the step can go no faster than its products or its host-to-device bytes
-            attainable = min(R, link_roof)
-            pred = {"kernel_flop_rate_TFLOPs": R / 1e12,
-                    "link_h2d_GBps": link["h2d_GBps"],
-                    "balance_flop_per_byte": R / (link["h2d_GBps"] * 1e9),
-                    "ait_step_flop_per_h2d_byte": ait,
-                    "link_roofline_TFLOPs": link_roof / 1e12,
-                    "bound": "link" if link_roof < R else "mfma",
-                    "attainable_TFLOPs": attainable / 1e12,
-                    "frac_of_attainable": tflops * 1e12 / attainable}
-        except ZeroDivisionError:
-            pred = None
+    if link and busy_ms > 0:
+        R = flops_step * args.steps / (busy_ms * 1e-3)
+        ait = flops_step / h2d_bytes_step
+        link_roof = ait * link["h2d_GBps"] * 1e9
+        attainable = min(R, link_roof)
+        pred = {"kernel_flop_rate_TFLOPs": R / 1e12,
+                "kernel_rate_basis": "step FLOPs / union of the kernels' intervals",
+                "link_h2d_GBps": link["h2d_GBps"],
+                "balance_flop_per_byte": R / (link["h2d_GBps"] * 1e9),
+                "ait_step_flop_per_h2d_byte": ait,
+                "link_roofline_TFLOPs": link_roof / 1e12,
+                "bound": "link" if link_roof < R else "mfma",
+                "attainable_TFLOPs": attainable / 1e12,
+                "frac_of_attainable": tflops * 1e12 / attainable}
 
     result = {
         "metric": METRIC,
@@ -390,13 +518,19 @@ def main():
         "d2h_GBps_achieved": round(d2h_rate / 1e9, 2),
         "link_peak": link,
         "kernels": kernel_table,
+        "kinds": kinds_table,
         "model": pred,
-        "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 2),
+        "roofline": {"kernel": dom["kernel"], "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_MFMA_F16 / 1e12, "unit": "TFLOP/s",
                      "frac": round(achieved * 1e12 / PEAK_MFMA_F16, 4),
-                     "flops_per_launch": flops_launch, "avg_launch_ms": round(avg_ms, 4),
-                     "traffic": measured_traffic(config, dom_name)},
+                     "flops_per_launch": dom["flops_per_launch"], "avg_launch_ms": dom["avg_ms"],
+                     "launches_timed": dom["solo_launches"] or dom["launches"],
+                     "traffic": measured_traffic(config, dom["kernel"])},
+        "step_clock": {"source": sampler.source, "error": sampler.error, "per_step": step_clock},
     }
+    if config["workload"] == "ffn_block_fwd_recompute_bwd":
+        # the recomputed forward is work the step repeats; without it 7PT
+        result["useful_7PT_TFLOPs"] = round(tflops * 7.0 / 8.0, 3)
 
     if sources:
         result["nvme"] = nvme_report(args, tiling, sources, src_before, kinds, wall, flops_step * args.steps)
@@ -680,17 +814,24 @@ def _bits(torch, np, t):
 
 
 def cpu_baseline(args, np, torch, config, env):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+    """The oracle, as it stands, on a bounded sample of the same workload.
+
+    The sample runs on every host core the process may use; the weight decode
+    it pays (the oracle turns every 16-bit weight it reads into a double) is
+    then timed on its own with the same calls, so the products' rate can be
+    stated apart from it.  A second, smaller sample runs on one thread.  Both
+    rates are extrapolated to the whole step (labelled as extrapolated: the
+    oracle never runs the whole step here)."""
     import oracle
 
     oracle.set_threads(0)
     cores = oracle.get_threads()
     dtype = config["dtype"]
     t_start = time.perf_counter()
+    rng = np.random.default_rng(0)
     if config["workload"] == "ffn_block_fwd_recompute_bwd":
         X, dY, W1t, W2t = (_bits(torch, np, env[k]) for k in ("X", "dY", "W1t", "W2t"))
         T, D, F = config["T"], config["d_model"], config["d_ff"]
-        rng = np.random.default_rng(0)
         nt = 32
         nf = 64
         t_rows = np.sort(rng.choice(T, nt, replace=False))
@@ -706,6 +847,21 @@ def cpu_baseline(args, np, torch, config, env):
                        nf * T * (len(d2) + len(dc)))
         sample = ("oracle.ffn_sample: %d token row(s) through the whole block and %d hidden "
                   "column(s) over all %d tokens (%.3g FLOPs)" % (nt, nf, T, flops))
+        # the decode of both weights as the sample reads them (same calls, same chunks)
+        t1 = time.perf_counter()
+        for f0 in range(0, F, 4096):
+            fidx = np.arange(f0, min(F, f0 + 4096), dtype=np.int64)
+            oracle.gather(W1t, dtype, D, 1, fidx, F, None, D)
+            oracle.gather(W2t, dtype, 1, F, fidx, F, None, D)
+        decode_s = time.perf_counter() - t1
+        flops_step = 8.0 * D * F * 2 * T
+        # one thread: token rows of the up-projection over one tile's columns
+        one_rows = rng.choice(T, 16, replace=False)
+        one_cols = np.arange(F // 16)
+        one_flops = 2.0 * len(one_rows) * len(one_cols) * D
+        one_what = "oracle.linear_fwd_sample, 1 thread: %d token rows x %d columns of W1" % (
+            len(one_rows), len(one_cols))
+        one_args = (X, W1t, one_rows, one_cols)
     else:
         X, dY, Wt = (_bits(torch, np, env[k]) for k in ("X", "dY", "Wt"))
         T, K, M = config["T"], config["K"], config["M"]
@@ -715,9 +871,36 @@ def cpu_baseline(args, np, torch, config, env):
         secs = time.perf_counter() - t0
         flops = 2.0 * len(rows) * K * M
         sample = "oracle.linear_fwd_sample: %d rows x all %d columns (%.3g FLOPs)" % (len(rows), M, flops)
-    log("cpu baseline: %.1f s sample, %.1f s total" % (secs, time.perf_counter() - t_start))
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": sample, "seconds": round(secs, 2)}
+        t1 = time.perf_counter()
+        oracle.gather(Wt, dtype, K, 1, np.arange(M), M, None, K)
+        decode_s = time.perf_counter() - t1
+        flops_step = 6.0 * T * K * M
+        one_rows = rows[:4]
+        one_cols = np.arange(min(M, 4096))
+        one_flops = 2.0 * len(one_rows) * len(one_cols) * K
+        one_what = "oracle.linear_fwd_sample, 1 thread: %d rows x %d columns" % (len(one_rows), len(one_cols))
+        one_args = (X, Wt, one_rows, one_cols)
+    oracle.set_threads(1)
+    t2 = time.perf_counter()
+    oracle.linear_fwd_sample(*one_args, dtype)
+    one_s = time.perf_counter() - t2
+    oracle.set_threads(0)
+    prod_s = max(secs - decode_s, 1e-9)
+    log("cpu baseline: %.1f s sample (%.1f s of it weight decode), %.1f s one thread, %.1f s total" % (
+        secs, decode_s, one_s, time.perf_counter() - t_start))
+    rate, rate_prod, rate_one = flops / secs, flops / prod_s, one_flops / one_s
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds": round(secs, 2),
+            "decode_seconds": round(decode_s, 2),
+            "products_TFLOPs": rate_prod / 1e12,
+            "one_thread": {"value": rate_one / 1e12, "unit": "TFLOP/s", "cores": 1, "sample": one_what,
+                           "seconds": round(one_s, 2)},
+            "extrapolated_full_step_s": {
+                "note": "extrapolated from the sample rates, not run: step FLOPs / rate",
+                "step_flops": flops_step,
+                "all_cores": round(flops_step / rate, 1),
+                "all_cores_products_only": round(flops_step / rate_prod, 1),
+                "one_thread": round(flops_step / rate_one, 1)}}
 
 
 if __name__ == "__main__":
