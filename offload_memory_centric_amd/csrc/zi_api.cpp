@@ -117,6 +117,9 @@ namespace {
 uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
 zi_status hip_fail(zi_ctx *c, hipError_t e, const char *what) {
+    // the runtime also keeps the error as the thread's last one; take it, so
+    // that the caller's next, unrelated error check does not report it again
+    (void)hipGetLastError();
     char buf[400];
     snprintf(buf, sizeof(buf), "%s failed: %s (%d)", what, hipGetErrorString(e), (int)e);
     if (c && c->sticky == ZI_OK) {

@@ -686,6 +686,11 @@ __global__ __launch_bounds__(256) void gelu_bwd_kernel(const float *__restrict__
                 r[2 * w] = g[2 * w] * gelu_grad_f32(value16<T>(av[w] & 0xffffu));
                 r[2 * w + 1] = g[2 * w + 1] * gelu_grad_f32(value16<T>(av[w] >> 16));
             }
+            // the product is rounded to fp32 first and then, once, to 16 bits:
+            // kept from fusing into a mixed-precision multiply that would
+            // round the exact product straight to 16 bits
+#pragma unroll
+            for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(r[e]));
             if constexpr (OUT_F32) {
                 *reinterpret_cast<f32x4 *>(dA32 + i) = f32x4{r[0], r[1], r[2], r[3]};
                 *reinterpret_cast<f32x4 *>(dA32 + i + 4) = f32x4{r[4], r[5], r[6], r[7]};
@@ -697,7 +702,8 @@ __global__ __launch_bounds__(256) void gelu_bwd_kernel(const float *__restrict__
             }
         } else {
             for (int64_t e = i; e < count; ++e) {
-                const float r = dH[e] * gelu_grad_f32(value16<T>(A[e]));
+                float r = dH[e] * gelu_grad_f32(value16<T>(A[e]));
+                asm volatile("" : "+v"(r));
                 if constexpr (OUT_F32)
                     dA32[e] = r;
                 else

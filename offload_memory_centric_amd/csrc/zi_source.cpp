@@ -350,6 +350,7 @@ static zi_status tier_start(zi_tier *t) {
         void *p = nullptr;
         hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocDefault);
         if (e != hipSuccess) {
+            (void)hipGetLastError();  // not the caller's next error
             undo();
             return fail(ZI_ERR_HIP, "hipHostMalloc of a %llu B staging buffer: %s", (unsigned long long)bytes,
                         hipGetErrorString(e));

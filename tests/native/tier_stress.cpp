@@ -21,6 +21,7 @@ hipError_t hipEventCreateWithFlags(hipEvent_t *e, unsigned) { *e = (hipEvent_t)m
 hipError_t hipEventDestroy(hipEvent_t e) { free(e); return hipSuccess; }
 hipError_t hipEventSynchronize(hipEvent_t) { return hipSuccess; }
 const char *hipGetErrorString(hipError_t) { return "stub"; }
+hipError_t hipGetLastError() { return hipSuccess; }
 }
 namespace zi {
 zi_status fail(zi_status st, const char *fmt, ...) { va_list a; va_start(a, fmt); vfprintf(stderr, fmt, a); va_end(a); fprintf(stderr, "\n"); return st; }

@@ -76,25 +76,6 @@ def sampled_parity(T, K, M, N, dtype, X, Wt, dY, Y, dX, dWt, seed, tol=TOL):
     assert_close(vals(gdw), ref_dw, "dW", tol)
 
 
-def test_extreme_width_layer():
-    # hd = 65536 -> 262144: W and dW 32 GiB each in pinned host memory,
-    # N = 16 tiles of 2 GiB, T = 2048, d = 2
-    T, K, M, N, d = 2048, 65536, 262144, 16, 2
-    say("case extreme width: allocating 64 GiB pinned")
-    release_pinned()
-    from offload_memory_centric_amd import zi
-    try:
-        X, Wt, dY = big_linear(T, K, M, N, d, "f16", seed=2, chunk_rows=8192)
-        Y, dX, dWt, info = run_pass(T, K, M, N, d, "f16", X, Wt, dY)
-    except zi.ZiError as e:
-        if "out of memory" in str(e):
-            pytest.skip("the host could not pin 64 GiB for W and dW (%s)" % e)
-        raise
-    assert info.tile_bytes == 2 ** 31
-    say("case extreme width: sampled parity")
-    sampled_parity(T, K, M, N, "f16", X, Wt, dY, Y, dX, dWt, seed=300)
-
-
 def test_mid_ffn_up_projection_bf16():
     # X[4096x8192], W[8192x32768] bf16 (0.5 GB) pinned, N = 8 tiles of 4096, d = 2
     T, K, M, N, d = 4096, 8192, 32768, 8, 2

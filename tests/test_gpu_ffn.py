@@ -121,16 +121,24 @@ def test_ffn_block_small(dtype):
     assert_close(values(f["dW2t"], dtype), r["dW2t"], "dW2 fp32")
     # A's rounding is unique except where the exact product lies within the
     # fp32 sum's error of a rounding boundary; there the two sides may hold
-    # neighbouring values.  Where they agree, H is unique (bit-exact) and dA's
-    # fp32 product meets the bar; where they do not, A differs by one unit in
-    # the last place, and dA by at most |dH| max|GeLU''| |dA_in| (0.8 = GeLU''(0)).
+    # different values (several units apart where the sum nearly cancels and
+    # its fp32 error exceeds the 16-bit spacing of the tiny result).  Where
+    # they agree, H is unique (bit-exact) and dA's fp32 product meets the bar;
+    # where they do not, the fp32 A lies within the bound of any fp32 sum of K
+    # products, K 2^-24 sum_k |x_k w_k|, of the exact one, and dA within
+    # |dH| max|GeLU''| |dA_in| of the oracle's (0.8 = GeLU''(0)).
     a_gpu = host_bits(b["A"]).astype(np.int64)
     a_ref = oracle.encode(r["A"], dtype).astype(np.int64)
     same = a_gpu == a_ref
     nd = int((~same).sum())
-    say("  A: %d of %d elements take the neighbouring value" % (nd, same.size))
+    say("  A: %d of %d elements round to another 16-bit value than the oracle's" % (nd, same.size))
     assert nd <= max(4, same.size // 1000), nd
-    assert np.all(np.abs(a_gpu[~same] - a_ref[~same]) == 1), "A off by more than one unit"
+    if nd:
+        absx = np.abs(oracle.decode(host_bits(b["X"]), dtype))
+        absw = np.abs(oracle.decode(host_bits(h["W1t"]), dtype))
+        bound = D * 2.0 ** -24 * (absx @ absw.T)
+        a32 = values(f["A"], dtype)
+        assert np.all(np.abs(a32 - r["A_exact"])[~same] <= bound[~same]), "fp32 A beyond the sum's error"
     h_gpu = host_bits(b["H"])
     assert np.array_equal(h_gpu[same], oracle.encode(r["H"], dtype)[same]), "H differs where A agrees"
     dA32 = values(f["dA"], dtype)
