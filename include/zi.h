@@ -292,6 +292,30 @@ zi_status zi_gelu_bwd(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const voi
 zi_status zi_gelu_bwd_f32(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const void *A_dev,
                           float *dA_dev, int64_t count);
 
+/* The forward of zi_tiled_linear_fwd for callers that cannot allocate: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same products, same kernel, same tile order, same results as
+ * zi_tiled_linear_fwd (bit for bit), but with no context: each weight tile is
+ * copied into a static device buffer that the library owns (one per device,
+ * ZI_NOALLOC_SCRATCH_BYTES, held until the process ends) and multiplied
+ * there, every copy and product on `stream` (a hipStream_t of the current
+ * device, default priority, passed as void*; NULL: the null stream).  The call
+ * allocates nothing: no device or host memory, no events; its first call on a
+ * device looks up that device's buffer address once.
+ * The copies do not overlap the products (one stream, one buffer); the ring of
+ * a context is the overlapped form.  The caller passes X [T x K] and Y [T x M]
+ * (16-byte aligned device pointers) and a plan whose W_host is pinned; the
+ * plan's d, budget and dW_host are not used.  Returns at once; Y is complete
+ * when `stream` is.  Calls that overlap on one device (two streams, two host
+ * threads) share that device's buffer and race: serialise them.
+ * ZI_ERR_BUDGET when one tile exceeds ZI_NOALLOC_SCRATCH_BYTES (split W into
+ * more tiles), ZI_ERR_ARG / ZI_ERR_ALIGN on NULL or misaligned pointers,
+ * ZI_ERR_NOT_PINNED when W_host is not page-locked: all before anything is
+ * enqueued.  ZI_ERR_HIP when a copy or launch cannot be enqueued (earlier
+ * tiles may then be enqueued already). */
+#define ZI_NOALLOC_SCRATCH_BYTES (64ull << 20)
+zi_status zi_tiled_linear_fwd_noalloc(const zi_plan *plan, const void *X_dev, void *Y_dev, void *stream);
+
 /* Wait for everything enqueued on the context's three streams (and the
  * second product stream, if set) and for the host optimizers attached to it;
  * return the first error, which stays with the context (sticky).  The passes

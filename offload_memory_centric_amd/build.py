@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libzi.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
-SOURCES = ["zi_kernels.hip", "zi_api.cpp", "zi_plan.cpp", "zi_adam.cpp", "zi_source.cpp"]
+SOURCES = ["zi_kernels.hip", "zi_api.cpp", "zi_plan.cpp", "zi_adam.cpp", "zi_source.cpp", "zi_noalloc.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(ROOT, "include")]
 # Packed fp32 VALU forms are kept out of every device code object.

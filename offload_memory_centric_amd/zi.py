@@ -21,6 +21,7 @@ STATUS_NAMES = ["ZI_OK", "ZI_ERR_ARG", "ZI_ERR_SHAPE", "ZI_ERR_BUDGET", "ZI_ERR_
                 "ZI_ERR_ALIGN", "ZI_ERR_HIP", "ZI_ERR_STATE", "ZI_ERR_IO"]
 ZI_F16, ZI_BF16 = 1, 2
 ZI_FLAG_F32_OUT = 0x1
+ZI_NOALLOC_SCRATCH_BYTES = 64 << 20  # static tile buffer of zi_tiled_linear_fwd_noalloc
 DTYPE_CODES = {"f16": ZI_F16, "bf16": ZI_BF16}
 
 
@@ -162,6 +163,7 @@ _sigs = {
     "zi_tiled_linear_bwd_recompute": (_S, [_P, _P, _P, _P, _P, _P]),
     "zi_gelu_bwd": (_S, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_int64]),
     "zi_gelu_bwd_f32": (_S, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_int64]),
+    "zi_tiled_linear_fwd_noalloc": (_S, [_P, _P, _P, _P]),
     "zi_sync": (_S, [_P]),
     "zi_ctx_set_timing": (_S, [_P, ctypes.c_int32]),
     "zi_ctx_set_debug": (_S, [_P, ctypes.c_uint32, ctypes.c_uint32]),
@@ -315,6 +317,10 @@ def zi_tiled_linear_bwd(ctx, plan, X, dY, dX) -> None:
 
 def zi_tiled_linear_bwd_recompute(ctx, plan, X, dY, dX, Yr) -> None:
     _check(_lib.zi_tiled_linear_bwd_recompute(ctx, plan, _ptr(X), _ptr(dY), _ptr(dX), _ptr(Yr)))
+
+
+def zi_tiled_linear_fwd_noalloc(plan, X, Y, stream=None) -> None:
+    _check(_lib.zi_tiled_linear_fwd_noalloc(plan, _ptr(X), _ptr(Y), _stream(stream)))
 
 
 def zi_gelu_bwd(ctx, dtype: int, dH, A, dA, count: int) -> None:

@@ -139,6 +139,22 @@ def test_null_arguments_are_rejected_without_a_gpu(zi):
         assert f(*([None] * nargs)) == zi.ZI_ERR_ARG, name
     lib.zi_ctx_create.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64] + [ctypes.c_void_p] * 4
     assert lib.zi_ctx_create(None, None, 0, None, None, None, None) == zi.ZI_ERR_ARG
+    # the no-allocation forward checks its arguments and the tile against its
+    # static buffer before any HIP call (the pointers here are never read)
+    lib.zi_tiled_linear_fwd_noalloc.argtypes = [ctypes.c_void_p] * 4
+    assert lib.zi_tiled_linear_fwd_noalloc(None, None, None, None) == zi.ZI_ERR_ARG
+    big, _ = zi.zi_plan_tiles(zi.zi_problem(T=16, K=8192, M=16400, N=2, d=1, dtype=zi.ZI_F16, flags=0,
+                                            device_budget_bytes=0, W_host=None, dW_host=None))
+    fake = 1 << 40
+    assert lib.zi_tiled_linear_fwd_noalloc(big, None, fake, None) == zi.ZI_ERR_ARG
+    assert lib.zi_tiled_linear_fwd_noalloc(big, fake + 8, fake, None) == zi.ZI_ERR_ALIGN
+    assert lib.zi_tiled_linear_fwd_noalloc(big, fake, fake, None) == zi.ZI_ERR_BUDGET
+    assert "static tile buffer" in zi.zi_last_error()
+    fits, _ = zi.zi_plan_tiles(zi.zi_problem(T=16, K=8192, M=8192, N=2, d=1, dtype=zi.ZI_F16, flags=0,
+                                             device_budget_bytes=0, W_host=None, dW_host=None))
+    assert lib.zi_tiled_linear_fwd_noalloc(fits, fake, fake, None) == zi.ZI_ERR_ARG  # no W_host
+    zi.zi_plan_destroy(big)
+    zi.zi_plan_destroy(fits)
     lib.zi_stream_create.argtypes = [ctypes.c_void_p]
     assert lib.zi_stream_create(None) == zi.ZI_ERR_ARG
     lib.zi_copy_stream_create.argtypes = [ctypes.c_int32, ctypes.c_void_p]
