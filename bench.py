@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--K", type=int, default=None)
     ap.add_argument("--M", type=int, default=None)
     ap.add_argument("--N", type=int, default=None)
+    ap.add_argument("--budget-tiles", type=float, default=0.0,
+                    help="device budget of the tile buffers, in weight tiles (linear workload; "
+                         "0: no cap).  With a budget of 2 tiles the gradient forms in its weight "
+                         "tile's slot")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-link-peak", action="store_true")
     ap.add_argument("--link-peak-only", action="store_true",
@@ -372,7 +376,9 @@ def main():
         Wt = tiling.host_tensor((M, K), tdt)
         inputs.fill_(Wt, "gaussian", seed, "W", std=0.02, device="cuda", chunk_rows=4096)
         dWt = tiling.host_tensor((M, K), tdt)
-        p = tiling.Plan(T, K, M, N, d, dtype, Wt, dWt)
+        tile_bytes = K * (M // N) * 2
+        budget = int(args.budget_tiles * tile_bytes)
+        p = tiling.Plan(T, K, M, N, d, dtype, Wt, dWt, budget=budget)
         ctx = tiling.Context(p, **ctx_kw)
         Y = torch.empty((T, M), dtype=tdt, device="cuda")
         dX = torch.empty((T, K), dtype=torch.float32, device="cuda")
@@ -385,6 +391,9 @@ def main():
 
         config = {"workload": "tiled_linear_fwd_bwd", "T": T, "K": K, "M": M, "N": N, "n": M // N,
                   "d": d, "weights": "pinned host", "dtype": dtype}
+        if budget:
+            config.update({"budget_tiles": args.budget_tiles, "budget_bytes": budget,
+                           "gradient_slots": p.info.dw_slots, "ring_bytes": p.info.ring_bytes})
         plans = (p,)
     sources, tier = [], None
     if args.nvme:
@@ -866,13 +875,17 @@ def cpu_baseline(args, np, torch, config, env):
         X, dY, Wt = (_bits(torch, np, env[k]) for k in ("X", "dY", "Wt"))
         T, K, M = config["T"], config["K"], config["M"]
         rows = np.arange(0, T, max(1, T // 32))[:32]
+        # at most 16384 output columns: the oracle decodes every weight row it
+        # reads into doubles (a 32 GiB weight would take 137 GB)
+        cols = np.arange(min(M, 16384))
         t0 = time.perf_counter()
-        oracle.linear_fwd_sample(X, Wt, rows, np.arange(M), dtype)
+        oracle.linear_fwd_sample(X, Wt, rows, cols, dtype)
         secs = time.perf_counter() - t0
-        flops = 2.0 * len(rows) * K * M
-        sample = "oracle.linear_fwd_sample: %d rows x all %d columns (%.3g FLOPs)" % (len(rows), M, flops)
+        flops = 2.0 * len(rows) * K * len(cols)
+        sample = "oracle.linear_fwd_sample: %d rows x %d of the %d columns (%.3g FLOPs)" % (
+            len(rows), len(cols), M, flops)
         t1 = time.perf_counter()
-        oracle.gather(Wt, dtype, K, 1, np.arange(M), M, None, K)
+        oracle.gather(Wt, dtype, K, 1, cols, M, None, K)
         decode_s = time.perf_counter() - t1
         flops_step = 6.0 * T * K * M
         one_rows = rows[:4]
