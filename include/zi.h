@@ -105,6 +105,11 @@ typedef struct {
     double ait_bwd;            /* flops_bwd / h2d bytes  (= 2T) */
     double working_bytes_one;  /* layer bytes / N: one tile resident */
     double working_bytes_two;  /* twice that: one tile computing, one in flight */
+    int32_t fwd_tile[2];       /* output rows (of T) x columns (of n) one workgroup of the
+                                  forward product covers: 256 x 256, or 192 x 320 when
+                                  that covers the tile width with clearly less padding */
+    int32_t dw_tile[2];        /* the same for the gradient product dW_i^t [n x K]:
+                                  256 x 256, or 320 x 192 */
 } zi_plan_info;
 
 typedef struct zi_plan zi_plan; /* library-owned, immutable after creation */

@@ -324,7 +324,7 @@ zi_status run_fwd(zi_ctx *c, const zi_plan *p, const void *X, void *Y, void *H) 
     // Only tiles whose product takes a few waves of workgroups gain: with many
     // waves the partial last one is a small share (measured: 3.5 waves per
     // tile, -5 %; 12.5 waves, no change).
-    const int64_t wgs = ((pr.T + 255) / 256) * ((n + 255) / 256);
+    const int64_t wgs = gemm_workgroups(H ? GemmOp::FwdGelu : GemmOp::Fwd, pr.T, n);
     const bool two = c->comp2 && N > 1 && wgs < 8 * (int64_t)c->cus;
     if (two) {
         HIPCHK(c, hipEventRecord(c->fork, c->comp));

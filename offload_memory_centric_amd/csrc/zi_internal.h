@@ -39,6 +39,14 @@ struct GemmArgs {
 // dtype: 1 = fp16, 2 = bf16.  Returns the launch status (hipGetLastError).
 hipError_t launch_gemm(GemmOp op, int dtype, const GemmArgs &a, hipStream_t stream);
 
+// Workgroups (one macro-tile each) that launch_gemm runs for a product with
+// `rows` output rows and `cols` output columns: the macro-tile is 256 x 256,
+// or 192 x 320 / 320 x 192 (rows x columns) where that tile covers a forward's
+// columns or a gradient's rows with clearly less padding.
+int64_t gemm_workgroups(GemmOp op, int64_t rows, int64_t cols);
+// That macro-tile: output rows and columns of one workgroup.
+void gemm_tile(GemmOp op, int64_t rows, int64_t cols, int *tile_rows, int *tile_cols);
+
 // Builds the per-device tables H = RNE16(GeLU(A)) over every 16-bit A (fp16
 // and bf16) that the forward GeLU epilogue reads; enqueued on `stream`.
 hipError_t build_gelu_tables(hipStream_t stream);
@@ -48,9 +56,6 @@ hipError_t build_gelu_tables(hipStream_t stream);
 hipError_t launch_gelu_bwd(int dtype, const float *dH, const void *A, void *dA, int64_t count,
                            bool out_f32, hipStream_t stream);
 
-// Macro-tile of the GEMM kernels (rows of p, columns of q per workgroup).
-constexpr int kTileP = 256;
-constexpr int kTileQ = 256;
 // Reduction values per pipeline step of the GEMM kernels.
 constexpr int kGemmStep = 64;
 

@@ -60,9 +60,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int BK = kGemmStep;                        // reduction elements per step
-constexpr int kUnitBytes = 256 * BK * 2;        // 32 KiB: one operand, one step
-constexpr int kUnits = 5;                       // ring of operand units: 160 KiB of LDS
-constexpr int kLdsBytes = kUnits * kUnitBytes;
 
 // Epilogues: RNE to 16 bits; fp32; GeLU (A and H = GeLU(A) in 16 bits);
 // accumulate into fp32 C; GeLU with A kept in fp32 (H still from the 16-bit A).
@@ -113,19 +110,28 @@ __device__ __forceinline__ void copy16(rsrc_t rs, char *lds_block, uint32_t voff
 }
 #pragma clang diagnostic pop
 
-// Copy j (0..7) of wave w fills bytes [(8 w + j) * 1 KiB, +1 KiB) of an
-// operand unit; lane l writes the 16 bytes at offset 16 l of that block.
+// An operand unit holds one step (BK reduction values) of ROWS rows of an
+// operand: ROWS * BK * 2 bytes, filled by NCOPY = ROWS / 32 copies per wave.
+// Copy j of wave w fills bytes [(NCOPY w + j) * 1 KiB, +1 KiB) of the unit;
+// lane l writes the 16 bytes at offset 16 l of that block.  Each wave reads
+// the fragments of its half of the rows (WROWS = ROWS / 2: the workgroup's
+// four waves form 2 x 2 over the macro-tile).
 
 // Reduction-contiguous operand, element (r, k) at M[r * ld + k].  LDS rows of
 // 64 reduction values (128 B, eight 16-byte chunks); chunk c of row r sits at
 // c ^ ((r >> 1) & 7).  Eight lanes fetch one 128-byte row of global memory.
+template <int ROWS>
 struct RcOperand {
+    static constexpr int NCOPY = ROWS / 32;
+    static constexpr int WROWS = ROWS / 2;
+    static constexpr int UNIT = ROWS * BK * 2;
+    static_assert(ROWS % 64 == 0 && WROWS % 16 == 0, "rows come in 16-row fragments per wave");
     const char *base;  // &M[r0 * ld]
-    uint32_t voff[8];
+    uint32_t voff[NCOPY];
 
     __device__ __forceinline__ static int chunk_pos(int r, int c) { return c ^ ((r >> 1) & 7); }
     __device__ __forceinline__ static int chunk_of(int j, int wave, int lane) {
-        const int pos = (wave * 8 + j) * 1024 + lane * 16;
+        const int pos = (wave * NCOPY + j) * 1024 + lane * 16;
         return chunk_pos(pos >> 7, (pos >> 4) & 7);
     }
 
@@ -133,39 +139,39 @@ struct RcOperand {
                                          int wave, int lane) {
         base = reinterpret_cast<const char *>(M + r0 * ld);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = ((wave * 8 + j) * 1024 + lane * 16) >> 7;
+        for (int j = 0; j < NCOPY; ++j) {
+            const int r = ((wave * NCOPY + j) * 1024 + lane * 16) >> 7;
             voff[j] = (r0 + r < rext) ? (uint32_t)((r * ld + chunk_of(j, wave, lane) * 8) * 2) : kOOB;
         }
     }
 
-    // Copy j (0..7) of this wave for the step starting at reduction index k0.
+    // Copy j of this wave for the step starting at reduction index k0.
     // Chunks at or past the reduction length (a ragged last step, or a step
     // past the end) read as zero.
     __device__ __forceinline__ void issue(char *unit, int64_t k0, int64_t red, int wave, int lane, int j) {
         const rsrc_t rs = make_rsrc(base + k0 * 2);
         const bool ok = k0 + chunk_of(j, wave, lane) * 8 < red;
-        copy16(rs, unit + (wave * 8 + j) * 1024, ok ? voff[j] : kOOB);
+        copy16(rs, unit + (wave * NCOPY + j) * 1024, ok ? voff[j] : kOOB);
     }
 
     // The same when the reduction length is a multiple of BK: a whole step is
     // in range or (past the last unit) none of it, which the descriptor's
     // record count expresses without a per-lane select.
     __device__ __forceinline__ void issue_aligned(char *unit, int64_t k0, bool valid, int wave, int j) {
-        copy16(make_rsrc(base + k0 * 2, valid ? kNumRecords : 0u), unit + (wave * 8 + j) * 1024, voff[j]);
+        copy16(make_rsrc(base + k0 * 2, valid ? kNumRecords : 0u), unit + (wave * NCOPY + j) * 1024, voff[j]);
     }
 
-    // Fragment reads (v_mfma_f32_16x16x32).  Fragment f (0..7) of half ks
-    // (0, 1) of a step holds rows wq * 128 + 16 f + (lane & 15) and reduction
-    // values 32 ks + 8 (lane >> 4) .. +7: one 16-byte read.  Its address is the
+    // Fragment reads (v_mfma_f32_16x16x32).  Fragment f of half ks (0, 1) of
+    // a step holds rows wh * WROWS + 16 f + (lane & 15) and reduction values
+    // 32 ks + 8 (lane >> 4) .. +7: one 16-byte read.  Its address is the
     // unit's, plus a per-lane part that depends on ks only through the
     // swizzle (flo[ks], fixed for the kernel), plus 16 f rows (a constant).
     uint32_t flo[2];
-    __device__ __forceinline__ void init_reads(int wq, int lane) {
-        const int r = lane & 15;  // the swizzle sees r modulo 16
+    __device__ __forceinline__ void init_reads(int wh, int lane) {
+        const int r = lane & 15;  // the swizzle sees r modulo 16 (WROWS and 16 f are multiples of 16)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            flo[ks] = (uint32_t)((wq * 128 + r) * 128 + (chunk_pos(r, ks * 4 + (lane >> 4)) << 4));
+            flo[ks] = (uint32_t)((wh * WROWS + r) * 128 + (chunk_pos(r, ks * 4 + (lane >> 4)) << 4));
     }
     // Per-lane base of the reads of half ks in the unit at LDS address
     // `unit`: one add, hidden from the optimiser so that the constant parts of
@@ -182,17 +188,28 @@ struct RcOperand {
     }
 };
 
-// Reduction-strided operand, element (r, k) at M[k * ld + r].  LDS rows of 256
-// elements (512 B, sixteen 32-byte segments) per reduction index k; segment s
-// of row k sits at s ^ ((k & 3) | ((k >> 1) & 4)), so that the eight rows one
-// transposing read touches (k = 8 h + 4 t + 0..3 for two h) fall on eight
-// different bank groups.
+// Reduction-strided operand, element (r, k) at M[k * ld + r].  LDS rows of
+// ROWS elements (ROWB bytes, 32-byte segments) per reduction index k.  The
+// segments of row k are permuted so that the eight rows one transposing read
+// touches (k = 8 h + 4 t + 0..3 for two h) fall on eight different 32-byte
+// bank groups: with rows of a multiple of 256 bytes, segment s of row k sits
+// at s ^ ((k & 3) | ((k >> 1) & 4)); with rows of 128 bytes past such a
+// multiple (row k then starts half a bank period after row k - 1, which sets
+// bit 2 of the bank group from k's parity), at s ^ (((k >> 1) & 1) | ((k >> 2) & 2)).
+// Both permute within aligned groups of 8 (of 4) segments, so within a row.
+template <int ROWS>
 struct RsOperand {
+    static constexpr int NCOPY = ROWS / 32;
+    static constexpr int WROWS = ROWS / 2;
+    static constexpr int ROWB = ROWS * 2;
+    static constexpr int UNIT = ROWB * BK;
+    static_assert(ROWB % 256 == 0 || ROWB % 256 == 128, "row layouts of the swizzles above");
+    static_assert(WROWS % 16 == 0, "rows come in 16-row fragments per wave");
     const char *base;   // &M[r0]
     const char *base2;  // &M2[r0]: reduction rows from `split` on (split = 0: none)
     int64_t split;
     int64_t ldb;        // ld in bytes
-    uint32_t voff[8];
+    uint32_t voff[NCOPY];
 
     __device__ __forceinline__ void set_split(const void *M2, int64_t split_, int64_t r0) {
         split = M2 ? split_ : 0;
@@ -203,7 +220,12 @@ struct RsOperand {
         return (split && k0 >= split) ? base2 + (k0 - split) * ldb : base + k0 * ldb;
     }
 
-    __device__ __forceinline__ static int seg_pos(int k, int s) { return s ^ ((k & 3) | ((k >> 1) & 4)); }
+    __device__ __forceinline__ static int seg_pos(int k, int s) {
+        if constexpr (ROWB % 256 == 0)
+            return s ^ ((k & 3) | ((k >> 1) & 4));
+        else
+            return s ^ (((k >> 1) & 1) | ((k >> 2) & 2));
+    }
 
     __device__ __forceinline__ void init(const uint16_t *M, int64_t ld, int64_t r0, int64_t rext,
                                          int wave, int lane) {
@@ -212,48 +234,48 @@ struct RsOperand {
         split = 0;
         ldb = ld * 2;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int pos = (wave * 8 + j) * 1024 + lane * 16;
-            const int k = pos >> 9;                          // 512 B per LDS row
-            const int s = seg_pos(k, (pos >> 5) & 15);       // logical 32-byte segment
+        for (int j = 0; j < NCOPY; ++j) {
+            const int pos = (wave * NCOPY + j) * 1024 + lane * 16;
+            const int k = pos / ROWB;                        // LDS row
+            const int s = seg_pos(k, (pos % ROWB) >> 5);     // logical 32-byte segment
             const int r = s * 16 + ((pos >> 4) & 1) * 8;     // first of 8 elements
             voff[j] = (r0 + r < rext) ? (uint32_t)(k * ldb + r * 2) : kOOB;  // rext % 8 == 0
         }
     }
 
-    // Copy j (0..7) of this wave for the step starting at reduction index k0;
-    // rows at or past the reduction length read as zero.  Row k of the unit
-    // lies in bytes [k ldb, (k + 1) ldb) from row(k0), so a descriptor that
-    // ends after the last valid row cuts the rest off, with no per-lane select.
+    // Copy j of this wave for the step starting at reduction index k0; rows
+    // at or past the reduction length read as zero.  Row k of the unit lies
+    // in bytes [k ldb, (k + 1) ldb) from row(k0), so a descriptor that ends
+    // after the last valid row cuts the rest off, with no per-lane select.
     __device__ __forceinline__ void issue(char *unit, int64_t k0, int64_t red, int wave, int lane, int j) {
         (void)lane;
         const int64_t rem = red - k0;  // valid rows from k0 on (none past the end)
         const uint32_t records = rem <= 0 ? 0u : (rem >= kGemmStep ? kNumRecords : (uint32_t)(rem * ldb));
-        copy16(make_rsrc(row(k0), records), unit + (wave * 8 + j) * 1024, voff[j]);
+        copy16(make_rsrc(row(k0), records), unit + (wave * NCOPY + j) * 1024, voff[j]);
     }
 
     __device__ __forceinline__ void issue_aligned(char *unit, int64_t k0, bool valid, int wave, int j) {
-        copy16(make_rsrc(row(k0), valid ? kNumRecords : 0u), unit + (wave * 8 + j) * 1024, voff[j]);
+        copy16(make_rsrc(row(k0), valid ? kNumRecords : 0u), unit + (wave * NCOPY + j) * 1024, voff[j]);
     }
 
-    // Fragment reads (v_mfma_f32_16x16x32).  Fragment f (0..7) of half ks
-    // (0, 1) of a step holds columns wq * 128 + 16 f + (lane & 15) and reduction values
+    // Fragment reads (v_mfma_f32_16x16x32).  Fragment f of half ks (0, 1) of
+    // a step holds columns wh * WROWS + 16 f + (lane & 15) and reduction values
     // 32 ks + 8 (lane >> 4) .. +7: two transposing reads of 4 values each
     // (rows 0..3 and 4..7 of the lane's eight), issued together.  ds_read_b64_tr_b16 hands lane j
     // of each 16 the (j % 4)-th of the 4 values read by lanes 4e + j / 4
     // (e = 0..3); pointing those lanes at 4 consecutive rows x 4 four-column
     // groups gives lane j 4 consecutive reduction values of column j.  The
-    // swizzle mixes f into the per-lane address but not ks or t, so the
-    // address is the unit's plus flo[f] (fixed for the kernel) plus
-    // (32 ks + 4 t) rows of 512 bytes (a constant).
-    uint32_t flo[8];
-    __device__ __forceinline__ void init_reads(int wq, int lane) {
+    // permutation of segments depends on bits 0, 1 and 3 of k only, which
+    // 32 ks + 4 t does not change, so the address is the unit's plus flo[f]
+    // (fixed for the kernel) plus (32 ks + 4 t) rows of ROWB bytes (a constant).
+    uint32_t flo[WROWS / 16];
+    __device__ __forceinline__ void init_reads(int wh, int lane) {
         const int s = lane & 15;
         const int kl = 8 * (lane >> 4) + (s >> 2);
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
-            const int r = wq * 128 + f * 16 + 4 * (s & 3);
-            flo[f] = (uint32_t)(kl * 512 + (seg_pos(kl, r >> 4) << 5) + (r & 15) * 2);
+        for (int f = 0; f < WROWS / 16; ++f) {
+            const int r = wh * WROWS + f * 16 + 4 * (s & 3);
+            flo[f] = (uint32_t)(kl * ROWB + (seg_pos(kl, r >> 4) << 5) + (r & 15) * 2);
         }
     }
     // The reads of one fragment share a per-lane base, formed right before
@@ -268,9 +290,9 @@ struct RsOperand {
         uint32_t base = b.unit + flo[f];
         asm volatile("" : "+v"(base));
         const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(uintptr_t)(base + (32 * ks) * 512));
+            (__attribute__((address_space(3))) s16x4 *)(uintptr_t)(base + (32 * ks) * ROWB));
         const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(uintptr_t)(base + (32 * ks + 4) * 512));
+            (__attribute__((address_space(3))) s16x4 *)(uintptr_t)(base + (32 * ks + 4) * ROWB));
         const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
         out = u32x4{w0[0], w0[1], w1[0], w1[1]};
     }
@@ -280,8 +302,13 @@ struct RsOperand {
 // its LDS reads have returned, then meet the other waves.
 template <int n>
 __device__ __forceinline__ void wait_and_barrier() {
-    static_assert(n == 8, "the pipeline keeps one unit (8 copies per wave) in flight");
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    static_assert(n == 6 || n == 8 || n == 10, "the pipeline keeps one unit (n copies per wave) in flight");
+    if constexpr (n == 6)
+        asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (n == 8)
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ---- MFMA ------------------------------------------------------------------------
@@ -307,16 +334,15 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c);
 
 // A point that every write of the accumulators comes before and every read
 // after, with more than the longest XDL-result latency of wait states
-// (NOPS_FIRST: at its start, else at its end).  Eight volatile statements,
-// which keep their order, each tied to one row of accumulators.
-template <bool NOPS_FIRST>
-__device__ __forceinline__ void mfma_fence(f32x4 (&acc)[8][8]) {
+// (NOPS_FIRST: at its start, else at its end).  One volatile statement per
+// accumulator (volatile statements keep their order), each tied to it.
+template <bool NOPS_FIRST, int QB, int PB>
+__device__ __forceinline__ void mfma_fence(f32x4 (&acc)[QB][PB]) {
     if constexpr (NOPS_FIRST) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        asm volatile(""
-                     : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
-                       "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+    for (int i = 0; i < QB; ++i)
+#pragma unroll
+        for (int j = 0; j < PB; ++j) asm volatile("" : "+a"(acc[i][j]));
     if constexpr (!NOPS_FIRST) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
@@ -390,14 +416,16 @@ __device__ __forceinline__ float gelu_grad_f32(float a) {
 // ---- workgroup -> macro-tile ------------------------------------------------------
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
-// XCD w % 8).  When the tile count allows it, XCD x is given the contiguous
-// range of tiles [x * nt/8, (x+1) * nt/8), so the workgroups that share an L2
-// also share operand tiles; inside a range, tiles go in column groups 8
-// macro-rows tall (8 P tiles reuse one Q tile, 8 consecutive groups reuse P).
+// XCD w % 8, as its (w / 8)-th).  XCD x is given a contiguous range of tiles,
+// [x q + min(x, r), ...) of q + (x < r) tiles (nt = 8 q + r), so the
+// workgroups that share an L2 also share operand tiles; inside a range, tiles
+// go in column groups 8 macro-rows tall (8 P tiles reuse one Q tile, 8
+// consecutive groups reuse P).
 __device__ __forceinline__ void tile_coords(int w, int tiles_p, int tiles_q, int &tp, int &tq) {
     const int nt = tiles_p * tiles_q;
-    int t = w;
-    if ((nt & 7) == 0) t = (w & 7) * (nt >> 3) + (w >> 3);
+    const int x = w & 7, k = w >> 3;
+    const int q8 = nt >> 3, r8 = nt & 7;
+    const int t = x * q8 + min(x, r8) + k;
     constexpr int G = 8;
     const int per_group = G * tiles_q;
     const int g = t / per_group;
@@ -421,13 +449,49 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
-template <bool RS>
-using OperandT = typename std::conditional<RS, RsOperand, RcOperand>::type;
+template <bool RS, int ROWS>
+using OperandT = typename std::conditional<RS, RsOperand<ROWS>, RcOperand<ROWS>>::type;
 
-template <typename T, bool Q_RS, bool P_RS, int EPI, bool ALIGNED>
+// Position of copy k of the first half of a step's MFMAs (n copies spread
+// evenly over MFMAs 0 .. half - 1): MFMA (half (2 k + 1)) / (2 n).  Returns
+// the k whose copy follows MFMA m, or -1.
+template <int n, int half>
+__device__ constexpr int copy_at(int m) {
+    for (int k = 0; k < n; ++k)
+        if ((half * (2 * k + 1)) / (2 * n) == m) return k;
+    return -1;
+}
+
+// The macro-tile is (32 QB) columns of q by (32 PB) rows of p; each of the
+// four waves owns a (16 QB) x (16 PB) quarter: QB x PB blocks of 16 x 16, so
+// 4 QB PB fp32 accumulators per lane (at most 256: one wave per SIMD).
+//   (8, 8)   256 x 256, every product;
+//   (10, 6)  320 x 192, forward products whose q extent (the tile width) is
+//            a multiple of 320 but not of 256 (the down-projection's 1600);
+//   (6, 10)  192 x 320, gradient products whose p extent is such a width.
+template <typename T, bool Q_RS, bool P_RS, int EPI, bool ALIGNED, int QB, int PB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
-    __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+    constexpr int TQ = 32 * QB, TP = 32 * PB;
+    static_assert(QB * PB <= 64, "accumulators beyond the 256 AGPRs of a lane");
+    static_assert((EPI != EPI_ACC && EPI != EPI_GELU && EPI != EPI_GELU_F32A) || (QB == 8 && PB == 8),
+                  "the accumulating and GeLU epilogues are built for the 256 x 256 tile");
+    using QOp = OperandT<Q_RS, TQ>;
+    using POp = OperandT<P_RS, TP>;
+    // LDS ring.  Each step's two units are issued first-operand first; the
+    // pipeline keeps three first-operand units and two second-operand units
+    // alive (see the main loop), so the operand with the smaller unit goes
+    // first.  Equal units share one ring of five slots.
+    constexpr bool Q_FIRST = QOp::UNIT <= POp::UNIT;
+    constexpr int UF = Q_FIRST ? QOp::UNIT : POp::UNIT;
+    constexpr int US = Q_FIRST ? POp::UNIT : QOp::UNIT;
+    constexpr int NF = Q_FIRST ? QOp::NCOPY : POp::NCOPY;  // copies per wave of a first-operand unit
+    constexpr int NS = Q_FIRST ? POp::NCOPY : QOp::NCOPY;
+    constexpr bool MIXED = UF == US;
+    constexpr int LDS_BYTES = MIXED ? 5 * UF : 3 * UF + 2 * US;
+    static_assert(LDS_BYTES <= 160 * 1024, "the ring exceeds the LDS");
+    static_assert(EPI != EPI_GELU && EPI != EPI_GELU_F32A ? true : LDS_BYTES >= 65536 * 2, "GeLU table");
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -437,69 +501,77 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
 
     int tp, tq;
     tile_coords(blockIdx.x, tiles_p, tiles_q, tp, tq);
-    const int64_t p0 = (int64_t)tp * 256;
-    const int64_t q0 = (int64_t)tq * 256;
+    const int64_t p0 = (int64_t)tp * TP;
+    const int64_t q0 = (int64_t)tq * TQ;
 
-    OperandT<Q_RS> qo;
-    OperandT<P_RS> po;
+    QOp qo;
+    POp po;
     qo.init(static_cast<const uint16_t *>(a.Q), a.ldq, q0, a.cols, wave, lane);
     po.init(static_cast<const uint16_t *>(a.P), a.ldp, p0, a.rows, wave, lane);
     if constexpr (Q_RS) qo.set_split(a.Q2, a.qsplit, q0);
     qo.init_reads(wq, lane);
     po.init_reads(wp, lane);
 
-    // Operand units: Q of step s is unit 2s, P of step s is unit 2s + 1; unit
-    // u lives in slot u % kUnits.  Copies and fragment reads are spread evenly
-    // between the MFMAs, so that no wave stalls on a burst of copies while its
-    // matrix unit idles.
+    // Operand units: the first operand of step s is unit 2s, the second unit
+    // 2s + 1.  Copies and fragment reads are spread evenly between the
+    // MFMAs, so that no wave stalls on a burst of copies while its matrix
+    // unit idles.
     const int64_t ksteps = (a.red + BK - 1) / BK;
     const int64_t nunits = 2 * ksteps;
-    auto slot = [&](int64_t u) __attribute__((always_inline)) -> char * { return lds + ((uint32_t)u % kUnits) * kUnitBytes; };
-    // copy j of unit u into slot st (zeros past the last unit)
-    auto copy_to = [&](char *st, int64_t u, int j) __attribute__((always_inline)) {
-        const int64_t k0 = (u >> 1) * BK;
-        if constexpr (ALIGNED) {
-            const bool valid = u < nunits;
-            if (u & 1)
-                po.issue_aligned(st, k0, valid, wave, j);
-            else
-                qo.issue_aligned(st, k0, valid, wave, j);
+    auto slot = [&](int64_t u) __attribute__((always_inline)) -> char * {
+        if constexpr (MIXED) {
+            return lds + ((uint32_t)u % 5u) * UF;
         } else {
-            if (u & 1)
-                po.issue(st, k0, a.red, wave, lane, j);
-            else
-                qo.issue(st, k0, a.red, wave, lane, j);
+            const uint32_t st = (uint32_t)(u >> 1);
+            return (u & 1) ? lds + 3 * UF + (st & 1u) * US : lds + (st % 3u) * UF;
         }
     };
-    auto copy = [&](int64_t u, int j) __attribute__((always_inline)) { copy_to(slot(u), u, j); };
+    // copy j of unit u into its slot (zeros past the last unit)
+    auto copy = [&](int64_t u, int j) __attribute__((always_inline)) {
+        char *st = slot(u);
+        const int64_t k0 = (u >> 1) * BK;
+        const bool is_q = ((u & 1) == 0) == Q_FIRST;
+        if constexpr (ALIGNED) {
+            const bool valid = u < nunits;
+            if (is_q)
+                qo.issue_aligned(st, k0, valid, wave, j);
+            else
+                po.issue_aligned(st, k0, valid, wave, j);
+        } else {
+            if (is_q)
+                qo.issue(st, k0, a.red, wave, lane, j);
+            else
+                po.issue(st, k0, a.red, wave, lane, j);
+        }
+    };
+    auto qslot = [&](int64_t s) __attribute__((always_inline)) { return slot(2 * s + (Q_FIRST ? 0 : 1)); };
+    auto pslot = [&](int64_t s) __attribute__((always_inline)) { return slot(2 * s + (Q_FIRST ? 1 : 0)); };
 
-    using QOp = OperandT<Q_RS>;
-    using POp = OperandT<P_RS>;
-    using QB = typename QOp::Bases;
-    using PB = typename POp::Bases;
+    using QBs = typename QOp::Bases;
+    using PBs = typename POp::Bases;
 
     // acc[i][j]: the 16 x 16 block of q-block i and p-block j of this wave.
     // Register e of block (i, j) holds C[p][q] with
-    // p = p0 + wp 128 + 16 j + (lane & 15), q = q0 + wq 128 + 16 i + 4 (lane >> 4) + e.
+    // p = p0 + wp 16 PB + 16 j + (lane & 15), q = q0 + wq 16 QB + 16 i + 4 (lane >> 4) + e.
     // An accumulating product starts from C, so its epilogue is a plain
     // store.  C is loaded straight into the accumulator registers (every
     // lane, every block: out-of-range elements, and all of them when not
     // accumulating, come back as zeros from the buffer unit), issued before
     // the first operand copies, so the prologue's wait for the first two
-    // units (vmcnt counts loads in issue order) covers it too.  Row block j
-    // has its own descriptor, so a lane offset stays below 16 ldc + 256
-    // elements (the host keeps that under the descriptor's range).
-    const int64_t pb = p0 + wp * 128 + (lane & 15);
-    const int64_t qb = q0 + wq * 128 + 4 * (lane >> 4);
-    f32x4 acc[8][8];
+    // steps' units (vmcnt counts loads in issue order) covers it too.  Row
+    // block j has its own descriptor, so a lane offset stays below
+    // 16 ldc + 256 elements (the host keeps that under the descriptor's range).
+    const int64_t pb = p0 + wp * (16 * PB) + (lane & 15);
+    const int64_t qb = q0 + wq * (16 * QB) + 4 * (lane >> 4);
+    f32x4 acc[QB][PB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < PB; ++j) {
         if constexpr (EPI == EPI_ACC) {
-            const int64_t prow = p0 + wp * 128 + 16 * j;
+            const int64_t prow = p0 + wp * (16 * PB) + 16 * j;
             const rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(static_cast<const float *>(a.C) + prow * a.ldc + q0),
                                         a.accumulate ? kNumRecords : 0u);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < QB; ++i) {
                 const int64_t p = pb + j * 16, q = qb + i * 16;
                 const uint32_t off =
                     (p < a.rows && q < a.cols) ? (uint32_t)(((lane & 15) * a.ldc + (q - q0)) * 4) : kOOB;
@@ -507,50 +579,74 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i][j] = f32x4{};
+            for (int i = 0; i < QB; ++i) acc[i][j] = f32x4{};
         }
     }
 
-    // Fragments of one step (64 reduction values in two halves h = 0, 1):
-    // Q fragment (i, h) and P fragment (j, h).  Block (i, j) takes its two
-    // MFMAs back to back (h = 0, then h = 1), so the matrix core chains the
-    // second onto the first through its accumulator without a register-file
-    // round trip, which saves power (and so clock) under the board's limit.
-    // MFMA m of a step is block (i, j) = ((m / 2) / 8, (m / 2) % 8), half m % 2.
-    // Q row i is dead after MFMA 16 i + 15, so the next step's Q fragments of
-    // row i are read into the same registers right after it; Q row 7 and the P
-    // fragments are used to the end of the step and are double-buffered
-    // (parity `par` of the step).  P reads are spread over the first half.
-    u32x4 xq[7][2], xq7[2][2], xp[2][8][2];
-    // One step: 128 MFMAs; between them the reads of the next step (from
-    // the slots qs, ps) and 16 copies: copy_a(0..7) in the first half,
-    // copy_b(0..7) in the second.
+    // Fragments of one step (64 reduction values in two halves h = 0, 1).
+    // The MFMAs of a step run over the blocks row by row of the "row"
+    // operand (the one with more blocks per wave; Q on a tie) and, within a
+    // row, over the blocks of the "column" operand.  Block (i, j) takes its
+    // two MFMAs back to back (h = 0, then h = 1), so the matrix core chains
+    // the second onto the first through its accumulator without a
+    // register-file round trip, which saves power (and so clock) under the
+    // board's limit.  A row operand fragment is dead after its row's last
+    // MFMA, so the next step's fragments of that row are read into the same
+    // registers right after it; its last row and every column-operand
+    // fragment are used to the end of the step and are double-buffered
+    // (parity `par` of the step).  Column reads are spread over the first
+    // part of the step.
+    constexpr bool ROW_Q = QB >= PB;
+    constexpr int NR = ROW_Q ? QB : PB;  // rows of blocks
+    constexpr int NC = ROW_Q ? PB : QB;  // blocks per row
+    constexpr int NM = 2 * NR * NC;      // MFMAs per step
+    constexpr int MH = NM / 2;
+    u32x4 xr[NR - 1][2], xrl[2][2], xc[2][NC][2];
+    auto qfrag = [&](const QBs &b0, const QBs &b1, int h, int f, u32x4 &out) __attribute__((always_inline)) {
+        qo.frag(h ? b1 : b0, h, f, out);
+    };
+    auto pfrag = [&](const PBs &b0, const PBs &b1, int h, int f, u32x4 &out) __attribute__((always_inline)) {
+        po.frag(h ? b1 : b0, h, f, out);
+    };
+    // One step: NM MFMAs; between them the reads of the next step (from the
+    // slots qs, ps) and the copies: copy_a(0 .. NS-1) in the first half,
+    // copy_b(0 .. NF-1) in the second.
     auto step = [&](auto PAR, const char *qs, const char *ps, auto &&copy_a, auto &&copy_b) __attribute__((always_inline)) {
         constexpr int par = decltype(PAR)::value;
-        const QB qb0 = qo.bases(lds_addr(qs), 0), qb1 = qo.bases(lds_addr(qs), 1);
-        const PB pb0 = po.bases(lds_addr(ps), 0), pb1 = po.bases(lds_addr(ps), 1);
-        static_for<0, 128>([&](auto M_) __attribute__((always_inline)) {
+        const QBs qb0 = qo.bases(lds_addr(qs), 0), qb1 = qo.bases(lds_addr(qs), 1);
+        const PBs pb0 = po.bases(lds_addr(ps), 0), pb1 = po.bases(lds_addr(ps), 1);
+        auto rfrag = [&](int h, int f, u32x4 &out) __attribute__((always_inline)) {
+            if constexpr (ROW_Q) qfrag(qb0, qb1, h, f, out); else pfrag(pb0, pb1, h, f, out);
+        };
+        auto cfrag = [&](int h, int f, u32x4 &out) __attribute__((always_inline)) {
+            if constexpr (ROW_Q) pfrag(pb0, pb1, h, f, out); else qfrag(qb0, qb1, h, f, out);
+        };
+        static_for<0, NM>([&](auto M_) __attribute__((always_inline)) {
             constexpr int m = decltype(M_)::value;
-            constexpr int blk = m >> 1, h = m & 1, i = blk >> 3, j = blk & 7;
-            if constexpr (i < 7)
-                acc[i][j] = mfma16<T>(xq[i][h], xp[par][j][h], acc[i][j]);
-            else
-                acc[i][j] = mfma16<T>(xq7[par][h], xp[par][j][h], acc[i][j]);
-            if constexpr (m % 4 == 1 && m < 64) {  // P fragment (m / 8, (m / 4) % 2) of the next step
+            constexpr int blk = m >> 1, h = m & 1, r = blk / NC, c = blk % NC;
+            constexpr int i = ROW_Q ? r : c, j = ROW_Q ? c : r;
+            u32x4 &rf = (r < NR - 1) ? xr[r < NR - 1 ? r : 0][h] : xrl[par][h];
+            u32x4 &cf = xc[par][c][h];
+            (void)i;
+            (void)j;
+            acc[i][j] = mfma16<T>(ROW_Q ? rf : cf, ROW_Q ? cf : rf, acc[i][j]);
+            if constexpr (m % 4 == 1 && m < 8 * NC) {  // column fragment (m / 8, (m / 4) % 2) of the next step
                 constexpr int f = m / 8, hh = (m / 4) & 1;
-                po.frag(hh ? pb1 : pb0, hh, f, xp[par ^ 1][f][hh]);
+                cfrag(hh, f, xc[par ^ 1][f][hh]);
             }
-            if constexpr (m % 16 == 15 && m < 112) {  // Q row m / 16 of the next step
-                qo.frag(qb0, 0, m / 16, xq[m / 16][0]);
-                qo.frag(qb1, 1, m / 16, xq[m / 16][1]);
+            if constexpr ((m + 1) % (2 * NC) == 0 && m / (2 * NC) < NR - 1) {  // row m / (2 NC) of the next step
+                constexpr int row = m / (2 * NC);
+                rfrag(0, row, xr[row][0]);
+                rfrag(1, row, xr[row][1]);
             }
-            if constexpr (m == 66) qo.frag(qb0, 0, 7, xq7[par ^ 1][0]);
-            if constexpr (m == 70) qo.frag(qb1, 1, 7, xq7[par ^ 1][1]);
-            if constexpr (m % 8 == 4) {
-                if constexpr (m < 64)
-                    copy_a(m / 8);
-                else
-                    copy_b((m - 64) / 8);
+            if constexpr (m == MH + 2) rfrag(0, NR - 1, xrl[par ^ 1][0]);
+            if constexpr (m == MH + 6) rfrag(1, NR - 1, xrl[par ^ 1][1]);
+            if constexpr (m < MH) {
+                constexpr int k = copy_at<NS, MH>(m);
+                if constexpr (k >= 0) copy_a(k);
+            } else {
+                constexpr int k = copy_at<NF, MH>(m - MH);
+                if constexpr (k >= 0) copy_b(k);
             }
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -559,36 +655,42 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     using P1 = std::integral_constant<int, 1>;
 
     // Prologue: units 0..4 in flight (units past the last one read zeros);
-    // wait for units 0..3, read the fragments of step 0 from units 0 and 1.
+    // wait for units 0..3, read the fragments of step 0.
 #pragma unroll
-    for (int u = 0; u < 5; ++u)
+    for (int u = 0; u < 5; ++u) {
+        const bool first = (u & 1) == 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) copy(u, j);
-    wait_and_barrier<8>();
+        for (int j = 0; j < (first ? NF : NS); ++j) copy(u, j);
+    }
+    wait_and_barrier<NF>();
     {
-        const QB qb0 = qo.bases(lds_addr(slot(0)), 0), qb1 = qo.bases(lds_addr(slot(0)), 1);
-        const PB pb0 = po.bases(lds_addr(slot(1)), 0), pb1 = po.bases(lds_addr(slot(1)), 1);
+        const char *qs = qslot(0), *ps = pslot(0);
+        const QBs qb0 = qo.bases(lds_addr(qs), 0), qb1 = qo.bases(lds_addr(qs), 1);
+        const PBs pb0 = po.bases(lds_addr(ps), 0), pb1 = po.bases(lds_addr(ps), 1);
 #pragma unroll
-        for (int f = 0; f < 7; ++f) {
-            qo.frag(qb0, 0, f, xq[f][0]);
-            qo.frag(qb1, 1, f, xq[f][1]);
-        }
-        qo.frag(qb0, 0, 7, xq7[0][0]);
-        qo.frag(qb1, 1, 7, xq7[0][1]);
+        for (int f = 0; f < NR; ++f)
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
-            po.frag(pb0, 0, f, xp[0][f][0]);
-            po.frag(pb1, 1, f, xp[0][f][1]);
-        }
+            for (int h = 0; h < 2; ++h) {
+                u32x4 &dst = f < NR - 1 ? xr[f < NR - 1 ? f : 0][h] : xrl[0][h];
+                if constexpr (ROW_Q) qfrag(qb0, qb1, h, f, dst); else pfrag(pb0, pb1, h, f, dst);
+            }
+#pragma unroll
+        for (int f = 0; f < NC; ++f)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if constexpr (ROW_Q) pfrag(pb0, pb1, h, f, xc[0][f][h]); else qfrag(qb0, qb1, h, f, xc[0][f][h]);
+            }
     }
 
     mfma_fence<false>(acc);  // accumulator writes, then the first MFMA
 
     // Step s reads step s + 1 from units 2s + 2, 2s + 3 (landed), copies unit
-    // 2s + 5 under its first half (into the slot of unit 2s, read during step
-    // s - 1) and unit 2s + 6 under its second (slot of unit 2s + 1); at its
-    // end every wave has read units 2s + 2, 2s + 3, and units 2s + 4 and
-    // 2s + 5 must have landed (unit 2s + 6 may still be in flight).
+    // 2s + 5 (the second operand of step s + 2) under its first half, into
+    // the slot of step s's second operand, and unit 2s + 6 (the first operand
+    // of step s + 3) under its second half, into the slot of step s's first
+    // operand (both read during step s - 1); at its end every wave has read
+    // units 2s + 2, 2s + 3, and units 2s + 4 and 2s + 5 must have landed
+    // (unit 2s + 6 may still be in flight: NF copies per wave).
     //
     // Every MFMA sits in this loop, whose body is two steps (the register
     // parity).  With an odd step count its last pass runs one step past the
@@ -599,14 +701,14 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     const int64_t npairs = (ksteps + 1) / 2;
     for (int64_t t = 0; t < npairs; ++t) {
         const int64_t s0 = 2 * t, s1 = 2 * t + 1;
-        step(P0{}, slot(2 * s0 + 2), slot(2 * s0 + 3),
+        step(P0{}, qslot(s0 + 1), pslot(s0 + 1),
              [&](int c) __attribute__((always_inline)) { copy(2 * s0 + 5, c); },
              [&](int c) __attribute__((always_inline)) { copy(2 * s0 + 6, c); });
-        wait_and_barrier<8>();
-        step(P1{}, slot(2 * s1 + 2), slot(2 * s1 + 3),
+        wait_and_barrier<NF>();
+        step(P1{}, qslot(s1 + 1), pslot(s1 + 1),
              [&](int c) __attribute__((always_inline)) { copy(2 * s1 + 5, c); },
              [&](int c) __attribute__((always_inline)) { copy(2 * s1 + 6, c); });
-        wait_and_barrier<8>();
+        wait_and_barrier<NF>();
     }
     mfma_fence<true>(acc);  // the last MFMA, then accumulator reads
     // the copies past the last unit are still in flight: none may land after
@@ -630,11 +732,11 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     [[maybe_unused]] const __attribute__((address_space(3))) uint16_t *gtab =
         (const __attribute__((address_space(3))) uint16_t *)(uintptr_t)lds_addr(lds);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < QB; ++i) {
         const int64_t q = qb + i * 16;
         if (q >= a.cols) continue;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < PB; ++j) {
             const int64_t p = pb + j * 16;
             if (p >= a.rows) continue;
             f32x4 v = acc[i][j];
@@ -713,40 +815,88 @@ __global__ __launch_bounds__(256) void gelu_bwd_kernel(const float *__restrict__
     }
 }
 
-template <typename T, bool Q_RS, bool P_RS, int EPI>
-hipError_t run(const GemmArgs &a, hipStream_t s) {
-    const int tiles_p = (int)((a.rows + kTileP - 1) / kTileP);
-    const int tiles_q = (int)((a.cols + kTileQ - 1) / kTileQ);
+// Launch shapes (per-wave blocks of q, p).  A product takes the 256 x 256
+// tile unless a 320-wide tile covers its tile width (the forward's q extent,
+// the gradient's p extent) with clearly less padding: the down-projection's
+// 1600-column tiles fill 6.25 tiles of 256 but exactly 5 of 320.  (A 320 x 128
+// forward tile, which at T = 32768 would fill five whole rounds of workgroups
+// on 256 compute units where 320 x 192 leaves the fourth a third full, ran
+// 14 % slower: 80 MFMAs per step do not cover the step's barrier and copies.)
+enum Shape { SHAPE_8x8 = 0, SHAPE_10x6 = 1, SHAPE_6x10 = 2 };
+
+int64_t padded(int64_t x, int64_t t) { return (x + t - 1) / t * t; }
+
+Shape shape_for(GemmOp op, int64_t rows, int64_t cols) {
+    const int64_t a88 = padded(cols, 256) * padded(rows, 256);
+    if (op == GemmOp::Fwd) {
+        const int64_t a = padded(cols, 320) * padded(rows, 192);
+        if (a * 50 < a88 * 49) return SHAPE_10x6;
+    } else if (op == GemmOp::Dw) {
+        const int64_t a = padded(cols, 192) * padded(rows, 320);
+        if (a * 50 < a88 * 49) return SHAPE_6x10;
+    }
+    return SHAPE_8x8;
+}
+
+template <typename T, bool Q_RS, bool P_RS, int EPI, int QB, int PB>
+hipError_t run_shape(const GemmArgs &a, hipStream_t s) {
+    const int tiles_p = (int)((a.rows + 32 * PB - 1) / (32 * PB));
+    const int tiles_q = (int)((a.cols + 32 * QB - 1) / (32 * QB));
     const int64_t nt = (int64_t)tiles_p * tiles_q;
     if (nt <= 0) return hipSuccess;
     if (a.red < 1) return hipErrorInvalidValue;
     // the accumulating epilogue addresses 16 rows of C through one descriptor
     if (EPI == EPI_ACC && (a.ldc < 0 || (16 * a.ldc + 256) * 4 >= (int64_t)kNumRecords)) return hipErrorInvalidValue;
     if (a.red % BK == 0)
-        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, true>), dim3((unsigned)nt), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, true, QB, PB>), dim3((unsigned)nt), dim3(kThreads), 0, s,
                            a, tiles_p, tiles_q);
     else
-        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, false>), dim3((unsigned)nt), dim3(kThreads), 0, s,
-                           a, tiles_p, tiles_q);
+        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, false, QB, PB>), dim3((unsigned)nt), dim3(kThreads), 0,
+                           s, a, tiles_p, tiles_q);
     return hipGetLastError();
+}
+
+template <typename T, bool Q_RS, bool P_RS, int EPI>
+hipError_t run(GemmOp op, const GemmArgs &a, hipStream_t s) {
+    // the forward (both operands reduction-contiguous) may take 320 x 192,
+    // the gradient (both reduction-strided) 192 x 320
+    if constexpr ((EPI == EPI_LP || EPI == EPI_F32) && !Q_RS && !P_RS) {
+        if (shape_for(op, a.rows, a.cols) == SHAPE_10x6) return run_shape<T, Q_RS, P_RS, EPI, 10, 6>(a, s);
+    }
+    if constexpr ((EPI == EPI_LP || EPI == EPI_F32) && Q_RS && P_RS) {
+        if (shape_for(op, a.rows, a.cols) == SHAPE_6x10) return run_shape<T, Q_RS, P_RS, EPI, 6, 10>(a, s);
+    }
+    return run_shape<T, Q_RS, P_RS, EPI, 8, 8>(a, s);
 }
 
 template <typename T>
 hipError_t dispatch(GemmOp op, const GemmArgs &a, hipStream_t s) {
     switch (op) {
         case GemmOp::Fwd:
-            return a.out_f32 ? run<T, false, false, EPI_F32>(a, s) : run<T, false, false, EPI_LP>(a, s);
+            return a.out_f32 ? run<T, false, false, EPI_F32>(op, a, s) : run<T, false, false, EPI_LP>(op, a, s);
         case GemmOp::FwdGelu:
-            return a.out_f32 ? run<T, false, false, EPI_GELU_F32A>(a, s) : run<T, false, false, EPI_GELU>(a, s);
+            return a.out_f32 ? run<T, false, false, EPI_GELU_F32A>(op, a, s) : run<T, false, false, EPI_GELU>(op, a, s);
         case GemmOp::Dx:
-            return run<T, true, false, EPI_ACC>(a, s);
+            return run<T, true, false, EPI_ACC>(op, a, s);
         case GemmOp::Dw:
-            return a.out_f32 ? run<T, true, true, EPI_F32>(a, s) : run<T, true, true, EPI_LP>(a, s);
+            return a.out_f32 ? run<T, true, true, EPI_F32>(op, a, s) : run<T, true, true, EPI_LP>(op, a, s);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+void gemm_tile(GemmOp op, int64_t rows, int64_t cols, int *tile_rows, int *tile_cols) {
+    const Shape sh = (op == GemmOp::Fwd || op == GemmOp::Dw) ? shape_for(op, rows, cols) : SHAPE_8x8;
+    *tile_cols = sh == SHAPE_10x6 ? 320 : (sh == SHAPE_6x10 ? 192 : 256);
+    *tile_rows = sh == SHAPE_10x6 ? 192 : (sh == SHAPE_6x10 ? 320 : 256);
+}
+
+int64_t gemm_workgroups(GemmOp op, int64_t rows, int64_t cols) {
+    int tp = 256, tq = 256;
+    gemm_tile(op, rows, cols, &tp, &tq);
+    return ((rows + tp - 1) / tp) * ((cols + tq - 1) / tq);
+}
 
 hipError_t launch_gemm(GemmOp op, int dtype, const GemmArgs &a, hipStream_t stream) {
     if (dtype == 1) return dispatch<_Float16>(op, a, stream);

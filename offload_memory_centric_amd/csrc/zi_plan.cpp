@@ -13,6 +13,7 @@
 
 #include "../../include/zi.h"
 #include "zi_host.h"
+#include "zi_internal.h"
 
 namespace zi {
 
@@ -81,6 +82,8 @@ zi_status plan_validate_and_fill(const zi_problem *p, zi_plan_info *info, bool w
     o.ait_bwd = o.flops_bwd / o.h2d_bytes_pass;
     o.working_bytes_one = o.h2d_bytes_pass / (double)p->N;
     o.working_bytes_two = 2.0 * o.working_bytes_one;
+    gemm_tile(GemmOp::Fwd, p->T, n, &o.fwd_tile[0], &o.fwd_tile[1]);
+    gemm_tile(GemmOp::Dw, n, p->K, &o.dw_tile[0], &o.dw_tile[1]);
     *info = o;
     return ZI_OK;
 }

@@ -46,7 +46,8 @@ class zi_plan_info(ctypes.Structure):
                 ("flops_fwd", ctypes.c_double), ("flops_bwd", ctypes.c_double),
                 ("h2d_bytes_pass", ctypes.c_double), ("d2h_bytes_bwd", ctypes.c_double),
                 ("ait_fwd", ctypes.c_double), ("ait_bwd", ctypes.c_double),
-                ("working_bytes_one", ctypes.c_double), ("working_bytes_two", ctypes.c_double)]
+                ("working_bytes_one", ctypes.c_double), ("working_bytes_two", ctypes.c_double),
+                ("fwd_tile", ctypes.c_int32 * 2), ("dw_tile", ctypes.c_int32 * 2)]
 
 
 class zi_prediction(ctypes.Structure):

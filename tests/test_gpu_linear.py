@@ -373,3 +373,42 @@ def test_small_workspace_rejected():
     with pytest.raises(zi.ZiError) as e:
         tiling.Context(plan, workspace_bytes=plan.info.ring_bytes - 256)
     assert e.value.status == zi.ZI_ERR_BUDGET
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,K,M,N,d,fwd_rows", [(380, 584, 3200, 2, 2, 192), (700, 576, 1920, 2, 1, 192),
+                                                (32, 1600, 1600, 1, 1, 192), (7200, 128, 1600, 1, 1, 192)])
+def test_320_wide_tiles_bit_exact(dtype, T, K, M, N, d, fwd_rows):
+    # tile widths that 320 divides and 256 does not: the forward runs 192 x 320
+    # workgroup tiles, the gradient 320 x 192 (both checked in the
+    # plan), with ragged rows (T = 380, 700, 7200), a reduction that is not a
+    # multiple of the 64-value step (K = 584, T = 380, 7200) or an odd number
+    # of steps (K = 576: 9); small integers, so every result is unique
+    # (|dW| <= 9 T stays below fp16's 65504)
+    say("case 320-wide tiles", dtype, T, K, M, N, d)
+    tiling = lib()
+    X, Wt, dY = make_linear_inputs(T, K, M, dtype, "small_int", seed=13)
+    info = tiling.Plan(T, K, M, N, d, dtype, None).info
+    assert tuple(info.fwd_tile) == (fwd_rows, 320) and tuple(info.dw_tile) == (320, 192)
+    r = run_fwd_bwd(T, K, M, N, d, dtype, X, Wt, dY)
+    Y, dX, dWt = oracle_linear(X, Wt, dY, dtype)
+    assert np.array_equal(host_bits(r["Y"]), oracle.encode(Y, dtype)), "Y bits"
+    assert np.array_equal(r["dX"].cpu().numpy().astype(np.float64), dX), "dX exact"
+    assert np.array_equal(host_bits(r["dWt"]), oracle.encode(dWt, dtype)), "dW bits"
+
+
+def test_320_wide_tiles_gaussian_bf16():
+    # the same shapes on Gaussian values: the fp32 epilogues at the 2e-3 bar
+    # and the bf16 results one RNE rounding of them
+    T, K, M, N, d = 380, 584, 3200, 2, 2
+    say("case 320-wide tiles gaussian bf16")
+    X, Wt, dY = make_linear_inputs(T, K, M, "bf16", "gaussian", seed=14)
+    r32 = run_fwd_bwd(T, K, M, N, d, "bf16", X, Wt, dY, f32_out=True)
+    r16 = run_fwd_bwd(T, K, M, N, d, "bf16", X, Wt, dY)
+    Y, dX, dWt = oracle_linear(X, Wt, dY, "bf16")
+    assert_close(values(r32["Y"], "bf16"), Y, "Y fp32")
+    assert_close(values(r32["dX"], "bf16"), dX, "dX")
+    assert_close(values(r32["dWt"], "bf16"), dWt, "dW fp32")
+    assert torch.equal(r16["Y"], r32["Y"].to(torch.bfloat16))
+    assert torch.equal(r16["dWt"], r32["dWt"].to(torch.bfloat16))
+    assert torch.equal(r16["dX"], r32["dX"])

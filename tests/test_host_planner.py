@@ -355,3 +355,21 @@ def test_choice_errors(zi):
         zi.zi_plan_choose(_problem(zi, T, 8190, M, "f16", 0), [4096], [1e15], h2d_bytes_per_s=5e10,
                           d2h_bytes_per_s=5e10)
     assert e.value.status == zi.ZI_ERR_SHAPE
+
+
+def test_macro_tile_choice(zi):
+    # 320-wide workgroup tiles where the tile width is a multiple of 320 but not
+    # of 256 (the down-projection's 1600-column tiles: 5 tiles of 320 against
+    # 6.25 of 256); 256 x 256 wherever that pads less
+    def tiles(T, K, M, N):
+        _, info = zi.zi_plan_tiles(zi.zi_problem(T=T, K=K, M=M, N=N, d=2, dtype=zi.ZI_F16, flags=0,
+                                                 device_budget_bytes=0, W_host=None, dW_host=None), False)
+        return tuple(info.fwd_tile), tuple(info.dw_tile)
+    assert tiles(32768, 102400, 25600, 16) == ((192, 320), (320, 192))  # down-projection, n = 1600
+    assert tiles(8192, 102400, 25600, 16) == ((192, 320), (320, 192))
+    assert tiles(32768, 25600, 102400, 16) == ((256, 256), (256, 256))  # up-projection, n = 6400
+    assert tiles(4096, 8192, 32768, 8) == ((256, 256), (256, 256))      # n = 4096
+    assert tiles(4096, 25600, 102400, 16) == ((256, 256), (256, 256))
+    assert tiles(2048, 65536, 262144, 16) == ((256, 256), (256, 256))
+    assert tiles(380, 584, 3200, 2) == ((192, 320), (320, 192))
+    assert tiles(7200, 128, 1600, 1) == ((192, 320), (320, 192))
