@@ -87,6 +87,9 @@ def parse():
                          "the block's down-projection between 800 and 6400 columns)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain streaming kernel of known size (HBM counter calibration)")
+    ap.add_argument("--summarize-trace", type=str, default=None, metavar="DIR",
+                    help="summarise the rocprofv3 CSV output under DIR (kernel trace and/or counter "
+                         "collection) per kernel and grid size, and exit (no GPU needed)")
     return ap.parse_args()
 
 
@@ -187,22 +190,33 @@ def link_peak_in_child():
 
 
 class ClockSampler:
-    """Samples the shader clock (and board power, where the driver reports it)
+    """Samples the GPU's clocks, power, temperatures and throttle counters
     every `period` seconds on a host thread, and notes when each marked step's
-    end event completes, so that every timed step gets the clock it ran at.
-    Reads the AMD SMI library when it is importable, else the driver's
-    pp_dpm_sclk file; with neither it records nothing."""
+    end event completes, so that every timed step gets the conditions it ran
+    at.  Reads the AMD SMI library's GPU metrics when it is importable, else
+    only the shader clock from the driver's pp_dpm_sclk file."""
+
+    # gpu_metrics fields kept per sample (means per step) ...
+    LEVELS = ("current_gfxclk", "current_uclk", "current_socket_power", "temperature_hotspot", "temperature_mem")
+    # ... and accumulators whose increase over a step, over that of
+    # accumulation_counter, is the share of the step spent in that state
+    RESIDENCY = ("ppt_residency_acc", "socket_thm_residency_acc", "hbm_thm_residency_acc",
+                 "vr_thm_residency_acc", "prochot_residency_acc")
 
     def __init__(self, period=0.02):
         import threading
         self.period = period
-        self.samples = []        # (host time, sclk MHz, power W or None)
+        self.samples = []        # (host time, {field: value})
         self.ends = {}           # step index -> host time its end event was seen complete
         self.events, self.recorded = [], 0
         self.error = None
         self._stop = threading.Event()
         self._thread = None
         self._read = self._reader()
+
+    @staticmethod
+    def _num(v):
+        return float(v) if isinstance(v, (int, float)) and v not in (0xFFFF, 0xFFFFFFFF) and v >= 0 else None
 
     def _reader(self):
         try:
@@ -212,16 +226,14 @@ class ClockSampler:
 
             def read():
                 m = amdsmi.amdsmi_get_gpu_metrics_info(h)
-                clk = m.get("current_gfxclk")
-                if not isinstance(clk, (int, float)) or clk <= 0 or clk == 0xFFFF:
-                    clk = m.get("average_gfxclk_frequency")
-                pw = m.get("current_socket_power")
-                if not isinstance(pw, (int, float)) or pw <= 0 or pw == 0xFFFF:
-                    pw = m.get("average_socket_power")
-                return (float(clk) if isinstance(clk, (int, float)) else None,
-                        float(pw) if isinstance(pw, (int, float)) and pw != 0xFFFF else None)
+                out = {k: self._num(m.get(k)) for k in self.LEVELS + self.RESIDENCY + ("accumulation_counter",)}
+                xcc = [self._num(x) for x in (m.get("current_gfxclks") or [])]
+                xcc = [x for x in xcc if x]
+                if xcc:
+                    out["gfxclk_min_xcc"], out["gfxclk_max_xcc"] = min(xcc), max(xcc)
+                return out
             read()
-            self.source = "amdsmi gpu_metrics (current_gfxclk, current_socket_power)"
+            self.source = "amdsmi gpu_metrics"
             return read
         except Exception as e:  # no SMI library on this host: the driver's file
             self.error = "amdsmi: %s" % (e,)
@@ -235,15 +247,15 @@ class ClockSampler:
             def read(path=path):
                 for line in open(path):
                     if line.rstrip().endswith("*"):
-                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz")), None
-                return None, None
+                        return {"current_gfxclk": float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))}
+                return {}
             self.source = path
             return read
         self.source = None
         return None
 
     def watch(self, events):
-        """Step i ends at events[i + 1]; call recorded(i) after recording it."""
+        """Step i ends at events[i + 1]; call mark_recorded(i + 1) after recording it."""
         self.events = events
         self.recorded = 0
 
@@ -255,8 +267,7 @@ class ClockSampler:
             t = time.perf_counter()
             if self._read is not None:
                 try:
-                    clk, pw = self._read()
-                    self.samples.append((t, clk, pw))
+                    self.samples.append((t, self._read()))
                 except Exception as e:
                     self.error = str(e)
                     self._read = None
@@ -276,25 +287,40 @@ class ClockSampler:
             self._thread.join()
 
     def per_step(self, t_start, n):
-        """Mean sclk and power over each step's host interval (step 0 from t_start)."""
+        """Per step (step 0 from t_start): mean shader clock (and the slowest
+        and fastest XCC's), memory clock, power and temperatures over the
+        step's samples, and the share of the step each throttle state held."""
         out = []
         prev = t_start
+        names = {"current_gfxclk": "sclk_MHz", "gfxclk_min_xcc": "sclk_min_xcc_MHz",
+                 "gfxclk_max_xcc": "sclk_max_xcc_MHz", "current_uclk": "mclk_MHz",
+                 "current_socket_power": "power_W", "temperature_hotspot": "hotspot_C",
+                 "temperature_mem": "hbm_C"}
         for j in range(1, n + 1):
             end = self.ends.get(j)
             if end is None:
                 out.append(None)
                 continue
-            sel = [x for x in self.samples if prev <= x[0] <= end]
-            clk = [x[1] for x in sel if x[1]]
-            pw = [x[2] for x in sel if x[2]]
-            out.append({"sclk_MHz": round(statistics.mean(clk), 1) if clk else None,
-                        "power_W": round(statistics.mean(pw), 1) if pw else None, "samples": len(sel)})
+            sel = [x[1] for x in self.samples if prev <= x[0] <= end]
+            row = {"samples": len(sel)}
+            for k, nm in names.items():
+                v = [x[k] for x in sel if x.get(k)]
+                row[nm] = round(statistics.mean(v), 1) if v else None
+            if len(sel) >= 2 and sel[0].get("accumulation_counter") and sel[-1].get("accumulation_counter"):
+                dt = sel[-1]["accumulation_counter"] - sel[0]["accumulation_counter"]
+                for k in self.RESIDENCY:
+                    if dt > 0 and sel[0].get(k) is not None and sel[-1].get(k) is not None:
+                        row[k.replace("_residency_acc", "_share")] = round((sel[-1][k] - sel[0][k]) / dt, 3)
+            out.append(row)
             prev = end
         return out
 
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the tiled path runs on a single device and has no "
               "multi-GPU form (run with --gpus 1)", file=sys.stderr)
@@ -794,7 +820,6 @@ def machine_info(torch):
     cores and memory nodes, the copy-engine switch and the clocks the driver
     reports (where rocm-smi is there to read them)."""
     import glob
-    import subprocess
     props = torch.cuda.get_device_properties(0)
     info = {"device": props.name, "arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count, "hbm_bytes": props.total_memory,
@@ -806,13 +831,24 @@ def machine_info(torch):
             info["host_cpu"] = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
     except OSError:
         pass
+    # clocks and power limit through the AMD SMI library (no child process:
+    # a program started from a process that has initialised the GPU must not
+    # replace itself, and the rocm-smi script does)
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        if r.returncode == 0:
-            card = next(iter(json.loads(r.stdout).values()))
-            info["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()}
-    except Exception:
-        pass
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        clk = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+        mem = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)
+        info["clocks"] = {"sclk_MHz_now": clk.get("clk"), "sclk_MHz_max": clk.get("max_clk"),
+                          "mclk_MHz_now": mem.get("clk")}
+        try:
+            pw = amdsmi.amdsmi_get_power_cap_info(h)
+            info["power_cap_W"] = pw.get("power_cap") / 1e6 if pw.get("power_cap", 0) > 1e4 else pw.get("power_cap")
+        except Exception:
+            pass
+    except Exception as e:
+        info["clocks"] = {"error": str(e)[:200]}
     return info
 
 
