@@ -89,6 +89,15 @@ __device__ __forceinline__ rsrc_t make_rsrc(const char *base, uint32_t records =
     return rsrc_t{lo, hi & 0xffffu, records, kRsrcWord3};
 }
 
+// rs with its base moved on by `bytes` (bases stay below 2^48, so the carry
+// never reaches the stride field).
+__device__ __forceinline__ rsrc_t rsrc_add(rsrc_t rs, uint64_t bytes) {
+    const uint64_t b = (((uint64_t)rs[1] << 32) | rs[0]) + bytes;
+    rs[0] = (uint32_t)b;
+    rs[1] = (uint32_t)(b >> 32);
+    return rs;
+}
+
 // One 16-byte-per-lane copy global -> LDS at lds_block + 16 * lane.  Written as
 // inline assembly so that the compiler's wait-count pass, which cannot tell
 // LDS stages apart, does not drain every copy in flight before each LDS read;
@@ -99,8 +108,8 @@ __device__ __forceinline__ rsrc_t make_rsrc(const char *base, uint32_t records =
 // instruction touches m0 at all, so the warning is silenced here.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16(rsrc_t rs, char *lds_block, uint32_t voff) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_block));
+__device__ __forceinline__ void copy16(rsrc_t rs, uint32_t lds_block, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_block);
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "buffer_load_dwordx4 %1, %2, 0 offen lds"
@@ -145,20 +154,36 @@ struct RcOperand {
         }
     }
 
-    // Copy j of this wave for the step starting at reduction index k0.
-    // Chunks at or past the reduction length (a ragged last step, or a step
-    // past the end) read as zero.
-    __device__ __forceinline__ void issue(char *unit, int64_t k0, int64_t red, int wave, int lane, int j) {
-        const rsrc_t rs = make_rsrc(base + k0 * 2);
-        const bool ok = k0 + chunk_of(j, wave, lane) * 8 < red;
-        copy16(rs, unit + (wave * NCOPY + j) * 1024, ok ? voff[j] : kOOB);
+    // Copy cursor: the descriptor of the next step of this operand to copy
+    // (based at that step's first reduction index) and that index.  The
+    // steps are copied in order, so the cursor only moves on.
+    rsrc_t cur;
+    int32_t ck;
+    __device__ __forceinline__ void init_cursor() {
+        cur = make_rsrc(base);
+        ck = 0;
     }
-
-    // The same when the reduction length is a multiple of BK: a whole step is
-    // in range or (past the last unit) none of it, which the descriptor's
-    // record count expresses without a per-lane select.
-    __device__ __forceinline__ void issue_aligned(char *unit, int64_t k0, bool valid, int wave, int j) {
-        copy16(make_rsrc(base + k0 * 2, valid ? kNumRecords : 0u), unit + (wave * NCOPY + j) * 1024, voff[j]);
+    // The next step's descriptor and first reduction index k0; moves the
+    // cursor on.  With an aligned reduction length a step lies wholly in range
+    // or (past the last one) wholly out, which the record count expresses.
+    template <bool ALIGNED, bool SPLIT>
+    __device__ __forceinline__ rsrc_t take(int32_t red, int32_t &k0) {
+        rsrc_t rs = cur;
+        if constexpr (ALIGNED) rs[2] = ck < red ? kNumRecords : 0u;
+        k0 = ck;
+        cur = rsrc_add(cur, 2 * BK);
+        ck += BK;
+        return rs;
+    }
+    // Copy j of this wave of a step taken as (rs, k0) into the unit whose
+    // part for this wave starts at LDS address `at`; in a ragged step, chunks
+    // at or past the reduction length read as zero.
+    template <bool ALIGNED>
+    __device__ __forceinline__ void issue(const rsrc_t &rs, int32_t k0, int32_t red, uint32_t at, int wave,
+                                          int lane, int j) const {
+        uint32_t off = voff[j];
+        if constexpr (!ALIGNED) off = k0 + chunk_of(j, wave, lane) * 8 < red ? off : kOOB;
+        copy16(rs, at + j * 1024, off);
     }
 
     // Fragment reads (v_mfma_f32_16x16x32).  Fragment f of half ks (0, 1) of
@@ -207,17 +232,13 @@ struct RsOperand {
     static_assert(WROWS % 16 == 0, "rows come in 16-row fragments per wave");
     const char *base;   // &M[r0]
     const char *base2;  // &M2[r0]: reduction rows from `split` on (split = 0: none)
-    int64_t split;
+    int32_t split;
     int64_t ldb;        // ld in bytes
     uint32_t voff[NCOPY];
 
     __device__ __forceinline__ void set_split(const void *M2, int64_t split_, int64_t r0) {
-        split = M2 ? split_ : 0;
+        split = M2 ? (int32_t)split_ : 0;
         base2 = M2 ? reinterpret_cast<const char *>(static_cast<const uint16_t *>(M2) + r0) : base;
-    }
-    // Address of reduction row k0 (a step never straddles `split`).
-    __device__ __forceinline__ const char *row(int64_t k0) const {
-        return (split && k0 >= split) ? base2 + (k0 - split) * ldb : base + k0 * ldb;
     }
 
     __device__ __forceinline__ static int seg_pos(int k, int s) {
@@ -243,19 +264,48 @@ struct RsOperand {
         }
     }
 
-    // Copy j of this wave for the step starting at reduction index k0; rows
-    // at or past the reduction length read as zero.  Row k of the unit lies
-    // in bytes [k ldb, (k + 1) ldb) from row(k0), so a descriptor that ends
-    // after the last valid row cuts the rest off, with no per-lane select.
-    __device__ __forceinline__ void issue(char *unit, int64_t k0, int64_t red, int wave, int lane, int j) {
-        (void)lane;
-        const int64_t rem = red - k0;  // valid rows from k0 on (none past the end)
-        const uint32_t records = rem <= 0 ? 0u : (rem >= kGemmStep ? kNumRecords : (uint32_t)(rem * ldb));
-        copy16(make_rsrc(row(k0), records), unit + (wave * NCOPY + j) * 1024, voff[j]);
+    // Copy cursor: the descriptor of the next step of this operand to copy
+    // (based at that step's first reduction row) and that row's index.  The
+    // steps are copied in order, so the cursor only moves on: by BK rows, or
+    // to M2's first row when it reaches `split` (a step never straddles it).
+    rsrc_t cur, cur2;  // cur2: based at M2's first row
+    int32_t ck;
+    __device__ __forceinline__ void init_cursor() {
+        cur = make_rsrc(base);
+        cur2 = make_rsrc(base2);
+        ck = 0;
     }
-
-    __device__ __forceinline__ void issue_aligned(char *unit, int64_t k0, bool valid, int wave, int j) {
-        copy16(make_rsrc(row(k0), valid ? kNumRecords : 0u), unit + (wave * NCOPY + j) * 1024, voff[j]);
+    // The next step's descriptor and first reduction index k0; moves the
+    // cursor on (with selects, not a branch: the main loop stays one block).
+    // Rows at or past the reduction length read as zero: row k of
+    // the unit lies in bytes [k ldb, (k + 1) ldb) from the step's base, so a
+    // record count that ends after the last valid row cuts the rest off.
+    template <bool ALIGNED, bool SPLIT>
+    __device__ __forceinline__ rsrc_t take(int32_t red, int32_t &k0) {
+        rsrc_t rs = cur;
+        const int32_t rem = red - ck;  // valid rows from ck on (none past the end)
+        if constexpr (ALIGNED)
+            rs[2] = rem > 0 ? kNumRecords : 0u;
+        else
+            rs[2] = rem <= 0 ? 0u : (rem >= BK ? kNumRecords : (uint32_t)(rem * ldb));
+        k0 = ck;
+        cur = rsrc_add(cur, (uint64_t)(BK * ldb));
+        ck += BK;
+        if constexpr (SPLIT) {
+            const bool to2 = ck == split;
+            cur[0] = to2 ? cur2[0] : cur[0];
+            cur[1] = to2 ? cur2[1] : cur[1];
+        }
+        return rs;
+    }
+    template <bool ALIGNED>
+    __device__ __forceinline__ void issue(const rsrc_t &rs, int32_t k0, int32_t red, uint32_t at, int wave,
+                                          int lane, int j) const {
+        (void)k0;
+        (void)red;
+        (void)wave;
+        (void)lane;
+        copy16(rs, at + j * 1024, voff[j]);
     }
 
     // Fragment reads (v_mfma_f32_16x16x32).  Fragment f of half ks (0, 1) of
@@ -517,35 +567,37 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     // MFMAs, so that no wave stalls on a burst of copies while its matrix
     // unit idles.
     const int64_t ksteps = (a.red + BK - 1) / BK;
-    const int64_t nunits = 2 * ksteps;
-    auto slot = [&](int64_t u) __attribute__((always_inline)) -> char * {
+    const int32_t red = (int32_t)a.red;  // below 2^30 (the host checks)
+    auto slot = [&](int u) __attribute__((always_inline)) -> char * {
         if constexpr (MIXED) {
-            return lds + ((uint32_t)u % 5u) * UF;
+            return lds + (u % 5) * UF;
         } else {
-            const uint32_t st = (uint32_t)(u >> 1);
-            return (u & 1) ? lds + 3 * UF + (st & 1u) * US : lds + (st % 3u) * UF;
+            const int st = u >> 1;
+            return (u & 1) ? lds + 3 * UF + (st & 1) * US : lds + (st % 3) * UF;
         }
     };
-    // copy j of unit u into its slot (zeros past the last unit)
-    auto copy = [&](int64_t u, int j) __attribute__((always_inline)) {
-        char *st = slot(u);
-        const int64_t k0 = (u >> 1) * BK;
-        const bool is_q = ((u & 1) == 0) == Q_FIRST;
-        if constexpr (ALIGNED) {
-            const bool valid = u < nunits;
-            if (is_q)
-                qo.issue_aligned(st, k0, valid, wave, j);
-            else
-                po.issue_aligned(st, k0, valid, wave, j);
-        } else {
-            if (is_q)
-                qo.issue(st, k0, a.red, wave, lane, j);
-            else
-                po.issue(st, k0, a.red, wave, lane, j);
-        }
+    // The next step of the first / second operand to copy (in step order).
+    constexpr bool SPLIT = EPI == EPI_ACC;  // only the input-gradient product reads two weight tiles
+    auto take_f = [&](int32_t &k0) __attribute__((always_inline)) -> rsrc_t {
+        if constexpr (Q_FIRST) return qo.template take<ALIGNED, SPLIT>(red, k0);
+        else return po.template take<ALIGNED, false>(red, k0);
     };
-    auto qslot = [&](int64_t s) __attribute__((always_inline)) { return slot(2 * s + (Q_FIRST ? 0 : 1)); };
-    auto pslot = [&](int64_t s) __attribute__((always_inline)) { return slot(2 * s + (Q_FIRST ? 1 : 0)); };
+    auto take_s = [&](int32_t &k0) __attribute__((always_inline)) -> rsrc_t {
+        if constexpr (Q_FIRST) return po.template take<ALIGNED, false>(red, k0);
+        else return qo.template take<ALIGNED, SPLIT>(red, k0);
+    };
+    // copy j of such a step into the unit at LDS address `unit`
+    const uint32_t wf = (uint32_t)(wave * NF * 1024), ws = (uint32_t)(wave * NS * 1024);
+    auto issue_f = [&](const rsrc_t &rs, int32_t k0, uint32_t unit, int j) __attribute__((always_inline)) {
+        if constexpr (Q_FIRST) qo.template issue<ALIGNED>(rs, k0, red, unit + wf, wave, lane, j);
+        else po.template issue<ALIGNED>(rs, k0, red, unit + wf, wave, lane, j);
+    };
+    auto issue_s = [&](const rsrc_t &rs, int32_t k0, uint32_t unit, int j) __attribute__((always_inline)) {
+        if constexpr (Q_FIRST) po.template issue<ALIGNED>(rs, k0, red, unit + ws, wave, lane, j);
+        else qo.template issue<ALIGNED>(rs, k0, red, unit + ws, wave, lane, j);
+    };
+    qo.init_cursor();
+    po.init_cursor();
 
     using QBs = typename QOp::Bases;
     using PBs = typename POp::Bases;
@@ -608,13 +660,12 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     auto pfrag = [&](const PBs &b0, const PBs &b1, int h, int f, u32x4 &out) __attribute__((always_inline)) {
         po.frag(h ? b1 : b0, h, f, out);
     };
-    // One step: NM MFMAs; between them the reads of the next step (from the
-    // slots qs, ps) and the copies: copy_a(0 .. NS-1) in the first half,
-    // copy_b(0 .. NF-1) in the second.
-    auto step = [&](auto PAR, const char *qs, const char *ps, auto &&copy_a, auto &&copy_b) __attribute__((always_inline)) {
+    // One step: NM MFMAs; between them the reads of the next step (at the
+    // bases qb0, qb1, pb0, pb1) and the copies: copy_a(0 .. NS-1) in the
+    // first half, copy_b(0 .. NF-1) in the second.
+    auto step = [&](auto PAR, const QBs &qb0, const QBs &qb1, const PBs &pb0, const PBs &pb1, auto &&copy_a,
+                    auto &&copy_b) __attribute__((always_inline)) {
         constexpr int par = decltype(PAR)::value;
-        const QBs qb0 = qo.bases(lds_addr(qs), 0), qb1 = qo.bases(lds_addr(qs), 1);
-        const PBs pb0 = po.bases(lds_addr(ps), 0), pb1 = po.bases(lds_addr(ps), 1);
         auto rfrag = [&](int h, int f, u32x4 &out) __attribute__((always_inline)) {
             if constexpr (ROW_Q) qfrag(qb0, qb1, h, f, out); else pfrag(pb0, pb1, h, f, out);
         };
@@ -654,19 +705,36 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
 
+    // The slot ring: rg[k] is the LDS address of the slot of unit 2s + k
+    // (k = 0 .. 4) at step s.  Step s reads units 2s + 2 and 2s + 3, and
+    // copies unit 2s + 5 into the slot of unit 2s + 1 (with equal units, of
+    // unit 2s: (2s + 5) mod 5 = 2s mod 5) and unit 2s + 6 into that of unit
+    // 2s (of unit 2s + 1); both were read during step s - 1.  Moving on a step
+    // shifts the ring by two units and appends those two slots.
+    uint32_t rg[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) rg[k] = lds_addr(slot(k));
+
     // Prologue: units 0..4 in flight (units past the last one read zeros);
     // wait for units 0..3, read the fragments of step 0.
+    static_for<0, 5>([&](auto U_) __attribute__((always_inline)) {
+        constexpr int u = decltype(U_)::value;
+        int32_t k0;
+        if constexpr (u % 2 == 0) {
+            const rsrc_t rs = take_f(k0);
 #pragma unroll
-    for (int u = 0; u < 5; ++u) {
-        const bool first = (u & 1) == 0;
+            for (int j = 0; j < NF; ++j) issue_f(rs, k0, rg[u], j);
+        } else {
+            const rsrc_t rs = take_s(k0);
 #pragma unroll
-        for (int j = 0; j < (first ? NF : NS); ++j) copy(u, j);
-    }
+            for (int j = 0; j < NS; ++j) issue_s(rs, k0, rg[u], j);
+        }
+    });
     wait_and_barrier<NF>();
     {
-        const char *qs = qslot(0), *ps = pslot(0);
-        const QBs qb0 = qo.bases(lds_addr(qs), 0), qb1 = qo.bases(lds_addr(qs), 1);
-        const PBs pb0 = po.bases(lds_addr(ps), 0), pb1 = po.bases(lds_addr(ps), 1);
+        const uint32_t qs = Q_FIRST ? rg[0] : rg[1], ps = Q_FIRST ? rg[1] : rg[0];
+        const QBs qb0 = qo.bases(qs, 0), qb1 = qo.bases(qs, 1);
+        const PBs pb0 = po.bases(ps, 0), pb1 = po.bases(ps, 1);
 #pragma unroll
         for (int f = 0; f < NR; ++f)
 #pragma unroll
@@ -682,16 +750,51 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
             }
     }
 
+    // Read bases of the next step (units 2s + 2, 2s + 3), formed before the
+    // barrier that precedes the step, so that the step opens with its MFMAs.
+    QBs qb0, qb1;
+    PBs pb0, pb1;
+    auto next_bases = [&]() __attribute__((always_inline)) {
+        const uint32_t qs = Q_FIRST ? rg[2] : rg[3], ps = Q_FIRST ? rg[3] : rg[2];
+        qb0 = qo.bases(qs, 0);
+        qb1 = qo.bases(qs, 1);
+        pb0 = po.bases(ps, 0);
+        pb1 = po.bases(ps, 1);
+    };
+    next_bases();
+
     mfma_fence<false>(acc);  // accumulator writes, then the first MFMA
 
     // Step s reads step s + 1 from units 2s + 2, 2s + 3 (landed), copies unit
-    // 2s + 5 (the second operand of step s + 2) under its first half, into
-    // the slot of step s's second operand, and unit 2s + 6 (the first operand
-    // of step s + 3) under its second half, into the slot of step s's first
-    // operand (both read during step s - 1); at its end every wave has read
-    // units 2s + 2, 2s + 3, and units 2s + 4 and 2s + 5 must have landed
-    // (unit 2s + 6 may still be in flight: NF copies per wave).
-    //
+    // 2s + 5 (the second operand of step s + 2) under its first half and unit
+    // 2s + 6 (the first operand of step s + 3) under its second half; at its
+    // end every wave has read units 2s + 2, 2s + 3, and units 2s + 4 and
+    // 2s + 5 must have landed (unit 2s + 6 may still be in flight: NF copies
+    // per wave).
+    auto one_step = [&](auto PAR) __attribute__((always_inline)) {
+        const uint32_t ca = MIXED ? rg[0] : rg[1];  // unit 2s + 5
+        const uint32_t cb = MIXED ? rg[1] : rg[0];  // unit 2s + 6
+        rsrc_t rsa, rsb;
+        int32_t ka, kb;
+        step(PAR, qb0, qb1, pb0, pb1,
+             [&](int c) __attribute__((always_inline)) {
+                 if (c == 0) rsa = take_s(ka);
+                 issue_s(rsa, ka, ca, c);
+             },
+             [&](int c) __attribute__((always_inline)) {
+                 if (c == 0) rsb = take_f(kb);
+                 issue_f(rsb, kb, cb, c);
+             });
+        const uint32_t r2 = rg[2], r3 = rg[3], r4 = rg[4];
+        rg[0] = r2;
+        rg[1] = r3;
+        rg[2] = r4;
+        rg[3] = ca;
+        rg[4] = cb;
+        next_bases();
+        wait_and_barrier<NF>();
+    };
+
     // Every MFMA sits in this loop, whose body is two steps (the register
     // parity).  With an odd step count its last pass runs one step past the
     // end, on fragments read from units past the last one: zeros, which add
@@ -700,15 +803,8 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     // and so would not separate by the wait states they need.
     const int64_t npairs = (ksteps + 1) / 2;
     for (int64_t t = 0; t < npairs; ++t) {
-        const int64_t s0 = 2 * t, s1 = 2 * t + 1;
-        step(P0{}, qslot(s0 + 1), pslot(s0 + 1),
-             [&](int c) __attribute__((always_inline)) { copy(2 * s0 + 5, c); },
-             [&](int c) __attribute__((always_inline)) { copy(2 * s0 + 6, c); });
-        wait_and_barrier<NF>();
-        step(P1{}, qslot(s1 + 1), pslot(s1 + 1),
-             [&](int c) __attribute__((always_inline)) { copy(2 * s1 + 5, c); },
-             [&](int c) __attribute__((always_inline)) { copy(2 * s1 + 6, c); });
-        wait_and_barrier<NF>();
+        one_step(P0{});
+        one_step(P1{});
     }
     mfma_fence<true>(acc);  // the last MFMA, then accumulator reads
     // the copies past the last unit are still in flight: none may land after
@@ -725,7 +821,7 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
 #pragma unroll
         for (int c = 0; c < 32; ++c) {
             const int blk = wave * 32 + c;
-            copy16(rs, lds + blk * 1024, (uint32_t)(blk * 1024 + lane * 16));
+            copy16(rs, lds_addr(lds + blk * 1024), (uint32_t)(blk * 1024 + lane * 16));
         }
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
@@ -844,7 +940,9 @@ hipError_t run_shape(const GemmArgs &a, hipStream_t s) {
     const int tiles_q = (int)((a.cols + 32 * QB - 1) / (32 * QB));
     const int64_t nt = (int64_t)tiles_p * tiles_q;
     if (nt <= 0) return hipSuccess;
-    if (a.red < 1) return hipErrorInvalidValue;
+    // the kernel counts reduction indices in 32 bits
+    if (a.red < 1 || a.red >= ((int64_t)1 << 30)) return hipErrorInvalidValue;
+    if (a.Q2 && (a.qsplit <= 0 || a.qsplit % BK != 0 || a.qsplit >= a.red)) return hipErrorInvalidValue;
     // the accumulating epilogue addresses 16 rows of C through one descriptor
     if (EPI == EPI_ACC && (a.ldc < 0 || (16 * a.ldc + 256) * 4 >= (int64_t)kNumRecords)) return hipErrorInvalidValue;
     if (a.red % BK == 0)
