@@ -792,7 +792,6 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
         rg[3] = ca;
         rg[4] = cb;
         next_bases();
-        wait_and_barrier<NF>();
     };
 
     // Every MFMA sits in this loop, whose body is two steps (the register
@@ -800,10 +799,16 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     // end, on fragments read from units past the last one: zeros, which add
     // nothing.  A tail outside the loop would let the register allocator
     // place accumulator copies between the MFMAs, which it cannot see as such
-    // and so would not separate by the wait states they need.
+    // and so would not separate by the wait states they need.  The barrier
+    // between two steps opens the body rather than closing it, so that the
+    // register moves of the loop's back edge fall before it, under the last
+    // MFMAs, and every step starts with its first MFMA.  (Before the first
+    // step it finds everything it waits for already done.)
     const int64_t npairs = (ksteps + 1) / 2;
     for (int64_t t = 0; t < npairs; ++t) {
+        wait_and_barrier<NF>();
         one_step(P0{});
+        wait_and_barrier<NF>();
         one_step(P1{});
     }
     mfma_fence<true>(acc);  // the last MFMA, then accumulator reads
@@ -815,8 +820,9 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     if constexpr (EPI == EPI_GELU || EPI == EPI_GELU_F32A) {
         // H = table[A]: the GeLU table of this type goes into the now idle LDS
         // (128 KiB: 32 one-KiB copies per wave).  Every wave's copies of the
-        // main loop must have landed before the table overwrites the ring.
-        asm volatile("s_barrier" ::: "memory");
+        // main loop must have landed, and every wave's reads of the ring
+        // returned, before the table overwrites the ring.
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         const rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(gelu_table<T>()), 65536u * 2u);
 #pragma unroll
         for (int c = 0; c < 32; ++c) {
