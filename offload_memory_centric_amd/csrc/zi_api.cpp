@@ -377,6 +377,20 @@ zi_status run_bwd(zi_ctx *c, const zi_plan *p, const void *X, const void *dY, fl
     // runs after it and covers the copy of the next tile into the freed slot.
     static_assert(kPairStep == kGemmStep, "pairs split the reduction at a GEMM step");
     const bool pairs = pairs_apply((int)N, d, c->dw_slots, n);
+    // The recomputed forward of such a pair is one launch too (output columns
+    // of both tiles), run once tile 2j + 1 has landed, where that takes fewer
+    // rounds of workgroups over the compute units than two launches: at
+    // T = 32768 a 1600-column tile is 855 workgroups of 320 x 192 (4 rounds
+    // of 256, the last a third full) and the pair 1710 (7 rounds).  The
+    // launch's macro-tile must not straddle the two tiles' columns.
+    bool re_pairs = false;
+    if (pairs && Yr) {
+        int tr = 0, tc = 0;
+        gemm_tile(GemmOp::Fwd, pr.T, 2 * n, &tr, &tc);
+        const int64_t cus = c->cus > 0 ? c->cus : 1;
+        const int64_t w1 = gemm_workgroups(GemmOp::Fwd, pr.T, n), w2 = gemm_workgroups(GemmOp::Fwd, pr.T, 2 * n);
+        re_pairs = n % tc == 0 && (w2 + cus - 1) / cus < 2 * ((w1 + cus - 1) / cus);
+    }
     zi_status st;
     // The products of a backward pass stay on one stream: running the
     // recomputed forward beside the previous tile's dW on the second stream
@@ -389,22 +403,30 @@ zi_status run_bwd(zi_ctx *c, const zi_plan *p, const void *X, const void *dY, fl
         const int s = (int)((base + i) % d);
         HIPCHK(c, hipStreamWaitEvent(c->comp, c->w_ready[s], 0));
         const uint16_t *dYi = static_cast<const uint16_t *>(dY) + i * n;
-        if (Yr) {  // recomputed forward slice from the same staged tile
-            GemmArgs a{};
-            a.Q = c->wslot(s);
-            a.ldq = pr.K;
-            a.P = X;
-            a.ldp = pr.K;
-            a.C = static_cast<char *>(Yr) + i * n * (f32 ? 4 : 2);
-            a.ldc = pr.M;
-            a.rows = pr.T;
-            a.cols = n;
-            a.red = pr.K;
-            a.out_f32 = f32 ? 1 : 0;
-            if ((st = gemm(c, K_FWD_RECOMPUTE, GemmOp::Fwd, pr.dtype, a, tile_flops)) != ZI_OK) return st;
-        }
         const bool first_of_pair = pairs && (i % 2 == 0) && i + 1 < N;
         const bool second_of_pair = pairs && (i % 2 == 1);
+        if (Yr && !(re_pairs && first_of_pair)) {  // recomputed forward slice(s) from the staged tile(s)
+            const bool both = re_pairs && second_of_pair;
+            const int64_t i0 = both ? i - 1 : i;
+            GemmArgs a{};
+            a.Q = c->wslot(both ? (int)((base + i0) % d) : s);
+            a.ldq = pr.K;
+            if (both) {
+                a.Q2 = c->wslot(s);
+                a.qsplit = n;
+            }
+            a.P = X;
+            a.ldp = pr.K;
+            a.C = static_cast<char *>(Yr) + i0 * n * (f32 ? 4 : 2);
+            a.ldc = pr.M;
+            a.rows = pr.T;
+            a.cols = (i - i0 + 1) * n;
+            a.red = pr.K;
+            a.out_f32 = f32 ? 1 : 0;
+            if ((st = gemm(c, K_FWD_RECOMPUTE, GemmOp::Fwd, pr.dtype, a, tile_flops * (double)(i - i0 + 1))) !=
+                ZI_OK)
+                return st;
+        }
         if (!first_of_pair) {  // dX (+)= dY_i W_i^T (or over tiles i-1, i): W^t[r][k] read across its rows
             const int64_t i0 = second_of_pair ? i - 1 : i;
             GemmArgs a{};

@@ -29,9 +29,11 @@ struct GemmArgs {
     int64_t red;    // reduction length
     int accumulate; // Dx only: 0 = overwrite, 1 = add into C
     int out_f32;    // Fwd / Dw: write fp32 instead of the 16-bit format; FwdGelu: A in fp32
-    // Dx only: reduction rows k >= qsplit of Q come from Q2 (row k - qsplit), so
-    // one launch can consume two weight tiles held in different ring slots.
-    // qsplit = 0: no split.  Otherwise a multiple of the kernel's step (64).
+    // Two weight tiles held in different ring slots, consumed by one launch.
+    // Dx: reduction rows k >= qsplit of Q come from Q2 (row k - qsplit);
+    // qsplit a multiple of the kernel's step (64).  Fwd: output columns
+    // q >= qsplit come from Q2 (row q - qsplit); qsplit a multiple of the
+    // launch's macro-tile width (gemm_tile).  Q2 = null: no split.
     const void *Q2;
     int64_t qsplit;
 };

@@ -556,9 +556,18 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
 
     QOp qo;
     POp po;
-    qo.init(static_cast<const uint16_t *>(a.Q), a.ldq, q0, a.cols, wave, lane);
+    if constexpr (Q_RS) {
+        qo.init(static_cast<const uint16_t *>(a.Q), a.ldq, q0, a.cols, wave, lane);
+        qo.set_split(a.Q2, a.qsplit, q0);
+    } else {
+        // a forward product over two weight tiles: columns from qsplit on
+        // are rows of Q2 (qsplit is a multiple of the macro-tile's width, so
+        // a workgroup reads one tile)
+        const bool second = a.Q2 && q0 >= a.qsplit;
+        qo.init(static_cast<const uint16_t *>(second ? a.Q2 : a.Q), a.ldq, second ? q0 - a.qsplit : q0,
+                second ? a.cols - a.qsplit : a.cols, wave, lane);
+    }
     po.init(static_cast<const uint16_t *>(a.P), a.ldp, p0, a.rows, wave, lane);
-    if constexpr (Q_RS) qo.set_split(a.Q2, a.qsplit, q0);
     qo.init_reads(wq, lane);
     po.init_reads(wp, lane);
 
@@ -948,7 +957,13 @@ hipError_t run_shape(const GemmArgs &a, hipStream_t s) {
     if (nt <= 0) return hipSuccess;
     // the kernel counts reduction indices in 32 bits
     if (a.red < 1 || a.red >= ((int64_t)1 << 30)) return hipErrorInvalidValue;
-    if (a.Q2 && (a.qsplit <= 0 || a.qsplit % BK != 0 || a.qsplit >= a.red)) return hipErrorInvalidValue;
+    // a second weight tile: reduction rows from qsplit on (gradient products),
+    // or output columns from qsplit on (forward products), which no
+    // workgroup's columns may straddle
+    if (a.Q2) {
+        if (Q_RS && (a.qsplit <= 0 || a.qsplit % BK != 0 || a.qsplit >= a.red)) return hipErrorInvalidValue;
+        if (!Q_RS && (a.qsplit <= 0 || a.qsplit % (32 * QB) != 0 || a.qsplit >= a.cols)) return hipErrorInvalidValue;
+    }
     // the accumulating epilogue addresses 16 rows of C through one descriptor
     if (EPI == EPI_ACC && (a.ldc < 0 || (16 * a.ldc + 256) * 4 >= (int64_t)kNumRecords)) return hipErrorInvalidValue;
     if (a.red % BK == 0)
