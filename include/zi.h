@@ -144,7 +144,12 @@ int32_t zi_prefetch_depth(double t_fetch_s, double t_layer_s);
  * (pwwt.cn article, section "关键技术三：Overlap-Centric Design": the pipeline
  * runs at the pace of its slowest stage).  backward: 0 = forward pass,
  * 1 = backward pass, 2 = backward with the forward product recomputed per
- * tile.  Rates: flop_rate in FLOP/s (products), link rates in bytes/s. */
+ * tile, 3 = the same with the recomputed products of a dX pair (tiles 2j and
+ * 2j + 1, see zi_tiled_linear_bwd_recompute) run together once tile 2j + 1
+ * has landed, the order the context takes where one launch over both tiles
+ * needs fewer rounds of workgroups than two (the model, priced by FLOP rates,
+ * cannot tell that itself).  Rates: flop_rate in FLOP/s (products), link
+ * rates in bytes/s. */
 typedef struct {
     double t_pass_s;        /* first copy issued -> last product (and write-back) done */
     double t_compute_s;     /* sum of product times */
@@ -194,8 +199,9 @@ typedef struct {
  * budget (the rules of zi_plan_tiles; with backward > 0 as for a plan with
  * dW_host, so gradient slots are sized in).  Each is priced with the ring's
  * event recurrence (as zi_plan_predict) using that width's measured rates,
- * over back-to-back steps of one forward pass plus, for backward = 1 or 2,
- * one backward pass (2: with the forward product recomputed per tile), the
+ * over back-to-back steps of one forward pass plus, for backward = 1, 2 or 3,
+ * one backward pass (2: with the forward product recomputed per tile; 3: as
+ * zi_plan_predict's 3), the
  * ring's state carried from pass to pass.  The choice has the least t_step_s;
  * candidates within a relative 1e-9 of it count as equal, and then the
  * smaller ring, the smaller d and the smaller N win, in that order.
@@ -203,7 +209,7 @@ typedef struct {
  * the order considered (widths in curve order, d ascending); *table_len (if
  * not NULL) is set to the number of candidates, which may exceed table_cap.
  * ZI_ERR_ARG on a NULL problem, curve or out, non-positive or non-finite
- * rates, a width < 1, max_d < 1, or backward outside 0..2; ZI_ERR_SHAPE if
+ * rates, a width < 1, max_d < 1, or backward outside 0..3; ZI_ERR_SHAPE if
  * the problem's own shapes are invalid; ZI_ERR_BUDGET if no candidate fits. */
 zi_status zi_plan_choose(const zi_problem *problem, const zi_rate_curve *curve, double h2d_bytes_per_s,
                          double d2h_bytes_per_s, int32_t backward, int32_t max_d, zi_choice *out,
@@ -279,7 +285,12 @@ zi_status zi_tiled_linear_bwd(zi_ctx *ctx, const zi_plan *plan, const void *X_de
  * (activation checkpointing: forward, recomputed forward and backward,
  * transformer-math page, section "The FLOPs-per-byte test every tier must
  * pass"): per tile, Yr[:, i*n:(i+1)*n] = RNE(X W_i) first, then the two
- * backward products as in zi_tiled_linear_bwd.  Yr_dev: [T x M] device. */
+ * backward products as in zi_tiled_linear_bwd.  Where the backward runs the
+ * dX products of tiles 2j and 2j + 1 as one launch (gradient slots, d >= 2,
+ * n a multiple of 64) and one launch over both tiles' columns takes fewer
+ * rounds of workgroups than two, the recomputed products of the pair are
+ * that one launch, run once tile 2j + 1 has landed.  Yr is bit-identical to
+ * the forward's Y either way.  Yr_dev: [T x M] device. */
 zi_status zi_tiled_linear_bwd_recompute(zi_ctx *ctx, const zi_plan *plan, const void *X_dev,
                                         const void *dY_dev, float *dX_dev, void *Yr_dev);
 

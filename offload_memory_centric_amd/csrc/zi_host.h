@@ -29,6 +29,10 @@ struct PassModel {
     // both are resident (the stager does so with gradient slots, d >= 2,
     // N >= 2 and n a multiple of the GEMM's reduction step)
     bool pairs = false;
+    // with pairs: the recomputed forward products of tiles 2j and 2j + 1 also
+    // run together, once tile 2j + 1 is resident (the stager does so where one
+    // launch takes fewer rounds of workgroups than two)
+    bool re_pairs = false;
     double t_h2d = 0, t_d2h = 0;
     double t_fwd = 0, t_recompute = 0, t_dx = 0, t_dw = 0;
 };

@@ -121,10 +121,12 @@ static void run_pass(RingState &st, const PassModel &m, double *busy, double *li
         // recompute (optional) and dX read the weight slot
         if (m.pairs) {
             // tile 2j: recompute and dW only, its slot stays taken; tile 2j+1:
-            // recompute, then dX over both, which releases both slots
+            // recompute, then dX over both, which releases both slots.  With
+            // re_pairs tile 2j has only its dW, and tile 2j+1 recomputes both.
             const bool first = i % 2 == 0 && i + 1 < N;
             const bool second = i % 2 == 1;
-            const double t_w = m.t_recompute + (first ? 0.0 : second ? 2.0 * m.t_dx : m.t_dx);
+            const double t_re = !m.re_pairs ? m.t_recompute : first ? 0.0 : second ? 2.0 * m.t_recompute : m.t_recompute;
+            const double t_w = t_re + (first ? 0.0 : second ? 2.0 * m.t_dx : m.t_dx);
             const double after_w = start + t_w;
             *busy += t_w + m.t_dw;
             if (!first) {
@@ -229,7 +231,7 @@ extern "C" zi_status zi_plan_predict(const zi_plan *plan, int32_t backward, doub
     if (!plan || !out) return fail(ZI_ERR_ARG, "plan and out are required");
     if (!(flop_rate > 0) || !(h2d_bps > 0) || (backward && !(d2h_bps > 0)))
         return fail(ZI_ERR_ARG, "rates must be positive");
-    if (backward < 0 || backward > 2) return fail(ZI_ERR_ARG, "backward must be 0, 1 or 2");
+    if (backward < 0 || backward > 3) return fail(ZI_ERR_ARG, "backward must be 0, 1, 2 or 3");
     if (backward && !plan->prob.dW_host)
         return fail(ZI_ERR_STATE, "a backward needs a plan with dW_host");
     const zi_problem &p = plan->prob;
@@ -244,9 +246,10 @@ extern "C" zi_status zi_plan_predict(const zi_plan *plan, int32_t backward, doub
     m.t_fwd = tile_flops / flop_rate;
     m.t_dx = tile_flops / flop_rate;
     m.t_dw = tile_flops / flop_rate;
-    m.t_recompute = backward == 2 ? tile_flops / flop_rate : 0.0;
+    m.t_recompute = backward >= 2 ? tile_flops / flop_rate : 0.0;
     m.t_d2h = backward ? (double)i.dw_tile_bytes / d2h_bps : 0.0;
     m.pairs = backward && pairs_apply(m.N, m.d, m.dw_slots, i.n);
+    m.re_pairs = backward == 3 && m.pairs;
     Prediction r = simulate_pass(m);
     out->t_pass_s = r.t_pass;
     out->t_compute_s = r.t_compute;
@@ -263,7 +266,7 @@ extern "C" zi_status zi_plan_choose(const zi_problem *problem, const zi_rate_cur
     clear_error();
     if (table_len) *table_len = 0;
     if (!problem || !curve || !out) return fail(ZI_ERR_ARG, "problem, curve and out are required");
-    if (backward < 0 || backward > 2) return fail(ZI_ERR_ARG, "backward must be 0, 1 or 2");
+    if (backward < 0 || backward > 3) return fail(ZI_ERR_ARG, "backward must be 0, 1, 2 or 3");
     if (max_d < 1) return fail(ZI_ERR_ARG, "max_d must be >= 1 (got %d)", max_d);
     if (curve->count < 1 || !curve->n || !curve->fwd) return fail(ZI_ERR_ARG, "the curve has no samples");
     if (table_cap > 0 && !table) return fail(ZI_ERR_ARG, "table is NULL with table_cap > 0");
@@ -325,9 +328,10 @@ extern "C" zi_status zi_plan_choose(const zi_problem *problem, const zi_rate_cur
                 pm[1].t_fwd = 0.0;
                 pm[1].t_dx = tile_flops / r_dx;
                 pm[1].t_dw = tile_flops / r_dw;
-                pm[1].t_recompute = backward == 2 ? tile_flops / r_fwd : 0.0;
+                pm[1].t_recompute = backward >= 2 ? tile_flops / r_fwd : 0.0;
                 pm[1].t_d2h = (double)info.dw_tile_bytes / b_d2h;
                 pm[1].pairs = pairs_apply(q.N, d, info.dw_slots, n);
+                pm[1].re_pairs = backward == 3 && pm[1].pairs;
                 c.t_bwd_s = simulate_pass(pm[1]).t_pass;
             }
             c.t_step_s = simulate_steady_step(pm, backward ? 2 : 1);

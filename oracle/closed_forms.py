@@ -201,7 +201,11 @@ def ring_run(N: int, d: int, passes, grad_slots: int = 0):
     gradient's write-back) and `pairs`: the dX products of tiles 2j and 2j+1
     of the pass run as one product once both are resident (our reading of the
     grouping the library uses with gradient slots), which frees both slots;
-    tile 2j then runs only its recompute and dW before tile 2j+1 arrives."""
+    tile 2j then runs only its recompute and dW before tile 2j+1 arrives.
+    With `re_pairs` as well, the recomputed products of the pair also run
+    once tile 2j+1 is resident (tile 2j runs only its dW), as the library
+    orders them where one launch over both tiles takes fewer rounds of
+    workgroups than two."""
     if any(p.get("pairs") for p in passes) and not grad_slots:
         raise ValueError("pairs need gradient slots")
     release = []      # release[g]: when the g-th staged tile frees its weight slot
@@ -218,11 +222,13 @@ def ring_run(N: int, d: int, passes, grad_slots: int = 0):
                 release.append(comp)
                 continue
             h = len(grad_free)
+            re2 = bool(p.get("pairs") and p.get("re_pairs"))
             if p.get("pairs") and i % 2 == 0 and i + 1 < N:
-                w_done = start + p.get("t_re", 0.0)   # no dX yet; the slot stays taken
+                # no dX yet (nor, with re_pairs, the recompute); the slot stays taken
+                w_done = start + (0.0 if re2 else p.get("t_re", 0.0))
                 release.append(None)
             elif p.get("pairs") and i % 2 == 1:
-                w_done = start + p.get("t_re", 0.0) + 2 * p["t_dx"]
+                w_done = start + (2 if re2 else 1) * p.get("t_re", 0.0) + 2 * p["t_dx"]
                 release[g - 1] = w_done
                 release.append(w_done)
             else:
@@ -266,7 +272,8 @@ def choose_tiling(T: int, K: int, M: int, dtype: str, budget: int, widths, r_fwd
     steps of one forward pass plus, for backward 1 or 2, one backward pass (2:
     the forward product recomputed per tile), with the measured rates of that
     width (copy rates c_h2d / c_d2h per width, else h2d / d2h).  Returns
-    (choice, table): the candidate of least step time, where a candidate
+    (choice, table): backward 3 is 2 with the recomputed products of a dX
+    pair run together (re_pairs).  The candidate of least step time, where a candidate
     within a relative 1e-9 of the best so far counts as equal and then the
     smaller ring, the smaller d, the smaller N win; table lists every
     candidate in the order considered, each with its passes' times on their
@@ -287,11 +294,12 @@ def choose_tiling(T: int, K: int, M: int, dtype: str, budget: int, widths, r_fwd
             step = [{"t_copy": t_copy, "t_fwd": flops / r_fwd[j]}]
             if backward:
                 step.append({"t_copy": t_copy, "backward": True,
-                             "t_re": flops / r_fwd[j] if backward == 2 else 0.0,
+                             "t_re": flops / r_fwd[j] if backward >= 2 else 0.0,
                              "t_dx": flops / r_dx[j], "t_dw": flops / r_dw[j],
                              "t_back": K * n * (4 if grad_f32 else BYTES[dtype]) / (c_d2h[j] if c_d2h else d2h)})
             if backward:
                 step[1]["pairs"] = slots > 0 and d >= 2 and N >= 2 and n % 64 == 0
+                step[1]["re_pairs"] = backward == 3
             alone = [ring_run(N, d, [p], slots)[0] for p in step]
             c = {"N": N, "d": d, "n": n, "dw_slots": slots, "ring_bytes": nbytes,
                  "t_fwd_s": alone[0], "t_bwd_s": alone[1] if backward else 0.0,

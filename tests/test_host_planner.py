@@ -245,9 +245,29 @@ def test_model_backward_separate_and_in_slot(zi):
     rec = zi.zi_plan_predict(h_sep, 2, R, BW, BW)
     assert rec.t_compute_s == pytest.approx(8 * 3 * tile_flops / R)
     with pytest.raises(zi.ZiError):
-        zi.zi_plan_predict(h_sep, 3, R, BW, BW)
+        zi.zi_plan_predict(h_sep, 4, R, BW, BW)
     zi.zi_plan_destroy(h_sep)
     zi.zi_plan_destroy(h_in)
+
+
+def test_model_paired_recompute_matches_the_oracle(zi):
+    # backward = 3: the recomputed products of a dX pair run once tile 2j + 1
+    # has landed.  The library's recurrence against the oracle's, link-bound
+    # and compute-bound, with an odd tile count (the last tile on its own).
+    for N in (8, 7):
+        for BW in (5e10, 5e12):
+            R = 1e15
+            h, info = plan_for_model(zi, N=N, d=2)
+            assert info.dw_slots == 2
+            tile_flops = 2.0 * 4096 * 8192 * info.n
+            p = {"t_copy": info.tile_bytes / BW, "backward": True, "t_re": tile_flops / R,
+                 "t_dx": tile_flops / R, "t_dw": tile_flops / R, "t_back": info.dw_tile_bytes / BW}
+            for bwd, extra in ((2, {}), (3, {"re_pairs": True})):
+                got = zi.zi_plan_predict(h, bwd, R, BW, BW)
+                want = cf.ring_run(N, 2, [dict(p, pairs=True, **extra)], grad_slots=2)[0]
+                assert got.t_pass_s == pytest.approx(want, rel=1e-12), (N, BW, bwd)
+                assert got.t_compute_s == pytest.approx(N * 3 * tile_flops / R)
+            zi.zi_plan_destroy(h)
 
 
 # --- tile-width choice: zi_plan_choose against the oracle's brute force ------
@@ -283,7 +303,7 @@ def test_choice_matches_the_oracle(zi, seed):
     dx = [r * rng.uniform(0.8, 1.1) for r in fwd]
     dw = [r * rng.uniform(0.8, 1.1) for r in fwd]
     h2d, d2h = rng.uniform(2e10, 6e10), rng.uniform(2e10, 6e10)
-    backward = int(seed % 3)
+    backward = int(seed % 4)
     max_d = int(rng.integers(1, 5))
     tile_max = K * widths[-2] * 2
     budget = 0 if seed % 4 == 0 else int(rng.uniform(1.0, 5.0) * tile_max)
@@ -349,7 +369,7 @@ def test_choice_errors(zi):
         zi.zi_plan_choose(p, [4096], [1e15], h2d_bytes_per_s=5e10, d2h_bytes_per_s=5e10, max_d=0)
     assert e.value.status == zi.ZI_ERR_ARG
     with pytest.raises(zi.ZiError) as e:
-        zi.zi_plan_choose(p, [4096], [1e15], h2d_bytes_per_s=5e10, d2h_bytes_per_s=5e10, backward=3)
+        zi.zi_plan_choose(p, [4096], [1e15], h2d_bytes_per_s=5e10, d2h_bytes_per_s=5e10, backward=4)
     assert e.value.status == zi.ZI_ERR_ARG
     with pytest.raises(zi.ZiError) as e:  # the problem's own shape
         zi.zi_plan_choose(_problem(zi, T, 8190, M, "f16", 0), [4096], [1e15], h2d_bytes_per_s=5e10,

@@ -76,6 +76,30 @@ def test_paired_dx_by_hand():
         cf.ring_run(4, 2, [dict(b, pairs=True)], grad_slots=0)
 
 
+def test_paired_recompute_by_hand():
+    # N = 4, d = 2, copy 2, recompute 1, dX 1, dW 1, free write-back, two
+    # gradient slots, dX paired.  Recompute per tile: tile 0 copy [0,2]
+    # recompute [2,3] dW [3,4]; tile 1 copy [2,4] recompute [4,5] dX [5,7]
+    # dW [7,8]; tile 2 copy [7,9] (both slots freed at 7) recompute [9,10]
+    # dW [10,11]; tile 3 copy [9,11] recompute [11,12] dX [12,14] dW [14,15].
+    b = {"t_copy": 2.0, "backward": True, "t_re": 1.0, "t_dx": 1.0, "t_dw": 1.0, "t_back": 0.0,
+         "pairs": True}
+    assert cf.ring_run(4, 2, [b], grad_slots=2) == [15.0]
+    # re_pairs: tile 0 dW [2,3]; tile 1 copy [2,4] recompute of both [4,6]
+    # dX [6,8] dW [8,9]; tile 2 copy [8,10] dW [10,11]; tile 3 copy [10,12]
+    # recompute [12,14] dX [14,16] dW [16,17]: link-bound, holding the slots
+    # through the pair's recompute costs its time once per pair
+    assert cf.ring_run(4, 2, [dict(b, re_pairs=True)], grad_slots=2) == [17.0]
+    # compute-bound the order costs nothing in this model, which prices a
+    # product by its FLOPs (the pair's gain is in rounds of workgroups)
+    fast = dict(b, t_copy=0.5)
+    assert cf.ring_run(4, 2, [fast], grad_slots=2) == [12.5]
+    assert cf.ring_run(4, 2, [dict(fast, re_pairs=True)], grad_slots=2) == [12.5]
+    # re_pairs without pairs changes nothing
+    assert cf.ring_run(4, 2, [dict(b, pairs=False, re_pairs=True)], grad_slots=2) == \
+        cf.ring_run(4, 2, [dict(b, pairs=False)], grad_slots=2)
+
+
 def test_ring_bytes_reading():
     K, n = 1024, 512
     tile = K * n * 2
