@@ -62,6 +62,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--d2h-cus", type=int, default=None,
                     help="compute units of the device-to-host copy stream (0: unrestricted)")
+    ap.add_argument("--h2d-cus", type=int, default=None,
+                    help="compute units of the host-to-device copy stream (0: unrestricted)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="no second product stream (few-wave forward tiles then run on one stream too)")
     ap.add_argument("--adam", action="store_true",
@@ -91,6 +93,130 @@ def parse():
                     help="summarise the rocprofv3 CSV output under DIR (kernel trace and/or counter "
                          "collection) per kernel and grid size, and exit (no GPU needed)")
     return ap.parse_args()
+
+
+_EPI_NAMES = {0: "lp", 1: "f32", 2: "gelu", 3: "acc", 4: "gelu_f32a"}
+
+
+def kernel_label(name, grid, wg):
+    """Short name of a dispatched kernel and its workgroup count: the GEMM by
+    its template (type, Q and P layouts, epilogue, blocks per wave), the other
+    kernels of the library by name, the rest by the start of their name."""
+    import re
+    groups = grid // max(wg, 1)
+    m = re.search(r"gemm_kernelI(DF16b?)_Lb([01])ELb([01])ELi(\d)ELb([01])ELi(\d+)ELi(\d+)E", name)
+    if m:
+        t = "bf16" if m.group(1) == "DF16b" else "f16"
+        q = "rs" if m.group(2) == "1" else "rc"
+        p = "rs" if m.group(3) == "1" else "rc"
+        epi = _EPI_NAMES.get(int(m.group(4)), m.group(4))
+        ragged = "" if m.group(5) == "1" else ",ragged"
+        return "gemm<%s,%s,%s,%s,%sx%s%s> x%d" % (t, q, p, epi, m.group(6), m.group(7), ragged, groups)
+    for key, label in (("gelu_bwd_kernel", "gelu_bwd"), ("gelu_table_kernel", "gelu_table"),
+                       ("copyBuffer", "__amd_rocclr_copyBuffer"), ("neg_kernel", "neg_kernel")):
+        if key in name:
+            return "%s x%d" % (label, groups)
+    short = name[5:] if name.startswith("void ") else name
+    return "%s x%d" % (short.split("(")[0][:60], groups)
+
+
+def summarize_trace(path):
+    """Per kernel label: counter means/min/max over the dispatches (counter
+    collection CSV) and durations, with the dispatches no other dispatch (or
+    no other kernel of the library) overlapped (kernel trace CSV).  Prints one
+    JSON object {"counters": {...}, "kernels": {...}}."""
+    import csv
+    import glob
+    import json
+    counters, kernels = {}, {}
+    for f in sorted(glob.glob(os.path.join(path, "*counter_collection.csv"))):
+        per = {}  # (label, counter) -> {dispatch: value};  label -> {dispatch: ms}
+        dur = {}
+        for r in csv.DictReader(open(f)):
+            lab = kernel_label(r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+            did = r["Dispatch_Id"]
+            per.setdefault((lab, r["Counter_Name"]), {})
+            per[(lab, r["Counter_Name"])][did] = per[(lab, r["Counter_Name"])].get(did, 0.0) + float(r["Counter_Value"])
+            dur.setdefault(lab, {})[did] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+        for (lab, cn), vals in per.items():
+            v = list(vals.values())
+            counters.setdefault(lab, {})[cn] = {"dispatches": len(v), "mean": sum(v) / len(v), "min": min(v),
+                                                "max": max(v)}
+        for lab, vals in dur.items():
+            v = list(vals.values())
+            counters.setdefault(lab, {})["_dur"] = {"dispatches": len(v), "mean": sum(v) / len(v), "min": min(v),
+                                                    "max": max(v)}
+    for f in sorted(glob.glob(os.path.join(path, "*kernel_trace.csv"))):
+        rows = []
+        for r in csv.DictReader(open(f)):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"].startswith("_ZN2zi"),
+                         kernel_label(r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))))
+        rows.sort()
+        n = len(rows)
+
+        def alone(lib_only):
+            # a dispatch is alone if no other dispatch (of the library, with
+            # lib_only) runs during any part of it: sorted by start, that is no
+            # earlier one ending after its start and the next one starting
+            # before its end
+            out = [False] * n
+            idx = [i for i in range(n) if rows[i][2] or not lib_only]
+            mx = None
+            for a_, i in enumerate(idx):
+                s_, e_ = rows[i][0], rows[i][1]
+                nxt = rows[idx[a_ + 1]][0] if a_ + 1 < len(idx) else None
+                out[i] = (mx is None or mx <= s_) and (nxt is None or nxt >= e_)
+                mx = e_ if mx is None else max(mx, e_)
+            return out
+
+        solo, solo_lib = alone(False), alone(True)
+        for i, (s, e, lib, lab) in enumerate(rows):
+            k = kernels.setdefault(lab, {"dispatches": 0, "ms": 0.0, "solo": 0, "solo_ms": 0.0, "solo_lib": 0,
+                                         "solo_lib_ms": 0.0})
+            ms = (e - s) / 1e6
+            k["dispatches"] += 1
+            k["ms"] += ms
+            if solo[i]:
+                k["solo"] += 1
+                k["solo_ms"] += ms
+            if solo_lib[i] and lib:
+                k["solo_lib"] += 1
+                k["solo_lib_ms"] += ms
+        for k in kernels.values():
+            k["avg_ms"] = k["ms"] / k["dispatches"]
+            k["solo_avg_ms"] = k["solo_ms"] / k["solo"] if k["solo"] else None
+            k["solo_lib_avg_ms"] = k["solo_lib_ms"] / k["solo_lib"] if k["solo_lib"] else None
+    print(json.dumps({"counters": counters, "kernels": kernels}, indent=1, sort_keys=True))
+
+
+def per_step_parts(recs, kind_names, steps):
+    """Each timed step's kernel time by product kind, and its copies' rates,
+    from the context's per-launch records: a step enqueues the same launches
+    and copies in the same order, so the i-th share of each list is step i's
+    (a copy that prefetches the next step's first tile counts with the step
+    that enqueued it)."""
+    ker = [r for r in recs if r["what"] == "kernel"]
+    out = {"kernel_ms": {}, "kernel_span_ms": [], "h2d_GBps": [], "d2h_GBps": []}
+    if steps < 1 or not ker or len(ker) % steps:
+        out["error"] = "launches do not split evenly over the steps"
+        return out
+    per = len(ker) // steps
+    for i in range(steps):
+        part = ker[i * per:(i + 1) * per]
+        for r in part:
+            name = kind_names[r["kind"]] if 0 <= r["kind"] < len(kind_names) else str(r["kind"])
+            out["kernel_ms"].setdefault(name, [0.0] * steps)[i] += r["end_ms"] - r["start_ms"]
+        out["kernel_span_ms"].append(round(max(r["end_ms"] for r in part) - min(r["start_ms"] for r in part), 3))
+    for what in ("h2d", "d2h"):
+        cp = [r for r in recs if r["what"] == what]
+        if cp and len(cp) % steps == 0:
+            per = len(cp) // steps
+            for i in range(steps):
+                part = cp[i * per:(i + 1) * per]
+                ms = sum(r["end_ms"] - r["start_ms"] for r in part)
+                out[what + "_GBps"].append(round(sum(r["rows"] for r in part) / (ms * 1e-3) / 1e9, 2) if ms > 0 else None)
+    out["kernel_ms"] = {k: [round(x, 3) for x in v] for k, v in out["kernel_ms"].items()}
+    return out
 
 
 def copy_probe(torch, nbytes=1 << 30, reps=3):
@@ -354,6 +480,8 @@ def main():
     seed = 0
 
     ctx_kw = {} if args.d2h_cus is None else {"d2h_cus": args.d2h_cus}
+    if args.h2d_cus is not None:
+        ctx_kw["h2d_cus"] = args.h2d_cus
     if args.no_overlap:
         ctx_kw["overlap"] = False
 
@@ -478,6 +606,7 @@ def main():
     step_ms = spans(tev)
     step_clock = sampler.per_step(t0, args.steps)
     st = ctx.stats()
+    step_parts = per_step_parts(ctx.timed_records(), list(st["kinds"]), args.steps)
     ctx.set_timing(False)
 
     ms_step = wall / args.steps * 1e3
@@ -562,6 +691,7 @@ def main():
                      "launches_timed": dom["solo_launches"] or dom["launches"],
                      "traffic": measured_traffic(config, dom["kernel"])},
         "step_clock": {"source": sampler.source, "error": sampler.error, "per_step": step_clock},
+        "step_parts": step_parts,
     }
     if config["workload"] == "ffn_block_fwd_recompute_bwd":
         # the recomputed forward is work the step repeats; without it 7PT

@@ -406,6 +406,23 @@ zi_status zi_ctx_set_debug(zi_ctx *ctx, uint32_t flags, uint32_t copy_delay_us);
 zi_status zi_ctx_reset_stats(zi_ctx *ctx);
 zi_status zi_ctx_stats(zi_ctx *ctx, zi_stats *out);
 
+/* One timed launch or copy: what it was, and when it ran, in ms after the
+ * first timed event of the context (since the last reset). */
+typedef struct {
+    int32_t what;                /* 0: kernel, 1: host-to-device copy, 2: device-to-host copy */
+    int32_t kind;                /* kernels: index into zi_stats.kind_name; copies: -1 */
+    int64_t rows, cols, red;     /* kernels: as zi_kernel_stats; copies: rows = bytes, cols = red = 0 */
+    double start_ms, end_ms;
+} zi_timed_rec;
+/* The launches and copies timed since the last reset (zi_ctx_set_timing),
+ * kernels in launch order, then copies in enqueue order, for attributing a
+ * step's time to its products and copies step by step (the per-step view that
+ * zi_ctx_stats' totals do not give).  Waits for the context's work like
+ * zi_ctx_stats.  Writes at most cap records to out (out may be NULL with
+ * cap = 0) and the total in *count.  ZI_ERR_ARG on a NULL ctx or count, a
+ * negative cap, or a NULL out with cap > 0. */
+zi_status zi_ctx_timed_records(zi_ctx *ctx, zi_timed_rec *out, int32_t cap, int32_t *count);
+
 /* A new non-blocking stream of default priority, owned by the caller (release
  * with zi_stream_destroy).  The HIP runtime multiplexes streams onto a few
  * hardware queues; when the product stream and a copy stream share a queue, a

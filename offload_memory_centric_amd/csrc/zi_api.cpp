@@ -952,4 +952,32 @@ zi_status zi_ctx_stats(zi_ctx *ctx, zi_stats *out) {
     return ZI_OK;
 }
 
+zi_status zi_ctx_timed_records(zi_ctx *ctx, zi_timed_rec *out, int32_t cap, int32_t *count) {
+    clear_error();
+    if (!ctx || !count) return fail(ZI_ERR_ARG, "ctx and count are required");
+    if (cap < 0 || (cap > 0 && !out)) return fail(ZI_ERR_ARG, "out must hold cap = %d records", cap);
+    zi_status st = zi_sync(ctx);
+    if (st != ZI_OK) return st;
+    const size_t total = ctx->krec.size() + ctx->crec.size();
+    *count = total > (size_t)INT32_MAX ? INT32_MAX : (int32_t)total;
+    hipEvent_t ref = nullptr;
+    if (!ctx->krec.empty()) ref = ctx->krec.front().a;
+    if (!ctx->crec.empty() && !ref) ref = ctx->crec.front().a;
+    int32_t n = 0;
+    auto put = [&](int32_t what, int32_t kind, int64_t rows, int64_t cols, int64_t red, hipEvent_t a,
+                   hipEvent_t b) -> zi_status {
+        if (n >= cap) return ZI_OK;
+        float t0 = 0, t1 = 0;
+        HIPCHK(ctx, hipEventElapsedTime(&t0, ref, a));
+        HIPCHK(ctx, hipEventElapsedTime(&t1, ref, b));
+        out[n++] = zi_timed_rec{what, kind, rows, cols, red, (double)t0, (double)t1};
+        return ZI_OK;
+    };
+    for (const KernelRec &r : ctx->krec)
+        if ((st = put(0, r.kind, r.rows, r.cols, r.red, r.a, r.b)) != ZI_OK) return st;
+    for (const CopyRec &r : ctx->crec)
+        if ((st = put(r.d2h ? 2 : 1, -1, (int64_t)r.bytes, 0, 0, r.a, r.b)) != ZI_OK) return st;
+    return ZI_OK;
+}
+
 }  // extern "C"

@@ -89,8 +89,16 @@ def _out(plan) -> tuple:
     return (torch.float32,) if plan.f32_out else _lp(plan)
 
 
-# Compute units the device-to-host copy stream may use (see zi_copy_stream_create).
+# Compute units the copy streams may use (see zi_copy_stream_create).  The HIP
+# runtime carries out some host<->device copies as copy kernels rather than on
+# a DMA engine; on an unconfined stream those take compute units from the
+# products running beside them.  Measured on the FFN block at T = 32768 over
+# 20 steps: with the host-to-device stream unconfined, runs fell after 12-19
+# steps into steps 22-28 % longer, the products that overlap a tile copy
+# 35-40 % slower and the copy rate down from 56 to 36-40 GB/s; confined to 8
+# compute units (one per XCD), every step held at the same time.
 D2H_CUS = 8
+H2D_CUS = 8
 
 
 class Context:
@@ -98,8 +106,8 @@ class Context:
 
     By default the context creates its own three streams, one after another, so
     that they sit on distinct hardware queues (see zi_stream_create): products,
-    host-to-device copies, and device-to-host copies confined to ``d2h_cus``
-    compute units (0: unconfined).  With ``overlap`` (the default) it also
+    host-to-device copies confined to ``h2d_cus`` compute units, and
+    device-to-host copies confined to ``d2h_cus`` (0: unconfined).  With ``overlap`` (the default) it also
     makes a second product stream, on which forward passes whose tiles take
     few workgroup waves run every other tile's product.  The products do not run on torch's current stream: inputs
     must be complete before a call (torch.cuda.synchronize()), and outputs are
@@ -107,14 +115,14 @@ class Context:
     """
 
     def __init__(self, plan: Plan, device: str = "cuda", workspace_bytes: Optional[int] = None,
-                 streams=None, d2h_cus: int = D2H_CUS, overlap: bool = True):
+                 streams=None, d2h_cus: int = D2H_CUS, overlap: bool = True, h2d_cus: int = H2D_CUS):
         nbytes = int(workspace_bytes if workspace_bytes is not None else plan.info.ring_bytes)
         self.handle = None
         self._own_streams = []
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         if streams is None:
-            for _ in range(2):
-                self._own_streams.append(zi.zi_stream_create())
+            self._own_streams.append(zi.zi_stream_create())
+            self._own_streams.append(zi.zi_copy_stream_create(h2d_cus) if h2d_cus else zi.zi_stream_create())
             self._own_streams.append(zi.zi_copy_stream_create(d2h_cus) if d2h_cus else zi.zi_stream_create())
             streams = tuple(self._own_streams)
         self.streams = streams
@@ -189,6 +197,9 @@ class Context:
 
     def stats(self) -> dict:
         return zi.zi_ctx_stats(self.handle).as_dict()
+
+    def timed_records(self) -> list:
+        return zi.zi_ctx_timed_records(self.handle)
 
     def close(self):
         if self.handle:

@@ -135,6 +135,12 @@ class zi_stats(ctypes.Structure):
                 "kernels": [self.kernel[i].as_dict() for i in range(self.kernel_count)]}
 
 
+class zi_timed_rec(ctypes.Structure):
+    _fields_ = [("what", ctypes.c_int32), ("kind", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("red", ctypes.c_int64), ("start_ms", ctypes.c_double),
+                ("end_ms", ctypes.c_double)]
+
+
 if not os.path.exists(LIB_PATH):
     raise ImportError("libzi.so is not built (expected at %s); run "
                       "`python -m offload_memory_centric_amd.build`" % LIB_PATH)
@@ -171,6 +177,7 @@ _sigs = {
     "zi_ctx_set_second_stream": (_S, [_P, _P]),
     "zi_ctx_reset_stats": (_S, [_P]),
     "zi_ctx_stats": (_S, [_P, ctypes.POINTER(zi_stats)]),
+    "zi_ctx_timed_records": (_S, [_P, ctypes.POINTER(zi_timed_rec), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     "zi_stream_create": (_S, [ctypes.POINTER(_P)]),
     "zi_copy_stream_create": (_S, [ctypes.c_int32, ctypes.POINTER(_P)]),
     "zi_stream_destroy": (_S, [_P]),
@@ -375,6 +382,19 @@ def zi_ctx_stats(ctx) -> zi_stats:
     out = zi_stats()
     _check(_lib.zi_ctx_stats(ctx, ctypes.byref(out)))
     return out
+
+
+def zi_ctx_timed_records(ctx) -> list:
+    """Every launch and copy timed since the last reset: dicts with what
+    ("kernel", "h2d", "d2h"), kind (index into the stats' kinds, -1 for
+    copies), rows, cols, red (copies: rows = bytes), start_ms, end_ms."""
+    n = ctypes.c_int32(0)
+    _check(_lib.zi_ctx_timed_records(ctx, None, 0, ctypes.byref(n)))
+    buf = (zi_timed_rec * max(n.value, 1))()
+    _check(_lib.zi_ctx_timed_records(ctx, buf, n.value, ctypes.byref(n)))
+    names = ("kernel", "h2d", "d2h")
+    return [{"what": names[r.what], "kind": r.kind, "rows": r.rows, "cols": r.cols, "red": r.red,
+             "start_ms": r.start_ms, "end_ms": r.end_ms} for r in buf[:n.value]]
 
 
 def zi_adam_update(hp: zi_adam_hparams, dtype: int, grad_f32: int, step: int, count: int, grad, master, m, v,

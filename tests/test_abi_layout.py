@@ -11,7 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 STRUCTS = ["zi_problem", "zi_plan_info", "zi_prediction", "zi_rate_curve", "zi_choice", "zi_kernel_stats",
-           "zi_stats", "zi_adam_hparams", "zi_adam_stats", "zi_source_stats", "zi_tier_stats"]
+           "zi_stats", "zi_timed_rec", "zi_adam_hparams", "zi_adam_stats", "zi_source_stats", "zi_tier_stats"]
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")

@@ -104,3 +104,41 @@ def test_copy_delay_shows_as_stall_and_matches_the_model():
     assert abs(pred.t_pass_s * 1e3 - (st["span_ms"] + delay / 1000.0)) < 0.25 * pred.t_pass_s * 1e3
     ctx.close()
     plan.close()
+
+
+def test_timed_records_match_the_totals():
+    # the per-launch records add up to zi_ctx_stats' totals, kernels in launch
+    # order, copies after them, every interval inside the timed span
+    T, K, M, N, d = 256, 512, 2048, 4, 2
+    tiling = lib()
+    say("case timed records")
+    X, Wt, dY = make_linear_inputs(T, K, M, "f16", "small_int", seed=13)
+    dWt = tiling.host_tensor((M, K), torch.float16)
+    plan = tiling.Plan(T, K, M, N, d, "f16", Wt, dWt)
+    ctx = tiling.Context(plan)
+    Y = torch.empty((T, M), dtype=torch.float16, device="cuda")
+    dX = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    ctx.set_timing(True)
+    ctx.reset_stats()
+    ctx.fwd(plan, X, Y)
+    ctx.bwd(plan, X, dY, dX)
+    st = ctx.stats()
+    recs = ctx.timed_records()
+    ctx.set_timing(False)
+    kinds = list(st["kinds"])
+    ker = [r for r in recs if r["what"] == "kernel"]
+    assert len(ker) == sum(v["launches"] for v in st["kinds"].values())
+    assert [r["what"] for r in recs] == ["kernel"] * len(ker) + [r["what"] for r in recs[len(ker):]]
+    assert sum(1 for r in recs if r["what"] == "h2d") == st["h2d_copies"] == 2 * N
+    assert sum(1 for r in recs if r["what"] == "d2h") == st["d2h_copies"] == N
+    assert sum(r["rows"] for r in recs if r["what"] == "h2d") == st["h2d_bytes"]
+    for name, v in st["kinds"].items():
+        ms = sum(r["end_ms"] - r["start_ms"] for r in ker if kinds[r["kind"]] == name)
+        assert ms == pytest.approx(v["ms"], rel=1e-6, abs=1e-6), name
+    lo = min(r["start_ms"] for r in recs)
+    hi = max(r["end_ms"] for r in recs)
+    assert all(r["end_ms"] >= r["start_ms"] for r in recs)
+    assert hi - lo == pytest.approx(st["span_ms"], rel=1e-6, abs=1e-6)
+    assert [kinds[r["kind"]] for r in ker[:N]] == ["gemm_fwd"] * N
+    ctx.close()
+    plan.close()

@@ -210,14 +210,14 @@ def test_gradient_in_weight_slot_matches_separate_slots():
     assert err <= 1e-5 * ins["dX"].abs().max().item(), err
 
 
-@pytest.mark.parametrize("d2h_cus", [0, 8, 32])
-def test_device_to_host_stream_confinement(d2h_cus):
-    # the dW write-back stream confined to 8 or 32 compute units, or a plain
-    # torch stream (0): the same exact results
+@pytest.mark.parametrize("h2d_cus,d2h_cus", [(8, 0), (8, 8), (8, 32), (0, 8), (16, 16)])
+def test_copy_stream_confinement(h2d_cus, d2h_cus):
+    # the tile copy and dW write-back streams confined to 8, 16 or 32 compute
+    # units, or unconfined (0): the same exact results
     T, K, M, N, d = 128, 512, 2048, 4, 2
-    say("case d2h stream cus", d2h_cus)
+    say("case copy stream cus", h2d_cus, d2h_cus)
     X, Wt, dY = make_linear_inputs(T, K, M, "f16", "small_int", seed=6)
-    r = run_fwd_bwd(T, K, M, N, d, "f16", X, Wt, dY, d2h_cus=d2h_cus)
+    r = run_fwd_bwd(T, K, M, N, d, "f16", X, Wt, dY, h2d_cus=h2d_cus, d2h_cus=d2h_cus)
     Y, dX, dWt = oracle_linear(X, Wt, dY, "f16")
     assert np.array_equal(host_bits(r["Y"]), oracle.encode(Y, "f16"))
     assert np.array_equal(r["dX"].cpu().numpy().astype(np.float64), dX)

@@ -133,7 +133,8 @@ def test_null_arguments_are_rejected_without_a_gpu(zi):
     lib.zi_plan_tiles.argtypes = [ctypes.c_void_p] * 3
     assert lib.zi_plan_tiles(None, None, None) == zi.ZI_ERR_ARG
     for name, nargs in [("zi_tiled_linear_fwd", 4), ("zi_tiled_linear_bwd", 5), ("zi_tiled_linear_fwd_gelu", 5),
-                        ("zi_tiled_linear_bwd_recompute", 6), ("zi_sync", 1), ("zi_ctx_stats", 2)]:
+                        ("zi_tiled_linear_bwd_recompute", 6), ("zi_sync", 1), ("zi_ctx_stats", 2),
+                        ("zi_ctx_timed_records", 4)]:
         f = getattr(lib, name)
         f.argtypes = [ctypes.c_void_p] * nargs
         assert f(*([None] * nargs)) == zi.ZI_ERR_ARG, name
