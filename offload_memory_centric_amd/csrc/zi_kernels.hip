@@ -577,6 +577,8 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     // unit idles.
     const int64_t ksteps = (a.red + BK - 1) / BK;
     const int32_t red = (int32_t)a.red;  // below 2^30 (the host checks)
+    // slot of unit u (used for the first five units; the ring below rotates
+    // from there)
     auto slot = [&](int u) __attribute__((always_inline)) -> char * {
         if constexpr (MIXED) {
             return lds + (u % 5) * UF;
@@ -586,7 +588,7 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
         }
     };
     // The next step of the first / second operand to copy (in step order).
-    constexpr bool SPLIT = EPI == EPI_ACC;  // only the input-gradient product reads two weight tiles
+    constexpr bool SPLIT = EPI == EPI_ACC;  // only the input-gradient product splits its reduction over two tiles
     auto take_f = [&](int32_t &k0) __attribute__((always_inline)) -> rsrc_t {
         if constexpr (Q_FIRST) return qo.template take<ALIGNED, SPLIT>(red, k0);
         else return po.template take<ALIGNED, false>(red, k0);
