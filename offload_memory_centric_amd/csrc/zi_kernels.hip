@@ -469,14 +469,17 @@ __device__ __forceinline__ float gelu_grad_f32(float a) {
 // XCD w % 8, as its (w / 8)-th).  XCD x is given a contiguous range of tiles,
 // [x q + min(x, r), ...) of q + (x < r) tiles (nt = 8 q + r), so the
 // workgroups that share an L2 also share operand tiles; inside a range, tiles
-// go in column groups 8 macro-rows tall (8 P tiles reuse one Q tile, 8
-// consecutive groups reuse P).
+// go in column groups G macro-rows tall (G P tiles reuse one Q tile, the
+// consecutive groups reuse P).  G is set per product by measurement on the
+// FFN block at T = 32768: 4 for the forward and input-gradient products
+// (against 8: +1-2 % each, the down-projection's forward +10 %), 8 for the
+// weight-gradient products (4 lost 1-2.5 %; 16 lost on every product).
+template <int G>
 __device__ __forceinline__ void tile_coords(int w, int tiles_p, int tiles_q, int &tp, int &tq) {
     const int nt = tiles_p * tiles_q;
     const int x = w & 7, k = w >> 3;
     const int q8 = nt >> 3, r8 = nt & 7;
     const int t = x * q8 + min(x, r8) + k;
-    constexpr int G = 8;
     const int per_group = G * tiles_q;
     const int g = t / per_group;
     const int first = g * G;
@@ -550,7 +553,7 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     const int wp = wave >> 1;
 
     int tp, tq;
-    tile_coords(blockIdx.x, tiles_p, tiles_q, tp, tq);
+    tile_coords<(Q_RS && P_RS) ? 8 : 4>(blockIdx.x, tiles_p, tiles_q, tp, tq);
     const int64_t p0 = (int64_t)tp * TP;
     const int64_t q0 = (int64_t)tq * TQ;
 
