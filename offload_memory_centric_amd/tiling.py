@@ -91,14 +91,13 @@ def _out(plan) -> tuple:
 
 # Compute units the copy streams may use (see zi_copy_stream_create).  The HIP
 # runtime carries out some host<->device copies as copy kernels rather than on
-# a DMA engine; on an unconfined stream those take compute units from the
-# products running beside them.  Measured on the FFN block at T = 32768 over
-# 20 steps: with the host-to-device stream unconfined, runs fell after 12-19
-# steps into steps 22-28 % longer, the products that overlap a tile copy
-# 35-40 % slower and the copy rate down from 56 to 36-40 GB/s; confined to 8
-# compute units (one per XCD), every step held at the same time.
+# a DMA engine.  The device-to-host stream is confined to 8 compute units (one
+# per XCD); the host-to-device stream is unconfined by default: runs of the FFN
+# block with every copy forced onto copy kernels (HSA_ENABLE_SDMA=0) took the
+# same time with that stream confined to 8 compute units or not, so the
+# runtime's copy kernels for it do not keep to the stream's mask.
 D2H_CUS = 8
-H2D_CUS = 8
+H2D_CUS = 0
 
 
 class Context:
@@ -106,8 +105,8 @@ class Context:
 
     By default the context creates its own three streams, one after another, so
     that they sit on distinct hardware queues (see zi_stream_create): products,
-    host-to-device copies confined to ``h2d_cus`` compute units, and
-    device-to-host copies confined to ``d2h_cus`` (0: unconfined).  With ``overlap`` (the default) it also
+    host-to-device copies (confined to ``h2d_cus`` compute units if nonzero),
+    and device-to-host copies confined to ``d2h_cus`` (0: unconfined).  With ``overlap`` (the default) it also
     makes a second product stream, on which forward passes whose tiles take
     few workgroup waves run every other tile's product.  The products do not run on torch's current stream: inputs
     must be complete before a call (torch.cuda.synchronize()), and outputs are
