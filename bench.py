@@ -64,6 +64,15 @@ def parse():
                     help="compute units of the device-to-host copy stream (0: unrestricted)")
     ap.add_argument("--h2d-cus", type=int, default=None,
                     help="compute units of the host-to-device copy stream (0: unrestricted)")
+    ap.add_argument("--max-ahead", type=int, default=0,
+                    help="steps the host may enqueue ahead of the device (0: no limit)")
+    ap.add_argument("--unbounded-enqueue", dest="ahead_mid", action="store_false",
+                    help="enqueue every step at once (default: each step once the previous one has "
+                         "reached its middle: the down-projection's backward done, or the linear's "
+                         "forward)")
+    ap.add_argument("--ahead-poll", type=float, default=0.0,
+                    help="with --max-ahead: poll the step's end event every this many ms instead of "
+                         "waiting on it")
     ap.add_argument("--no-overlap", action="store_true",
                     help="no second product stream (few-wave forward tiles then run on one stream too)")
     ap.add_argument("--adam", action="store_true",
@@ -513,8 +522,8 @@ def main():
         flops_step = 8.0 * P * T
         h2d_bytes_step = 2.0 * (3 * D * F + 2 * D * F)
 
-        def step():
-            tiling.ffn_block_step(ctx, p1, p2, X, A, H, Y, dY, dH, dA, dX, Yr)
+        def step(mid=None):
+            tiling.ffn_block_step(ctx, p1, p2, X, A, H, Y, dY, dH, dA, dX, Yr, mid=mid)
 
         config = {"workload": "ffn_block_fwd_recompute_bwd", "T": T, "d_model": D, "d_ff": F,
                   "N_up": N1, "N_down": N2, "n_up": F // N1, "n_down": D // N2, "d": d,
@@ -539,8 +548,10 @@ def main():
         flops_step = 6.0 * T * K * M
         h2d_bytes_step = 2.0 * K * M * 2
 
-        def step():
+        def step(mid=None):
             ctx.fwd(p, X, Y)
+            if mid is not None:
+                mid()
             ctx.bwd(p, X, dY, dX)
 
         config = {"workload": "tiled_linear_fwd_bwd", "T": T, "K": K, "M": M, "N": N, "n": M // N,
@@ -558,22 +569,40 @@ def main():
         if tier is not None:
             pass_step = step
 
-            def step():
-                pass_step()
+            def step(mid=None):
+                pass_step(mid)
                 tier.step()
     torch.cuda.synchronize()
 
-    # Per-step marks: an event on the compute stream after every step (no
-    # host synchronisation, so the ring's prefetch still crosses steps).
+    # Per-step marks: an event on the compute stream after every step.  The
+    # host enqueues step i once step i - 1 has reached its middle, so the
+    # ring's prefetch still crosses steps while about one step is in flight
+    # (as in a training loop that reads its loss every step).  With every step
+    # enqueued at once the HIP runtime was seen, after 12-19 steps, to carry
+    # the tile copies out at 36-40 GB/s as copy kernels beside the products
+    # (steps 15-40 % longer), and with two or more whole steps in flight to
+    # stall write-backs at 13 GB/s; one step or less in flight avoided both.
     comp = torch.cuda.ExternalStream(ctx.streams[0])
 
     def marked(n, sampler=None):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         if sampler is not None:
             sampler.watch(ev)
+        mids = [torch.cuda.Event() for _ in range(n)]
         ev[0].record(comp)
         for i in range(n):
-            step()
+            e = None
+            if args.ahead_mid and i >= 1:
+                e = mids[i - 1]
+            elif args.max_ahead and i >= args.max_ahead:
+                e = ev[i - args.max_ahead + 1]
+            if e is not None:
+                if args.ahead_poll:
+                    while not e.query():
+                        time.sleep(args.ahead_poll * 1e-3)
+                else:
+                    e.synchronize()
+            step(mid=lambda: mids[i].record(comp))
             ev[i + 1].record(comp)
             if sampler is not None:
                 sampler.mark_recorded(i + 1)
@@ -692,6 +721,8 @@ def main():
                      "traffic": measured_traffic(config, dom["kernel"])},
         "step_clock": {"source": sampler.source, "error": sampler.error, "per_step": step_clock},
         "step_parts": step_parts,
+        "host_enqueue": ("each step once the previous one reached its middle" if args.ahead_mid
+                         else ("at most %d steps ahead" % args.max_ahead if args.max_ahead else "unbounded")),
     }
     if config["workload"] == "ffn_block_fwd_recompute_bwd":
         # the recomputed forward is work the step repeats; without it 7PT

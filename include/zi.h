@@ -339,7 +339,13 @@ zi_status zi_tiled_linear_fwd_noalloc(const zi_plan *plan, const void *X_dev, vo
  * products (transformer-math page, section "Prefetch depth: how far ahead the
  * pipeline must run"; pwwt.cn article, section "关键技术三：Overlap-Centric
  * Design"); this is the one point at which the host waits for them.  After
- * ZI_OK every output of the enqueued passes, device and host, may be read. */
+ * ZI_OK every output of the enqueued passes, device and host, may be read.
+ * How far ahead a caller enqueues is its own choice, but keep it to about one
+ * training step: with many steps of passes enqueued at once the HIP runtime
+ * was seen, after a while, to carry the tile copies out as copy kernels that
+ * take compute units from the products (steps 15-40 % longer), and with two
+ * or more whole steps in flight to stall write-backs; enqueueing a step once
+ * the previous one has reached its middle kept every step steady. */
 zi_status zi_sync(zi_ctx *ctx);
 
 /* Per-context timing (off by default).  When on, every kernel launch and

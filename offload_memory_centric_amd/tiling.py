@@ -319,14 +319,18 @@ def write_weight_file(path: str, W_host: torch.Tensor, chunk_bytes: int = 1 << 2
             f.write(flat[at:at + chunk_bytes].numpy())
 
 
-def ffn_block_step(ctx: Context, p1: Plan, p2: Plan, X, A, H, Y, dY, dH, dA, dX, Yr) -> None:
+def ffn_block_step(ctx: Context, p1: Plan, p2: Plan, X, A, H, Y, dY, dH, dA, dX, Yr, mid=None) -> None:
     """The feed-forward block with activation checkpointing, enqueued without
     host synchronisation (the ring carries prefetch across the calls):
     forward W1 (+GeLU), forward W2, recomputed forward W1 (+GeLU), backward W2
-    with the recomputed W2 product, dA = dH * GeLU'(A), backward W1."""
+    with the recomputed W2 product, dA = dH * GeLU'(A), backward W1.  mid, if
+    given, is called once the down-projection's backward is enqueued (a caller
+    can mark that point on the product stream)."""
     ctx.fwd_gelu(p1, X, A, H)
     ctx.fwd(p2, H, Y)
     ctx.fwd_gelu(p1, X, A, H)
     ctx.bwd_recompute(p2, H, dY, dH, Yr)
+    if mid is not None:
+        mid()
     ctx.gelu_bwd(p1.dtype, dH, A, dA, A.numel())
     ctx.bwd(p1, X, dA, dX)
