@@ -64,6 +64,9 @@ def parse():
                     help="compute units of the device-to-host copy stream (0: unrestricted)")
     ap.add_argument("--h2d-cus", type=int, default=None,
                     help="compute units of the host-to-device copy stream (0: unrestricted)")
+    ap.add_argument("--dx-per-tile", action="store_true",
+                    help="run the dX products one workgroup per output block instead of one persistent "
+                         "workgroup per compute unit (to compare the two forms)")
     ap.add_argument("--max-ahead", type=int, default=0,
                     help="steps the host may enqueue ahead of the device (0: no limit)")
     ap.add_argument("--unbounded-enqueue", dest="ahead_mid", action="store_false",
@@ -511,6 +514,8 @@ def main():
         p1 = tiling.Plan(T, D, F, N1, d, dtype, W1t, dW1t)
         p2 = tiling.Plan(T, F, D, N2, d, dtype, W2t, dW2t)
         ctx = tiling.Context(p1 if p1.info.ring_bytes >= p2.info.ring_bytes else p2, **ctx_kw)
+        if args.dx_per_tile:
+            ctx.set_debug(dx_per_tile=True)
         A = torch.empty((T, F), dtype=tdt, device="cuda")
         H = torch.empty_like(A)
         dA = torch.empty_like(A)
@@ -543,6 +548,8 @@ def main():
         budget = int(args.budget_tiles * tile_bytes)
         p = tiling.Plan(T, K, M, N, d, dtype, Wt, dWt, budget=budget)
         ctx = tiling.Context(p, **ctx_kw)
+        if args.dx_per_tile:
+            ctx.set_debug(dx_per_tile=True)
         Y = torch.empty((T, M), dtype=tdt, device="cuda")
         dX = torch.empty((T, K), dtype=torch.float32, device="cuda")
         flops_step = 6.0 * T * K * M
@@ -560,6 +567,8 @@ def main():
             config.update({"budget_tiles": args.budget_tiles, "budget_bytes": budget,
                            "gradient_slots": p.info.dw_slots, "ring_bytes": p.info.ring_bytes})
         plans = (p,)
+    if args.dx_per_tile:
+        config["dx_form"] = "one workgroup per output block"
     sources, tier = [], None
     if args.nvme:
         if args.adam:

@@ -408,6 +408,12 @@ zi_status zi_ctx_set_second_stream(zi_ctx *ctx, void *stream);
  * ring can tell.  Both cost time; they are for tests.  ZI_ERR_ARG on unknown
  * flags or a longer delay. */
 #define ZI_DEBUG_POISON 0x1u
+/* ZI_DEBUG_DX_PER_TILE: dX products run one workgroup per 256 x 256 output
+ * block, instead of one persistent workgroup per compute unit that takes
+ * its blocks in turn and moves the next block's first copies and its C
+ * under the stores of the last (the results are identical; the switch is
+ * there to compare the two forms). */
+#define ZI_DEBUG_DX_PER_TILE 0x2u
 zi_status zi_ctx_set_debug(zi_ctx *ctx, uint32_t flags, uint32_t copy_delay_us);
 zi_status zi_ctx_reset_stats(zi_ctx *ctx);
 zi_status zi_ctx_stats(zi_ctx *ctx, zi_stats *out);

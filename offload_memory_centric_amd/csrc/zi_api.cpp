@@ -444,6 +444,8 @@ zi_status run_bwd(zi_ctx *c, const zi_plan *p, const void *X, const void *dY, fl
             a.cols = pr.K;
             a.red = (i - i0 + 1) * n;
             a.accumulate = i0 > 0 ? 1 : 0;
+            // one persistent workgroup per compute unit
+            a.wg_cap = (c->debug & ZI_DEBUG_DX_PER_TILE) ? 0 : std::max(8, c->cus / 8 * 8);
             if ((st = gemm(c, K_DX, GemmOp::Dx, pr.dtype, a, tile_flops * (double)(i - i0 + 1))) != ZI_OK)
                 return st;
         }
@@ -812,7 +814,7 @@ zi_status zi_ctx_set_second_stream(zi_ctx *ctx, void *stream) {
 zi_status zi_ctx_set_debug(zi_ctx *ctx, uint32_t flags, uint32_t copy_delay_us) {
     clear_error();
     if (!ctx) return fail(ZI_ERR_ARG, "context is NULL");
-    if (flags & ~ZI_DEBUG_POISON) return fail(ZI_ERR_ARG, "unknown debug flags 0x%x", flags);
+    if (flags & ~(ZI_DEBUG_POISON | ZI_DEBUG_DX_PER_TILE)) return fail(ZI_ERR_ARG, "unknown debug flags 0x%x", flags);
     if (copy_delay_us > 10000000u) return fail(ZI_ERR_ARG, "copy delay above 10 s");
     ctx->debug = flags;
     ctx->delay_us = copy_delay_us;

@@ -36,6 +36,10 @@ struct GemmArgs {
     // launch's macro-tile width (gemm_tile).  Q2 = null: no split.
     const void *Q2;
     int64_t qsplit;
+    // Dx: at most this many workgroups (a multiple of 8), each taking several
+    // output tiles in turn, the next tile's first copies and C loads issued
+    // under the finished tile's stores; 0 = one workgroup per output tile.
+    int32_t wg_cap;
 };
 
 // dtype: 1 = fp16, 2 = bf16.  Returns the launch status (hipGetLastError).

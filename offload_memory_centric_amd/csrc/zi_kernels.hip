@@ -522,13 +522,19 @@ __device__ constexpr int copy_at(int m) {
 //   (10, 6)  320 x 192, forward products whose q extent (the tile width) is
 //            a multiple of 320 but not of 256 (the down-projection's 1600);
 //   (6, 10)  192 x 320, gradient products whose p extent is such a width.
-template <typename T, bool Q_RS, bool P_RS, int EPI, bool ALIGNED, int QB, int PB>
+// PERSIST (accumulating products only): a workgroup takes the output tiles
+// of workgroup indices w, w + G, w + 2G, ... (G = the grid, a multiple of 8,
+// so all of them fall on the XCD of w and keep its tile order); between two
+// tiles the next one's first operand units are copied and its C loaded while
+// the finished one's accumulators are stored.
+template <typename T, bool Q_RS, bool P_RS, int EPI, bool ALIGNED, int QB, int PB, bool PERSIST>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     constexpr int TQ = 32 * QB, TP = 32 * PB;
     static_assert(QB * PB <= 64, "accumulators beyond the 256 AGPRs of a lane");
     static_assert((EPI != EPI_ACC && EPI != EPI_GELU && EPI != EPI_GELU_F32A) || (QB == 8 && PB == 8),
                   "the accumulating and GeLU epilogues are built for the 256 x 256 tile");
+    static_assert(!PERSIST || EPI == EPI_ACC, "only the accumulating product runs persistent workgroups");
     using QOp = OperandT<Q_RS, TQ>;
     using POp = OperandT<P_RS, TP>;
     // LDS ring.  Each step's two units are issued first-operand first; the
@@ -552,25 +558,36 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     const int wq = wave & 1;
     const int wp = wave >> 1;
 
-    int tp, tq;
-    tile_coords<(Q_RS && P_RS) ? 8 : 4>(blockIdx.x, tiles_p, tiles_q, tp, tq);
-    const int64_t p0 = (int64_t)tp * TP;
-    const int64_t q0 = (int64_t)tq * TQ;
-
+    int w = blockIdx.x;  // workgroup index of the current output tile
+    int64_t p0, q0;      // its first output row and column
     QOp qo;
     POp po;
-    if constexpr (Q_RS) {
-        qo.init(static_cast<const uint16_t *>(a.Q), a.ldq, q0, a.cols, wave, lane);
-        qo.set_split(a.Q2, a.qsplit, q0);
-    } else {
-        // a forward product over two weight tiles: columns from qsplit on
-        // are rows of Q2 (qsplit is a multiple of the macro-tile's width, so
-        // a workgroup reads one tile)
-        const bool second = a.Q2 && q0 >= a.qsplit;
-        qo.init(static_cast<const uint16_t *>(second ? a.Q2 : a.Q), a.ldq, second ? q0 - a.qsplit : q0,
-                second ? a.cols - a.qsplit : a.cols, wave, lane);
-    }
-    po.init(static_cast<const uint16_t *>(a.P), a.ldp, p0, a.rows, wave, lane);
+    // The operands of the output tile of workgroup index wi, their copy
+    // cursors at the first step.  (ln is the lane index; a persistent
+    // workgroup passes it through an opaque copy, so that the per-lane
+    // offsets are formed anew for each tile rather than kept, or spilled,
+    // across the main loop.)
+    auto setup = [&](int wi, int ln) __attribute__((always_inline)) {
+        int tp, tq;
+        tile_coords<(Q_RS && P_RS) ? 8 : 4>(wi, tiles_p, tiles_q, tp, tq);
+        p0 = (int64_t)tp * TP;
+        q0 = (int64_t)tq * TQ;
+        if constexpr (Q_RS) {
+            qo.init(static_cast<const uint16_t *>(a.Q), a.ldq, q0, a.cols, wave, ln);
+            qo.set_split(a.Q2, a.qsplit, q0);
+        } else {
+            // a forward product over two weight tiles: columns from qsplit on
+            // are rows of Q2 (qsplit is a multiple of the macro-tile's width, so
+            // a workgroup reads one tile)
+            const bool second = a.Q2 && q0 >= a.qsplit;
+            qo.init(static_cast<const uint16_t *>(second ? a.Q2 : a.Q), a.ldq, second ? q0 - a.qsplit : q0,
+                    second ? a.cols - a.qsplit : a.cols, wave, ln);
+        }
+        po.init(static_cast<const uint16_t *>(a.P), a.ldp, p0, a.rows, wave, ln);
+        qo.init_cursor();
+        po.init_cursor();
+    };
+    setup(w, lane);
     qo.init_reads(wq, lane);
     po.init_reads(wp, lane);
 
@@ -610,8 +627,6 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
         if constexpr (Q_FIRST) po.template issue<ALIGNED>(rs, k0, red, unit + ws, wave, lane, j);
         else qo.template issue<ALIGNED>(rs, k0, red, unit + ws, wave, lane, j);
     };
-    qo.init_cursor();
-    po.init_cursor();
 
     using QBs = typename QOp::Bases;
     using PBs = typename POp::Bases;
@@ -627,22 +642,30 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     // steps' units (vmcnt counts loads in issue order) covers it too.  Row
     // block j has its own descriptor, so a lane offset stays below
     // 16 ldc + 256 elements (the host keeps that under the descriptor's range).
-    const int64_t pb = p0 + wp * (16 * PB) + (lane & 15);
-    const int64_t qb = q0 + wq * (16 * QB) + 4 * (lane >> 4);
+    // c_rsrc / c_off: that descriptor (records = 0: every read gives zero) and
+    // this lane's offset of block (i, j) in the tile at (p0_, q0_), kOOB
+    // outside C (a load reads zero there and a store is dropped).
+    auto c_rsrc = [&](int64_t p0_, int64_t q0_, int j, bool live) __attribute__((always_inline)) -> rsrc_t {
+        const int64_t prow = p0_ + wp * (16 * PB) + 16 * j;
+        return make_rsrc(reinterpret_cast<const char *>(static_cast<const float *>(a.C) + prow * a.ldc + q0_),
+                         live ? kNumRecords : 0u);
+    };
+    auto c_off = [&](int64_t p0_, int64_t q0_, int i, int j, int ln) __attribute__((always_inline)) -> uint32_t {
+        const int64_t p = p0_ + wp * (16 * PB) + (ln & 15) + 16 * j;
+        const int64_t q = q0_ + wq * (16 * QB) + 4 * (ln >> 4) + 16 * i;
+        return (p < a.rows && q < a.cols) ? (uint32_t)(((ln & 15) * a.ldc + (q - q0_)) * 4) : kOOB;
+    };
     f32x4 acc[QB][PB];
 #pragma unroll
     for (int j = 0; j < PB; ++j) {
         if constexpr (EPI == EPI_ACC) {
-            const int64_t prow = p0 + wp * (16 * PB) + 16 * j;
-            const rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(static_cast<const float *>(a.C) + prow * a.ldc + q0),
-                                        a.accumulate ? kNumRecords : 0u);
+            const rsrc_t rs = c_rsrc(p0, q0, j, a.accumulate != 0);
 #pragma unroll
-            for (int i = 0; i < QB; ++i) {
-                const int64_t p = pb + j * 16, q = qb + i * 16;
-                const uint32_t off =
-                    (p < a.rows && q < a.cols) ? (uint32_t)(((lane & 15) * a.ldc + (q - q0)) * 4) : kOOB;
-                asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=a"(acc[i][j]) : "v"(off), "s"(rs) : "memory");
-            }
+            for (int i = 0; i < QB; ++i)
+                asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen"
+                             : "=a"(acc[i][j])
+                             : "v"(c_off(p0, q0, i, j, lane)), "s"(rs)
+                             : "memory");
         } else {
 #pragma unroll
             for (int i = 0; i < QB; ++i) acc[i][j] = f32x4{};
@@ -726,26 +749,27 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     // 2s (of unit 2s + 1); both were read during step s - 1.  Moving on a step
     // shifts the ring by two units and appends those two slots.
     uint32_t rg[5];
-#pragma unroll
-    for (int k = 0; k < 5; ++k) rg[k] = lds_addr(slot(k));
 
     // Prologue: units 0..4 in flight (units past the last one read zeros);
     // wait for units 0..3, read the fragments of step 0.
-    static_for<0, 5>([&](auto U_) __attribute__((always_inline)) {
-        constexpr int u = decltype(U_)::value;
-        int32_t k0;
-        if constexpr (u % 2 == 0) {
-            const rsrc_t rs = take_f(k0);
+    auto copy_first_units = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int j = 0; j < NF; ++j) issue_f(rs, k0, rg[u], j);
-        } else {
-            const rsrc_t rs = take_s(k0);
+        for (int k = 0; k < 5; ++k) rg[k] = lds_addr(slot(k));
+        static_for<0, 5>([&](auto U_) __attribute__((always_inline)) {
+            constexpr int u = decltype(U_)::value;
+            int32_t k0;
+            if constexpr (u % 2 == 0) {
+                const rsrc_t rs = take_f(k0);
 #pragma unroll
-            for (int j = 0; j < NS; ++j) issue_s(rs, k0, rg[u], j);
-        }
-    });
-    wait_and_barrier<NF>();
-    {
+                for (int j = 0; j < NF; ++j) issue_f(rs, k0, rg[u], j);
+            } else {
+                const rsrc_t rs = take_s(k0);
+#pragma unroll
+                for (int j = 0; j < NS; ++j) issue_s(rs, k0, rg[u], j);
+            }
+        });
+    };
+    auto read_first_fragments = [&]() __attribute__((always_inline)) {
         const uint32_t qs = Q_FIRST ? rg[0] : rg[1], ps = Q_FIRST ? rg[1] : rg[0];
         const QBs qb0 = qo.bases(qs, 0), qb1 = qo.bases(qs, 1);
         const PBs pb0 = po.bases(ps, 0), pb1 = po.bases(ps, 1);
@@ -762,7 +786,10 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
             for (int h = 0; h < 2; ++h) {
                 if constexpr (ROW_Q) pfrag(pb0, pb1, h, f, xc[0][f][h]); else qfrag(qb0, qb1, h, f, xc[0][f][h]);
             }
-    }
+    };
+    copy_first_units();
+    wait_and_barrier<NF>();
+    read_first_fragments();
 
     // Read bases of the next step (units 2s + 2, 2s + 3), formed before the
     // barrier that precedes the step, so that the step opens with its MFMAs.
@@ -819,18 +846,56 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     // MFMAs, and every step starts with its first MFMA.  (Before the first
     // step it finds everything it waits for already done.)
     const int64_t npairs = (ksteps + 1) / 2;
-    for (int64_t t = 0; t < npairs; ++t) {
-        wait_and_barrier<NF>();
-        one_step(P0{});
-        wait_and_barrier<NF>();
-        one_step(P1{});
+    for (;;) {  // one pass per output tile of this workgroup
+        for (int64_t t = 0; t < npairs; ++t) {
+            wait_and_barrier<NF>();
+            one_step(P0{});
+            wait_and_barrier<NF>();
+            one_step(P1{});
+        }
+        mfma_fence<true>(acc);  // the last MFMA, then accumulator reads
+        // the copies past the last unit are still in flight: none may land
+        // after the workgroup has released its LDS, or under the next tile's
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (PERSIST) {
+            const int wn = w + (int)gridDim.x;
+            if (wn < tiles_p * tiles_q) {
+                const int64_t pd = p0, qd = q0;  // the finished tile
+                // every wave has read its last fragments before the ring refills
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                w = wn;
+                setup(w, ln);
+                copy_first_units();
+                // Block by block: store the finished tile's sums, then load the
+                // next tile's C into the same registers (a store reads its data
+                // registers when it issues, so the load cannot overtake it).
+#pragma unroll
+                for (int j = 0; j < PB; ++j) {
+                    const rsrc_t rst = c_rsrc(pd, qd, j, true), rld = c_rsrc(p0, q0, j, a.accumulate != 0);
+#pragma unroll
+                    for (int i = 0; i < QB; ++i)
+                        asm volatile(
+                            "buffer_store_dwordx4 %0, %1, %3, 0 offen\n\t"
+                            "buffer_load_dwordx4 %0, %2, %4, 0 offen"
+                            : "+a"(acc[i][j])
+                            : "v"(c_off(pd, qd, i, j, ln)), "v"(c_off(p0, q0, i, j, ln)), "s"(rst), "s"(rld)
+                            : "memory");
+                }
+                asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+                read_first_fragments();
+                next_bases();
+                mfma_fence<false>(acc);  // accumulator writes, then the first MFMA
+                continue;
+            }
+        }
+        break;
     }
-    mfma_fence<true>(acc);  // the last MFMA, then accumulator reads
-    // the copies past the last unit are still in flight: none may land after
-    // the workgroup has released its LDS
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Epilogue.
+    const int64_t pb = p0 + wp * (16 * PB) + (lane & 15);
+    const int64_t qb = q0 + wq * (16 * QB) + 4 * (lane >> 4);
     if constexpr (EPI == EPI_GELU || EPI == EPI_GELU_F32A) {
         // H = table[A]: the GeLU table of this type goes into the now idle LDS
         // (128 KiB: 32 one-KiB copies per wave).  Every wave's copies of the
@@ -971,12 +1036,27 @@ hipError_t run_shape(const GemmArgs &a, hipStream_t s) {
     }
     // the accumulating epilogue addresses 16 rows of C through one descriptor
     if (EPI == EPI_ACC && (a.ldc < 0 || (16 * a.ldc + 256) * 4 >= (int64_t)kNumRecords)) return hipErrorInvalidValue;
+    // persistent workgroups: a grid of wg_cap (a multiple of 8, so that each
+    // workgroup's tiles stay on its XCD) when there are more tiles than that
+    if (a.wg_cap < 0 || a.wg_cap % 8 != 0) return hipErrorInvalidValue;
+    if constexpr (EPI == EPI_ACC) {
+        if (a.wg_cap > 0 && nt > a.wg_cap) {
+            const dim3 g((unsigned)a.wg_cap);
+            if (a.red % BK == 0)
+                hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, true, QB, PB, true>), g, dim3(kThreads), 0, s, a,
+                                   tiles_p, tiles_q);
+            else
+                hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, false, QB, PB, true>), g, dim3(kThreads), 0, s,
+                                   a, tiles_p, tiles_q);
+            return hipGetLastError();
+        }
+    }
     if (a.red % BK == 0)
-        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, true, QB, PB>), dim3((unsigned)nt), dim3(kThreads), 0, s,
-                           a, tiles_p, tiles_q);
+        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, true, QB, PB, false>), dim3((unsigned)nt), dim3(kThreads),
+                           0, s, a, tiles_p, tiles_q);
     else
-        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, false, QB, PB>), dim3((unsigned)nt), dim3(kThreads), 0,
-                           s, a, tiles_p, tiles_q);
+        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, false, QB, PB, false>), dim3((unsigned)nt),
+                           dim3(kThreads), 0, s, a, tiles_p, tiles_q);
     return hipGetLastError();
 }
 

@@ -184,9 +184,11 @@ class Context:
     def sync(self):
         zi.zi_sync(self.handle)
 
-    def set_debug(self, poison: bool = False, copy_delay_us: int = 0):
-        """Test aids (zi_ctx_set_debug): poison released slots; delay every tile copy."""
-        zi.zi_ctx_set_debug(self.handle, zi.ZI_DEBUG_POISON if poison else 0, copy_delay_us)
+    def set_debug(self, poison: bool = False, copy_delay_us: int = 0, dx_per_tile: bool = False):
+        """Test aids (zi_ctx_set_debug): poison released slots; delay every tile copy;
+        run dX products one workgroup per output block instead of persistent ones."""
+        flags = (zi.ZI_DEBUG_POISON if poison else 0) | (zi.ZI_DEBUG_DX_PER_TILE if dx_per_tile else 0)
+        zi.zi_ctx_set_debug(self.handle, flags, copy_delay_us)
 
     def set_timing(self, on: bool):
         zi.zi_ctx_set_timing(self.handle, on)

@@ -364,6 +364,7 @@ def zi_ctx_set_second_stream(ctx, stream) -> None:
 
 
 ZI_DEBUG_POISON = 0x1
+ZI_DEBUG_DX_PER_TILE = 0x2
 
 
 def zi_ctx_set_debug(ctx, flags: int = 0, copy_delay_us: int = 0) -> None:

@@ -253,6 +253,37 @@ def test_paired_dx_odd_and_even_tile_counts(N, d):
     assert np.array_equal(host_bits(r["dWt"]), oracle.encode(dWt, "f16"))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,K,M,N,d", [(2304, 20480, 512, 4, 2), (1100, 14000, 600, 3, 2)])
+def test_persistent_dx_bit_exact(dtype, T, K, M, N, d):
+    # dX with more 256 x 256 output blocks than the compute units' persistent
+    # workgroups: 9 x 80 = 720 blocks (about three per workgroup, tile pairs:
+    # an aligned reduction of 256 over two slots, the first pair overwriting,
+    # the second adding), and 5 x 55 = 275 (ragged rows and columns, unpaired
+    # tiles of 200: an unaligned reduction).  Small integers make dX exact;
+    # the per-block form must give the same bits.
+    tiling = lib()
+    say("case persistent dX", dtype, "T", T, "K", K, "M", M, "N", N, "d", d)
+    X, Wt, dY = make_linear_inputs(T, K, M, dtype, "small_int", seed=23)
+    outs = []
+    dWt = tiling.host_tensor((M, K), inputs.torch_dtype(dtype))
+    for per_tile in (False, True):
+        plan = tiling.Plan(T, K, M, N, d, dtype, Wt, dWt)
+        ctx = tiling.Context(plan)
+        ctx.set_debug(dx_per_tile=per_tile)
+        dX = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        ctx.bwd(plan, X, dY, dX)
+        ctx.sync()
+        outs.append(dX.cpu().numpy())
+        ctx.close()
+        plan.close()
+    ref, ref_dw = oracle.linear_bwd(host_bits(X), host_bits(Wt), host_bits(dY), dtype)
+    assert np.array_equal(outs[0].astype(np.float64), ref), "persistent dX against the oracle"
+    assert np.array_equal(host_bits(dWt), oracle.encode(ref_dw, dtype)), "dW bits"
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), "persistent against per-block dX"
+
+
 def test_consecutive_calls_share_the_ring():
     # two forwards and a backward enqueued back to back with no host sync:
     # the first copies of each call overlap the previous call's products
