@@ -104,6 +104,10 @@ def parse():
     ap.add_argument("--summarize-trace", type=str, default=None, metavar="DIR",
                     help="summarise the rocprofv3 CSV output under DIR (kernel trace and/or counter "
                          "collection) per kernel and grid size, and exit (no GPU needed)")
+    ap.add_argument("--split", action="append", default=[], metavar="LABEL=R0,R1,...",
+                    help="with --summarize-trace: the dispatches of LABEL, in dispatch order, come in "
+                         "repeating runs of R0, R1, ... launches of different shapes (a persistent "
+                         "kernel's grid does not tell them apart); label run i 'LABEL #i'")
     return ap.parse_args()
 
 
@@ -116,14 +120,15 @@ def kernel_label(name, grid, wg):
     kernels of the library by name, the rest by the start of their name."""
     import re
     groups = grid // max(wg, 1)
-    m = re.search(r"gemm_kernelI(DF16b?)_Lb([01])ELb([01])ELi(\d)ELb([01])ELi(\d+)ELi(\d+)E", name)
+    m = re.search(r"gemm_kernelI(DF16_|DF16b)Lb([01])ELb([01])ELi(\d)ELb([01])ELi(\d+)ELi(\d+)E(?:Lb([01])E)?", name)
     if m:
         t = "bf16" if m.group(1) == "DF16b" else "f16"
         q = "rs" if m.group(2) == "1" else "rc"
         p = "rs" if m.group(3) == "1" else "rc"
         epi = _EPI_NAMES.get(int(m.group(4)), m.group(4))
         ragged = "" if m.group(5) == "1" else ",ragged"
-        return "gemm<%s,%s,%s,%s,%sx%s%s> x%d" % (t, q, p, epi, m.group(6), m.group(7), ragged, groups)
+        persist = ",persistent" if m.group(8) == "1" else ""
+        return "gemm<%s,%s,%s,%s,%sx%s%s%s> x%d" % (t, q, p, epi, m.group(6), m.group(7), ragged, persist, groups)
     for key, label in (("gelu_bwd_kernel", "gelu_bwd"), ("gelu_table_kernel", "gelu_table"),
                        ("copyBuffer", "__amd_rocclr_copyBuffer"), ("neg_kernel", "neg_kernel")):
         if key in name:
@@ -132,20 +137,51 @@ def kernel_label(name, grid, wg):
     return "%s x%d" % (short.split("(")[0][:60], groups)
 
 
-def summarize_trace(path):
+def split_labels(keys, labels, splits):
+    """labels[i] with ' #g' appended for the labels named in `splits`
+    ({label: [r0, r1, ...]}): ordered by keys[i], the dispatches of such a label
+    run through repeating runs of r0, r1, ... and g is the run's index."""
+    out = list(labels)
+    seen = {}
+    for i in sorted(range(len(labels)), key=lambda i: keys[i]):
+        runs = splits.get(labels[i])
+        if not runs:
+            continue
+        k = seen.get(labels[i], 0)
+        seen[labels[i]] = k + 1
+        k %= sum(runs)
+        g = 0
+        while k >= runs[g]:
+            k -= runs[g]
+            g += 1
+        out[i] = "%s #%d" % (labels[i], g)
+    return out
+
+
+def summarize_trace(path, splits=None):
     """Per kernel label: counter means/min/max over the dispatches (counter
     collection CSV) and durations, with the dispatches no other dispatch (or
     no other kernel of the library) overlapped (kernel trace CSV).  Prints one
-    JSON object {"counters": {...}, "kernels": {...}}."""
+    JSON object {"counters": {...}, "kernels": {...}}.  `splits` (see
+    split_labels) tells apart launches of one kernel and grid by their order."""
     import csv
     import glob
     import json
+    splits = splits or {}
     counters, kernels = {}, {}
     for f in sorted(glob.glob(os.path.join(path, "*counter_collection.csv"))):
         per = {}  # (label, counter) -> {dispatch: value};  label -> {dispatch: ms}
         dur = {}
-        for r in csv.DictReader(open(f)):
-            lab = kernel_label(r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+        recs = list(csv.DictReader(open(f)))
+        labs = [kernel_label(r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"])) for r in recs]
+        # one row per (dispatch, counter): order the dispatches, then label their rows
+        first = {}
+        for i, r in enumerate(recs):
+            first.setdefault(r["Dispatch_Id"], i)
+        order = sorted(first, key=lambda d: int(d))
+        dlab = dict(zip(order, split_labels(list(range(len(order))), [labs[first[d]] for d in order], splits)))
+        for r in recs:
+            lab = dlab[r["Dispatch_Id"]]
             did = r["Dispatch_Id"]
             per.setdefault((lab, r["Counter_Name"]), {})
             per[(lab, r["Counter_Name"])][did] = per[(lab, r["Counter_Name"])].get(did, 0.0) + float(r["Counter_Value"])
@@ -159,11 +195,12 @@ def summarize_trace(path):
             counters.setdefault(lab, {})["_dur"] = {"dispatches": len(v), "mean": sum(v) / len(v), "min": min(v),
                                                     "max": max(v)}
     for f in sorted(glob.glob(os.path.join(path, "*kernel_trace.csv"))):
-        rows = []
-        for r in csv.DictReader(open(f)):
-            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"].startswith("_ZN2zi"),
-                         kernel_label(r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))))
-        rows.sort()
+        recs = list(csv.DictReader(open(f)))
+        labs = split_labels([int(r["Dispatch_Id"]) for r in recs],
+                            [kernel_label(r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+                             for r in recs], splits)
+        rows = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"].startswith("_ZN2zi"),
+                       lab) for r, lab in zip(recs, labs))
         n = len(rows)
 
         def alone(lib_only):
@@ -457,7 +494,11 @@ class ClockSampler:
 def main():
     args = parse()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        splits = {}
+        for sp in args.split:
+            lab, _, runs = sp.rpartition("=")
+            splits[lab] = [int(x) for x in runs.split(",")]
+        summarize_trace(args.summarize_trace, splits)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the tiled path runs on a single device and has no "

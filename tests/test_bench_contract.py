@@ -13,3 +13,23 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_trace_labels_of_the_gemm_instances():
+    # rocprofv3 reports the mangled kernel names; the summaries label them by
+    # template arguments and workgroup count (grid in threads / 256)
+    sys.path.insert(0, ROOT)
+    import bench
+
+    pre = "_ZN2zi12_GLOBAL__N_111gemm_kernelI"
+    suf = "EvNS_8GemmArgsEii"
+    assert bench.kernel_label(pre + "DF16_Lb0ELb0ELi2ELb1ELi8ELi8ELb0EE" + suf, 3200 * 256, 256) == \
+        "gemm<f16,rc,rc,gelu,8x8> x3200"
+    assert bench.kernel_label(pre + "DF16_Lb1ELb0ELi3ELb1ELi8ELi8ELb1EE" + suf, 256 * 256, 256) == \
+        "gemm<f16,rs,rc,acc,8x8,persistent> x256"
+    assert bench.kernel_label(pre + "DF16bLb1ELb1ELi1ELb0ELi6ELi10ELb0EE" + suf, 2670 * 256, 256) == \
+        "gemm<bf16,rs,rs,f32,6x10,ragged> x2670"
+    # names from before the persistent flag existed
+    assert bench.kernel_label(pre + "DF16_Lb0ELb0ELi0ELb1ELi10ELi6EE" + suf, 855 * 256, 256) == \
+        "gemm<f16,rc,rc,lp,10x6> x855"
+    assert bench.kernel_label("void at::native::foo<float>(int)", 1024, 256) == "at::native::foo<float> x4"
