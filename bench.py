@@ -822,7 +822,8 @@ def choose_leg(args, torch, tiling, inputs, link, steps=3):
     tiled linear fwd + bwd is run over `steps` steps with per-launch events;
     the rates of its forward, dX and dW products and of its copies make the
     planner's curve.  The step time is then taken without those events, among
-    back-to-back steps (as the planner prices a step).
+    back-to-back steps (as the planner prices a step).  Both run with one
+    product stream, the schedule the planner's model describes.
     zi_plan_choose then picks N and d from that curve and the host-link rates,
     and its prediction for every width stands beside the measured step time.
     Default shape: the feed-forward block's down-projection, W2[102400 x 25600]
@@ -848,7 +849,11 @@ def choose_leg(args, torch, tiling, inputs, link, steps=3):
     rows = []
     for n in widths:
         plan = tiling.Plan(T, K, M, M // n, 2, dtype, Wt, dWt)
-        ctx = tiling.Context(plan)
+        # the planner's ring model runs a pass's products one after another,
+        # so the curve and the step times are taken with one product stream
+        # (a second one would overlap forward products, and their event
+        # durations would include the time they share the device)
+        ctx = tiling.Context(plan, overlap=False)
         Y = torch.empty((T, M), dtype=tdt, device="cuda")
         ctx.fwd(plan, X, Y)
         ctx.bwd(plan, X, dY, dX)
