@@ -472,8 +472,11 @@ __device__ __forceinline__ float gelu_grad_f32(float a) {
 // go in column groups G macro-rows tall (G P tiles reuse one Q tile, the
 // consecutive groups reuse P).  G is set per product by measurement on the
 // FFN block at T = 32768: 4 for the forward and input-gradient products
-// (against 8: +1-2 % each, the down-projection's forward +10 %), 8 for the
-// weight-gradient products (4 lost 1-2.5 %; 16 lost on every product).
+// (against 8: +1-2 % each, the down-projection's forward +10 %; against 2 and
+// 1: up to 2 % and 10 % slower), except 1 for the forward's 320 x 192 tiles
+// (the down-projection's: forward and paired recompute 2-4 % faster than
+// with 4), and 8 for the weight-gradient products (4 lost 1-2.5 %; 16 lost
+// on every product).
 template <int G>
 __device__ __forceinline__ void tile_coords(int w, int tiles_p, int tiles_q, int &tp, int &tq) {
     const int nt = tiles_p * tiles_q;
@@ -569,7 +572,7 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     // across the main loop.)
     auto setup = [&](int wi, int ln) __attribute__((always_inline)) {
         int tp, tq;
-        tile_coords<(Q_RS && P_RS) ? 8 : 4>(wi, tiles_p, tiles_q, tp, tq);
+        tile_coords<(Q_RS && P_RS) ? 8 : (QB == 10 ? 1 : 4)>(wi, tiles_p, tiles_q, tp, tq);
         p0 = (int64_t)tp * TP;
         q0 = (int64_t)tq * TQ;
         if constexpr (Q_RS) {
