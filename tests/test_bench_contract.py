@@ -33,3 +33,18 @@ def test_trace_labels_of_the_gemm_instances():
     assert bench.kernel_label(pre + "DF16_Lb0ELb0ELi0ELb1ELi10ELi6EE" + suf, 855 * 256, 256) == \
         "gemm<f16,rc,rc,lp,10x6> x855"
     assert bench.kernel_label("void at::native::foo<float>(int)", 1024, 256) == "at::native::foo<float> x4"
+
+
+def test_split_labels_by_dispatch_order():
+    # launches of one kernel and grid told apart by their order: runs of 2
+    # and 1 repeating, keyed by dispatch id (not by list position)
+    sys.path.insert(0, ROOT)
+    import bench
+
+    labels = ["k", "other", "k", "k", "k", "k", "k"]
+    keys = [5, 1, 2, 9, 7, 3, 11]  # dispatch ids: k's order is 2, 3, 5, 7, 9, 11
+    out = bench.split_labels(keys, labels, {"k": [2, 1]})
+    by_key = dict(zip(keys, out))
+    assert by_key[1] == "other"
+    assert [by_key[k] for k in (2, 3, 5, 7, 9, 11)] == ["k #0", "k #0", "k #1", "k #0", "k #0", "k #1"]
+    assert bench.split_labels(keys, labels, {}) == labels
