@@ -69,10 +69,12 @@ def parse():
                          "workgroup per compute unit (to compare the two forms)")
     ap.add_argument("--max-ahead", type=int, default=0,
                     help="steps the host may enqueue ahead of the device (0: no limit)")
-    ap.add_argument("--unbounded-enqueue", dest="ahead_mid", action="store_false",
-                    help="enqueue every step at once (default: each step once the previous one has "
-                         "reached its middle: the down-projection's backward done, or the linear's "
-                         "forward)")
+    ap.add_argument("--enqueue", choices=("mid", "all"), default=None,
+                    help="mid: enqueue each step once the previous one has reached its middle (the "
+                         "down-projection's backward done, or the linear's forward); all: every step "
+                         "at once (default: mid for the FFN block, all for the tiled linear)")
+    ap.add_argument("--unbounded-enqueue", dest="enqueue", action="store_const", const="all",
+                    help="the same as --enqueue all")
     ap.add_argument("--ahead-poll", type=float, default=0.0,
                     help="with --max-ahead: poll the step's end event every this many ms instead of "
                          "waiting on it")
@@ -624,14 +626,20 @@ def main():
                 tier.step()
     torch.cuda.synchronize()
 
-    # Per-step marks: an event on the compute stream after every step.  The
-    # host enqueues step i once step i - 1 has reached its middle, so the
-    # ring's prefetch still crosses steps while about one step is in flight
-    # (as in a training loop that reads its loss every step).  With every step
-    # enqueued at once the HIP runtime was seen, after 12-19 steps, to carry
-    # the tile copies out at 36-40 GB/s as copy kernels beside the products
-    # (steps 15-40 % longer), and with two or more whole steps in flight to
-    # stall write-backs at 13 GB/s; one step or less in flight avoided both.
+    # Per-step marks: an event on the compute stream after every step.  For
+    # the FFN block the host enqueues step i once step i - 1 has reached its
+    # middle, so the ring's prefetch still crosses steps while about one step
+    # is in flight (as in a training loop that reads its loss every step).
+    # With every step enqueued at once the HIP runtime was seen, after 12-19
+    # steps, to carry the tile copies out at 36-40 GB/s as copy kernels beside
+    # the products (steps 15-40 % longer), and with two or more whole steps in
+    # flight to stall write-backs at 13 GB/s; one step or less in flight
+    # avoided both.  The tiled linear's middle is its forward, and there the
+    # same gating slowed the write-backs of the step after the first to
+    # 8-19 GB/s in 11 of 12 three-step runs (every step enqueued at once: none
+    # of 6), so it enqueues every step at once by default.
+    if args.enqueue is None:
+        args.enqueue = "mid" if config["workload"] == "ffn_block_fwd_recompute_bwd" else "all"
     comp = torch.cuda.ExternalStream(ctx.streams[0])
 
     def marked(n, sampler=None):
@@ -642,7 +650,7 @@ def main():
         ev[0].record(comp)
         for i in range(n):
             e = None
-            if args.ahead_mid and i >= 1:
+            if args.enqueue == "mid" and i >= 1:
                 e = mids[i - 1]
             elif args.max_ahead and i >= args.max_ahead:
                 e = ev[i - args.max_ahead + 1]
@@ -771,7 +779,7 @@ def main():
                      "traffic": measured_traffic(config, dom["kernel"])},
         "step_clock": {"source": sampler.source, "error": sampler.error, "per_step": step_clock},
         "step_parts": step_parts,
-        "host_enqueue": ("each step once the previous one reached its middle" if args.ahead_mid
+        "host_enqueue": ("each step once the previous one reached its middle" if args.enqueue == "mid"
                          else ("at most %d steps ahead" % args.max_ahead if args.max_ahead else "unbounded")),
     }
     if config["workload"] == "ffn_block_fwd_recompute_bwd":
