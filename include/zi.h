@@ -345,7 +345,10 @@ zi_status zi_tiled_linear_fwd_noalloc(const zi_plan *plan, const void *X_dev, vo
  * was seen, after a while, to carry the tile copies out as copy kernels that
  * take compute units from the products (steps 15-40 % longer), and with two
  * or more whole steps in flight to stall write-backs; enqueueing a step once
- * the previous one has reached its middle kept every step steady. */
+ * the previous one has reached its middle kept the feed-forward block's steps
+ * steady.  For a single operator whose step is one forward and one backward,
+ * enqueueing the next step once the forward had run slowed the write-backs of
+ * the step in flight, while a few steps enqueued at once did not. */
 zi_status zi_sync(zi_ctx *ctx);
 
 /* Per-context timing (off by default).  When on, every kernel launch and
