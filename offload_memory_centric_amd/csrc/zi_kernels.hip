@@ -463,6 +463,25 @@ __device__ __forceinline__ float gelu_grad_f32(float a) {
     return cdf + a * pdf;
 }
 
+// GeLU' in fp32 of every 16-bit input, built once per device with the
+// function above (so a lookup gives the bits an evaluation would), for the
+// GeLU backward.
+__device__ float g_gelu_grad_f16[65536];
+__device__ float g_gelu_grad_bf16[65536];
+
+template <typename T>
+__device__ __forceinline__ float *gelu_grad_table();
+template <>
+__device__ __forceinline__ float *gelu_grad_table<_Float16>() { return g_gelu_grad_f16; }
+template <>
+__device__ __forceinline__ float *gelu_grad_table<__bf16>() { return g_gelu_grad_bf16; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void gelu_grad_table_kernel() {
+    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
+    gelu_grad_table<T>()[i] = gelu_grad_f32(value16<T>(i));
+}
+
 // ---- workgroup -> macro-tile ------------------------------------------------------
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
@@ -961,12 +980,34 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
 
 // ---- dA = RNE(dH * GeLU'(A)) ----------------------------------------------------------
 
+// dA = RNE(dH * GeLU'(A)) with GeLU' looked up rather than evaluated: the
+// evaluation (erfc and exp, tens of instructions per element) held the
+// kernel at half the HBM rate.  A workgroup of 1024 threads (one per compute
+// unit, with its LDS) copies the table's entries for |A| < 16 (both signs,
+// kLim codes each: 152 KiB for fp16, 131 KiB for bf16) into LDS and reads the
+// rest, which Gaussian-like data almost never holds, from the global table.
 // OUT_F32: dA is written as the fp32 product itself, the value the 16-bit
 // form rounds once.
+template <typename T>
+constexpr uint32_t gelu_grad_lim() { return std::is_same<T, _Float16>::value ? 0x4C00u : 0x4180u; }  // code of 16.0
+
 template <typename T, bool OUT_F32>
-__global__ __launch_bounds__(256) void gelu_bwd_kernel(const float *__restrict__ dH,
-                                                       const uint16_t *__restrict__ A,
-                                                       void *__restrict__ dA, int64_t count) {
+__global__ __launch_bounds__(1024) void gelu_bwd_kernel(const float *__restrict__ dH,
+                                                        const uint16_t *__restrict__ A,
+                                                        void *__restrict__ dA, int64_t count) {
+    constexpr uint32_t kLim = gelu_grad_lim<T>();
+    static_assert(kLim % 4 == 0 && 2 * kLim * 4 <= 160 * 1024, "LDS table");
+    __shared__ __attribute__((aligned(16))) float tab[2 * kLim];
+    const float *gtab = gelu_grad_table<T>();
+    for (uint32_t e = threadIdx.x * 4; e < 2 * kLim; e += blockDim.x * 4) {  // codes [0, kLim), [0x8000, +kLim)
+        const uint32_t c = e < kLim ? e : 0x8000u + (e - kLim);
+        *reinterpret_cast<f32x4 *>(tab + e) = *reinterpret_cast<const f32x4 *>(gtab + c);
+    }
+    __syncthreads();
+    auto grad = [&](uint32_t c) __attribute__((always_inline)) -> float {
+        const uint32_t m = c & 0x7fffu;
+        return m < kLim ? tab[(c >> 15) * kLim + m] : gtab[c];
+    };
     const int64_t stride = (int64_t)gridDim.x * blockDim.x * 8;
     uint16_t *dA16 = static_cast<uint16_t *>(dA);
     float *dA32 = static_cast<float *>(dA);
@@ -979,8 +1020,8 @@ __global__ __launch_bounds__(256) void gelu_bwd_kernel(const float *__restrict__
             float r[8];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                r[2 * w] = g[2 * w] * gelu_grad_f32(value16<T>(av[w] & 0xffffu));
-                r[2 * w + 1] = g[2 * w + 1] * gelu_grad_f32(value16<T>(av[w] >> 16));
+                r[2 * w] = g[2 * w] * grad(av[w] & 0xffffu);
+                r[2 * w + 1] = g[2 * w + 1] * grad(av[w] >> 16);
             }
             // the product is rounded to fp32 first and then, once, to 16 bits:
             // kept from fusing into a mixed-precision multiply that would
@@ -998,7 +1039,7 @@ __global__ __launch_bounds__(256) void gelu_bwd_kernel(const float *__restrict__
             }
         } else {
             for (int64_t e = i; e < count; ++e) {
-                float r = dH[e] * gelu_grad_f32(value16<T>(A[e]));
+                float r = dH[e] * grad(A[e]);
                 asm volatile("" : "+v"(r));
                 if constexpr (OUT_F32)
                     dA32[e] = r;
@@ -1126,17 +1167,23 @@ hipError_t build_gelu_tables(hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gelu_table_kernel<__bf16>, dim3(256), dim3(256), 0, stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(gelu_grad_table_kernel<_Float16>, dim3(256), dim3(256), 0, stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(gelu_grad_table_kernel<__bf16>, dim3(256), dim3(256), 0, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_gelu_bwd(int dtype, const float *dH, const void *A, void *dA, int64_t count,
                            bool out_f32, hipStream_t stream) {
     if (count <= 0) return hipSuccess;
+    // one workgroup of 1024 threads per compute unit (each holds the LDS
+    // table), fewer for small counts
     const int64_t threads = (count + 7) / 8;
-    int64_t blocks = (threads + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
+    int64_t blocks = (threads + 1023) / 1024;
+    if (blocks > 256) blocks = 256;
     const uint16_t *a16 = static_cast<const uint16_t *>(A);
-    const dim3 g((unsigned)blocks), b(256);
+    const dim3 g((unsigned)blocks), b(1024);
     if (dtype == 1 && !out_f32)
         hipLaunchKernelGGL((gelu_bwd_kernel<_Float16, false>), g, b, 0, stream, dH, a16, dA, count);
     else if (dtype == 1)

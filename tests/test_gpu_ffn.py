@@ -191,6 +191,46 @@ def test_gelu_bwd_kernel_elementwise(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_gelu_bwd_every_16bit_input(dtype):
+    # A takes every finite 16-bit value (GeLU' looked up: from LDS for
+    # |A| < 16, from the global table beyond), dH a random value each; the same
+    # bounds as the elementwise test, against the oracle's fp64 GeLU'.  Below
+    # a = -13.3 GeLU'(a) lies under fp32's smallest normal value 2^-126, where
+    # fp32 carries only absolute accuracy (the terms of Phi(a) + a phi(a)
+    # are subnormal, and exp may return 0): there an fp32 evaluation is off by
+    # up to 2^-126 |dH|, and the product's own rounding by up to 2^-150
+    tiling = lib()
+    tdt = inputs.torch_dtype(dtype)
+    codes = np.arange(65536, dtype=np.uint16)
+    a_all = oracle.decode(codes, dtype)
+    keep = np.isfinite(a_all)
+    codes, a = codes[keep], a_all[keep]
+    count = len(codes)
+    A = torch.from_numpy(codes.view(np.int16).copy()).view(tdt).cuda()
+    dH = torch.randn(count, generator=torch.Generator(device="cuda").manual_seed(7), device="cuda")
+    dA = torch.empty_like(A)
+    dA32 = torch.empty(count, dtype=torch.float32, device="cuda")
+    plan = tiling.Plan(1, 8, 8, 1, 1, dtype, tiling.host_tensor((8, 8), tdt))
+    ctx = tiling.Context(plan)
+    torch.cuda.synchronize()
+    ctx.gelu_bwd(dtype, dH, A, dA, count)
+    ctx.gelu_bwd(dtype, dH, A, dA32, count)
+    ctx.sync()
+    ref = dH.cpu().numpy().astype(np.float64) * oracle.gelu_grad(a)
+    g32 = dA32.cpu().numpy().astype(np.float64)
+    dh = np.abs(dH.cpu().numpy().astype(np.float64))
+    phi = oracle.gelu(a) / np.where(a == 0, 1.0, a)
+    parts = np.where(a == 0, 0.5, phi) + np.abs(a) * np.exp(-0.5 * a * a) / np.sqrt(2 * np.pi)
+    bound = dh * parts * (1 + a * a) * 2.0 ** -20 + np.abs(ref) * 2.0 ** -22
+    bound = bound + np.where(np.abs(oracle.gelu_grad(a)) < 2.0 ** -126, dh * 2.0 ** -126 + 2.0 ** -149, 0.0)
+    bad = np.flatnonzero(np.abs(g32 - ref) > bound)
+    assert len(bad) == 0, "%d over the bound, e.g. %s" % (len(bad), [
+        (float(a[i]), float(g32[i]), float(ref[i]), float(bound[i])) for i in bad[:12]])
+    assert torch.equal(dA32.to(tdt), dA), "dA is not RNE of its fp32 product"
+    ctx.close()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_gelu_epilogue_every_16bit_input(dtype):
     # X = e_0 and column m of W holds the 16-bit value with bits m in row 0
     # (zeros elsewhere): A[0][m] is that value, so H is GeLU at every 16-bit
