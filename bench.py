@@ -132,6 +132,7 @@ def kernel_label(name, grid, wg):
         persist = ",persistent" if m.group(8) == "1" else ""
         return "gemm<%s,%s,%s,%s,%sx%s%s%s> x%d" % (t, q, p, epi, m.group(6), m.group(7), ragged, persist, groups)
     for key, label in (("gelu_bwd_kernel", "gelu_bwd"), ("gelu_table_kernel", "gelu_table"),
+                       ("gelu_grad_table_kernel", "gelu_grad_table"),
                        ("copyBuffer", "__amd_rocclr_copyBuffer"), ("neg_kernel", "neg_kernel")):
         if key in name:
             return "%s x%d" % (label, groups)

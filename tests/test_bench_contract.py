@@ -33,6 +33,12 @@ def test_trace_labels_of_the_gemm_instances():
     assert bench.kernel_label(pre + "DF16_Lb0ELb0ELi0ELb1ELi10ELi6EE" + suf, 855 * 256, 256) == \
         "gemm<f16,rc,rc,lp,10x6> x855"
     assert bench.kernel_label("void at::native::foo<float>(int)", 1024, 256) == "at::native::foo<float> x4"
+    assert bench.kernel_label("_ZN2zi12_GLOBAL__N_115gelu_bwd_kernelIDF16_Lb0EEEvPKfPKtPvl", 256 * 1024, 1024) == \
+        "gelu_bwd x256"
+    assert bench.kernel_label("_ZN2zi12_GLOBAL__N_122gelu_grad_table_kernelIDF16bEEvv", 256 * 256, 256) == \
+        "gelu_grad_table x256"
+    assert bench.kernel_label("_ZN2zi12_GLOBAL__N_117gelu_table_kernelIDF16_EEvv", 256 * 256, 256) == \
+        "gelu_table x256"
 
 
 def test_split_labels_by_dispatch_order():
