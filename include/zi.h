@@ -295,9 +295,10 @@ zi_status zi_tiled_linear_bwd_recompute(zi_ctx *ctx, const zi_plan *plan, const 
                                         const void *dY_dev, float *dX_dev, void *Yr_dev);
 
 /* dA = RNE(dH * GeLU'(A)) elementwise on the compute stream, GeLU'(a) =
- * Phi(a) + a phi(a) evaluated in fp32 on the stored A (the chain rule through
- * the block's GeLU; transformer-math page, section "Memory-centric tiling":
- * the 1T model's FFN).  dH: fp32 device, A and dA: device, input format
+ * Phi(a) + a phi(a) evaluated in fp32 on the stored A, once per 16-bit code
+ * and device into a table that the kernel reads (the chain rule through the
+ * block's GeLU; transformer-math page, section "Memory-centric tiling": the
+ * 1T model's FFN).  dH: fp32 device, A and dA: device, input format
  * `dtype`; `count` elements each, 16-byte aligned pointers. */
 zi_status zi_gelu_bwd(zi_ctx *ctx, int32_t dtype, const float *dH_dev, const void *A_dev,
                       void *dA_dev, int64_t count);
