@@ -504,7 +504,12 @@ __global__ __launch_bounds__(256) void gelu_grad_table_kernel() {
 // G = 8 (the weight-gradient products) all XCDs work in the same group at
 // once, each on an eighth of it (8 rows x tiles_q / 8 columns), so that a
 // round touches 8 row panels instead of all of them: the up-projection's dW
-// (25 x 100 tiles of 256, panels of 16.8 MB) ran 1.2-2.0 % faster.
+// (25 x 100 tiles of 256, panels of 16.8 MB) ran 1.2-2.0 % faster.  With
+// G = 1 and an even number of column tiles (the down-projection's recompute
+// over two weight tiles), the left half of the columns comes first, so that
+// XCDs 0-3 read only the first tile's panels and 4-7 only the second's
+// (6.4 rows x 5 columns each instead of 3.2 x 10: a quarter fewer L2 misses
+// per round, the same HBM bytes): that launch ran 1.4 % faster.
 template <int G>
 __device__ __forceinline__ void tile_coords(int w, int tiles_p, int tiles_q, int &tp, int &tq) {
     const int nt = tiles_p * tiles_q;
@@ -519,6 +524,21 @@ __device__ __forceinline__ void tile_coords(int w, int tiles_p, int tiles_q, int
             const int pos = (x & 1) * per + (k - band * per);
             tp = band * 16 + (x >> 1) * 4 + (pos & 3);
             tq = pos >> 2;
+            return;
+        }
+    }
+    if constexpr (G == 1) {
+        if ((tiles_q & 1) == 0) {
+            // the left half of the columns first, then the right half (a
+            // product over two weight tiles: XCDs 0-3 on the first tile,
+            // 4-7 on the second, each reading half the weight panels)
+            const int q8 = nt >> 3, r8 = nt & 7;
+            const int t = x * q8 + min(x, r8) + k;
+            const int hq = tiles_q >> 1, half = tiles_p * hq;
+            const int h = t >= half ? 1 : 0;
+            const int r = t - h * half;
+            tp = r / hq;
+            tq = h * hq + (r - (r / hq) * hq);
             return;
         }
     }
