@@ -284,6 +284,27 @@ def test_persistent_dx_bit_exact(dtype, T, K, M, N, d):
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), "persistent against per-block dX"
 
 
+@pytest.mark.parametrize("dtype,K", [("f16", 4608), ("bf16", 256)])
+def test_banded_and_grouped_tile_orders_bit_exact(dtype, K):
+    # T = 4096: 16 macro-rows of 256, one whole band, so the forward and dX
+    # take their tiles in the band order (XCD pairs on 4-row strips); the
+    # tile of 2600 makes 11 dW row tiles, one 8-row group that all XCDs walk
+    # together and 3 rows split by ranges.  K = 4608: 16 x 18 = 288 dX blocks,
+    # more than the persistent workgroups.  Small integers: Y, dX and dW
+    # unique (|Y| <= 9 K, |dX| <= 9 M, |dW| <= 9 T, all within fp16's range).
+    T, M, N, d = 4096, 2600, 1, 1
+    say("case tile orders", dtype, T, K, M, N, d)
+    tiling = lib()
+    X, Wt, dY = make_linear_inputs(T, K, M, dtype, "small_int", seed=31)
+    info = tiling.Plan(T, K, M, N, d, dtype, None).info
+    assert tuple(info.fwd_tile) == (256, 256) and tuple(info.dw_tile) == (256, 256)
+    r = run_fwd_bwd(T, K, M, N, d, dtype, X, Wt, dY)
+    Y, dX, dWt = oracle_linear(X, Wt, dY, dtype)
+    assert np.array_equal(host_bits(r["Y"]), oracle.encode(Y, dtype)), "Y bits"
+    assert np.array_equal(r["dX"].cpu().numpy().astype(np.float64), dX), "dX exact"
+    assert np.array_equal(host_bits(r["dWt"]), oracle.encode(dWt, dtype)), "dW bits"
+
+
 def test_consecutive_calls_share_the_ring():
     # two forwards and a backward enqueued back to back with no host sync:
     # the first copies of each call overlap the previous call's products
@@ -314,9 +335,12 @@ def test_consecutive_calls_share_the_ring():
     plan.close()
 
 
-def test_recompute_matches_forward_bit_for_bit():
-    T, K, M, N, d = 200, 512, 1536, 3, 2
-    say("case recompute")
+@pytest.mark.parametrize("T,K,M,N,d", [(200, 512, 1536, 3, 2), (700, 576, 3200, 2, 2)])
+def test_recompute_matches_forward_bit_for_bit(T, K, M, N, d):
+    # (700, 576, 3200): tiles of 1600 in 192 x 320 workgroup tiles, so the
+    # recompute of the pair is one launch of 10 tile columns (the first tile's
+    # five on XCDs 0-3, the second's on 4-7) against five per forward launch
+    say("case recompute", T, K, M, N, d)
     tiling = lib()
     X, Wt, dY = make_linear_inputs(T, K, M, "f16", "gaussian", seed=10)
     dWt = tiling.host_tensor((M, K), torch.float16)
@@ -408,14 +432,16 @@ def test_small_workspace_rejected():
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("T,K,M,N,d,fwd_rows", [(380, 584, 3200, 2, 2, 192), (700, 576, 1920, 2, 1, 192),
-                                                (32, 1600, 1600, 1, 1, 192), (7200, 128, 1600, 1, 1, 192)])
+                                                (32, 1600, 1600, 1, 1, 192), (7200, 128, 1600, 1, 1, 192),
+                                                (700, 576, 1280, 2, 2, 192)])
 def test_320_wide_tiles_bit_exact(dtype, T, K, M, N, d, fwd_rows):
     # tile widths that 320 divides and 256 does not: the forward runs 192 x 320
     # workgroup tiles, the gradient 320 x 192 (both checked in the
     # plan), with ragged rows (T = 380, 700, 7200), a reduction that is not a
     # multiple of the 64-value step (K = 584, T = 380, 7200) or an odd number
     # of steps (K = 576: 9); small integers, so every result is unique
-    # (|dW| <= 9 T stays below fp16's 65504)
+    # (|dW| <= 9 T stays below fp16's 65504); M = 1280: two tile columns of
+    # 320, which the forward takes left half first
     say("case 320-wide tiles", dtype, T, K, M, N, d)
     tiling = lib()
     X, Wt, dY = make_linear_inputs(T, K, M, dtype, "small_int", seed=13)
