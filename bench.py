@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--dx-per-tile", action="store_true",
                     help="run the dX products one workgroup per output block instead of one persistent "
                          "workgroup per compute unit (to compare the two forms)")
+    ap.add_argument("--no-gelu-split", action="store_true",
+                    help="leave out the workspace that lets the GeLU forward split the reduction of its "
+                         "last, partial round of tiles between two workgroups each (to compare the two forms)")
     ap.add_argument("--max-ahead", type=int, default=0,
                     help="steps the host may enqueue ahead of the device (0: no limit)")
     ap.add_argument("--enqueue", choices=("mid", "all"), default=None,
@@ -536,6 +539,8 @@ def main():
     seed = 0
 
     ctx_kw = {} if args.d2h_cus is None else {"d2h_cus": args.d2h_cus}
+    if args.no_gelu_split:
+        ctx_kw["gelu_split"] = False
     if args.h2d_cus is not None:
         ctx_kw["h2d_cus"] = args.h2d_cus
     if args.no_overlap:
@@ -613,6 +618,8 @@ def main():
         plans = (p,)
     if args.dx_per_tile:
         config["dx_form"] = "one workgroup per output block"
+    if args.no_gelu_split:
+        config["gelu_split"] = False
     sources, tier = [], None
     if args.nvme:
         if args.adam:

@@ -222,10 +222,29 @@ zi_status zi_plan_choose(const zi_problem *problem, const zi_rate_curve *curve, 
  * consecutive calls share the ring, so the copies of the next call's first
  * tiles overlap the previous call's last products.
  * workspace_dev: 256-byte aligned device memory of at least info.ring_bytes.
+ * With at least zi_gelu_split_bytes() more past info.ring_bytes rounded up to
+ * 256, the context also lets the GeLU forward (zi_tiled_linear_fwd_gelu) split
+ * the reduction of a launch's last round of tiles when that round would keep
+ * at most half of the compute units busy: each of its tiles is then taken by
+ * two workgroups, one half of K each, and the second to finish adds the
+ * other's fp32 sums and writes A and H.  The sums then group differently from
+ * an unsplit launch (exact on integer-valued inputs, within the fp32 sum's
+ * error otherwise); the forward's results do not depend on which half
+ * finishes first, so a recomputation gives the same bits.
  * The context keeps no reference to the plan.  The first context created on
  * a device also builds that device's GeLU tables (H over every 16-bit A, read
  * by the forward GeLU epilogue) on compute_stream and waits for them;
  * ZI_ERR_HIP if that fails. */
+/* Extra workspace bytes that let a context split the GeLU forward's last
+ * round of tiles (see zi_ctx_create): for each of the context's two product
+ * streams (the compute stream and the second one of zi_ctx_set_second_stream),
+ * 128 tiles of two 256 x 256 fp32 half-sums (64 MiB) and their arrival
+ * counters (512 B), which the context clears when it is created and every
+ * launch leaves cleared.  A stream runs one launch at a time, so no two
+ * launches use one set at once, and the results do not depend on whether
+ * the second stream is used. */
+uint64_t zi_gelu_split_bytes(void);
+
 zi_status zi_ctx_create(const zi_plan *plan, void *workspace_dev, uint64_t workspace_bytes,
                         void *compute_stream, void *h2d_stream, void *d2h_stream,
                         zi_ctx **out);

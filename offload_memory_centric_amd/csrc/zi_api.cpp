@@ -80,6 +80,10 @@ struct zi_ctx {
     int cus = 256;  // compute units of the device
     char *ws = nullptr;
     uint64_t ws_bytes = 0;
+    // workspace past the ring for the split GeLU forward, one set per product
+    // stream (comp, comp2); null if too small
+    float *split_part[2] = {nullptr, nullptr};
+    uint32_t *split_cnt[2] = {nullptr, nullptr};
     int d = 1, dw_slots = 0;
     uint64_t slot_bytes = 0, dw_slot_bytes = 0;
     std::vector<hipEvent_t> w_ready, w_free, dw_ready, dw_free;
@@ -348,6 +352,12 @@ zi_status run_fwd(zi_ctx *c, const zi_plan *p, const void *X, void *Y, void *H) 
         a.cols = n;
         a.red = pr.K;
         a.out_f32 = f32 ? 1 : 0;
+        if (H) {  // each product stream has its own split workspace: one launch at a time uses it
+            const int k = ks == c->comp ? 0 : 1;
+            a.split_part = c->split_part[k];
+            a.split_cnt = c->split_cnt[k];
+            a.split_cap = c->cus;
+        }
         st = gemm(c, H ? K_FWD_GELU : K_FWD, H ? GemmOp::FwdGelu : GemmOp::Fwd, pr.dtype, a, tile_flops, ks);
         if (st != ZI_OK) return st;
         HIPCHK(c, hipEventRecord(c->w_free[s], ks));
@@ -639,9 +649,28 @@ zi_status zi_ctx_create(const zi_plan *plan, void *workspace_dev, uint64_t works
     }
     c->w_free_rec.assign(c->d, 0);
     c->dw_free_rec.assign(std::max(c->dw_slots, 1), 0);
+    const uint64_t split_at = round_up(in.ring_bytes, 256);
+    if (workspace_bytes >= split_at + 2 * kSplitBytes) {
+        // the counters start at zero; each launch leaves them at zero
+        for (int k = 0; k < 2; ++k) {
+            char *at = c->ws + split_at + (uint64_t)k * kSplitBytes;
+            c->split_part[k] = reinterpret_cast<float *>(at);
+            c->split_cnt[k] = reinterpret_cast<uint32_t *>(at + kSplitPartBytes);
+            if (hipMemsetAsync(c->split_cnt[k], 0, kSplitBytes - kSplitPartBytes, c->comp) != hipSuccess) {
+                zi_ctx_destroy(c);
+                return fail(ZI_ERR_HIP, "clearing the split counters failed");
+            }
+        }
+        if (hipStreamSynchronize(c->comp) != hipSuccess) {
+            zi_ctx_destroy(c);
+            return fail(ZI_ERR_HIP, "clearing the split counters failed");
+        }
+    }
     *out = c;
     return ZI_OK;
 }
+
+uint64_t zi_gelu_split_bytes(void) { return 2 * kSplitBytes; }
 
 zi_status zi_ctx_destroy(zi_ctx *c) {
     clear_error();

@@ -40,6 +40,16 @@ struct GemmArgs {
     // output tiles in turn, the next tile's first copies and C loads issued
     // under the finished tile's stores; 0 = one workgroup per output tile.
     int32_t wg_cap;
+    // FwdGelu: fp32 half-sums and arrival counters (workspace of
+    // kSplitBytes, counters zero between launches) for splitting the
+    // reduction of the launch's last, partial round of tiles between two
+    // workgroups each, when at most half of split_cap (the workgroups that run
+    // at once) would be busy in it; null: no split.  split_tail is set by the
+    // launch: the number of such tiles.
+    float *split_part;
+    uint32_t *split_cnt;
+    int32_t split_cap;
+    int32_t split_tail;
 };
 
 // dtype: 1 = fp16, 2 = bf16.  Returns the launch status (hipGetLastError).
@@ -64,5 +74,11 @@ hipError_t launch_gelu_bwd(int dtype, const float *dH, const void *A, void *dA, 
 
 // Reduction values per pipeline step of the GEMM kernels.
 constexpr int kGemmStep = 64;
+
+// Split GeLU forward: at most kSplitTiles tiles, each two fp32 half-sums of
+// 256 x 256 (256 KiB), then one 32-bit counter per tile.
+constexpr int kSplitTiles = 128;
+constexpr uint64_t kSplitPartBytes = (uint64_t)kSplitTiles * 2 * 256 * 256 * 4;
+constexpr uint64_t kSplitBytes = kSplitPartBytes + 512;
 
 }  // namespace zi

@@ -643,6 +643,19 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
 
     int w = blockIdx.x;  // workgroup index of the current output tile
     int64_t p0, q0;      // its first output row and column
+    // GeLU forward: the last split_tail tiles of the launch are each taken by
+    // two workgroups (indices from the tile count on), one half of the
+    // reduction each; half < 0 for a whole tile.
+    constexpr bool GELU = EPI == EPI_GELU || EPI == EPI_GELU_F32A;
+    int half = -1, sj = 0;
+    if constexpr (GELU) {
+        const int first = tiles_p * tiles_q - a.split_tail;
+        if (w >= first) {
+            sj = (w - first) >> 1;
+            half = (w - first) & 1;
+            w = first + sj;
+        }
+    }
     QOp qo;
     POp po;
     // The operands of the output tile of workgroup index wi, their copy
@@ -671,6 +684,16 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
         po.init_cursor();
     };
     setup(w, lane);
+    if constexpr (GELU) {
+        static_assert(!Q_RS && !P_RS, "a split half offsets reduction-contiguous rows");
+        if (half > 0) {  // the second half of the reduction
+            const int64_t koff = (a.red >> 1) * 2;
+            qo.base += koff;
+            po.base += koff;
+            qo.init_cursor();
+            po.init_cursor();
+        }
+    }
     qo.init_reads(wq, lane);
     po.init_reads(wp, lane);
 
@@ -678,8 +701,10 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     // 2s + 1.  Copies and fragment reads are spread evenly between the
     // MFMAs, so that no wave stalls on a burst of copies while its matrix
     // unit idles.
-    const int64_t ksteps = (a.red + BK - 1) / BK;
-    const int32_t red = (int32_t)a.red;  // below 2^30 (the host checks)
+    // below 2^30 (the host checks); a split half (an even number of whole
+    // steps, which the host checks) runs half of it
+    const int32_t red = (int32_t)(half >= 0 ? a.red >> 1 : a.red);
+    const int64_t ksteps = (red + BK - 1) / BK;
     // slot of unit u (used for the first five units; the ring below rotates
     // from there)
     auto slot = [&](int u) __attribute__((always_inline)) -> char * {
@@ -986,6 +1011,36 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
         break;
     }
 
+    // A split half stores its fp32 sums, in the accumulators' own layout
+    // (each lane's 16 bytes of a block side by side: 1 KiB per wave and
+    // block), and counts itself in; the half that arrives second adds the
+    // other's sums in the epilogue and finishes the tile, and the first ends
+    // here.  Neither waits for the other.  The sum of the two halves does
+    // not depend on which arrives second.
+    const f32x4 *other = nullptr;
+    if constexpr (GELU) {
+        if (half >= 0) {
+            constexpr int kWave = QB * PB * 64;  // a wave's share of a half: f32x4 each
+            f32x4 *part = reinterpret_cast<f32x4 *>(a.split_part);
+            f32x4 *mine = part + ((int64_t)(2 * sj + half) * 4 + wave) * kWave + lane;
+#pragma unroll
+            for (int i = 0; i < QB; ++i)
+#pragma unroll
+                for (int j = 0; j < PB; ++j) mine[(i * PB + j) * 64] = acc[i][j];
+            __threadfence();  // the sums reach device scope before the count
+            // every wave's sums stored and its reads of the ring returned:
+            // the first word of LDS then carries the count to the waves
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            volatile uint32_t *word = reinterpret_cast<volatile uint32_t *>(lds);
+            if (tid == 0) *word = atomicAdd(a.split_cnt + sj, 1u);
+            __syncthreads();
+            if (*word == 0) return;  // the other half finishes this tile
+            if (tid == 0) atomicExch(a.split_cnt + sj, 0u);  // zero again for the next launch
+            __threadfence();  // the other half's sums are read after its count
+            other = part + ((int64_t)(2 * sj + (1 - half)) * 4 + wave) * kWave + lane;
+        }
+    }
+
     // Epilogue.
     const int64_t pb = p0 + wp * (16 * PB) + (lane & 15);
     const int64_t qb = q0 + wq * (16 * QB) + 4 * (lane >> 4);
@@ -1014,6 +1069,12 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
             const int64_t p = pb + j * 16;
             if (p >= a.rows) continue;
             f32x4 v = acc[i][j];
+            if constexpr (GELU) {
+                if (other) {
+                    const f32x4 o = other[(i * PB + j) * 64];
+                    v = f32x4{v[0] + o[0], v[1] + o[1], v[2] + o[2], v[3] + o[3]};
+                }
+            }
             const int64_t off = p * a.ldc + q;
             if constexpr (EPI == EPI_F32 || EPI == EPI_ACC) {
                 *reinterpret_cast<f32x4 *>(static_cast<float *>(a.C) + off) = v;
@@ -1166,12 +1227,23 @@ hipError_t run_shape(const GemmArgs &a, hipStream_t s) {
             return hipGetLastError();
         }
     }
+    // GeLU forward: when the last round of tiles would leave at least half
+    // of the compute units idle, its tiles run as two half-reductions each
+    GemmArgs b = a;
+    b.split_tail = 0;
+    if constexpr (EPI == EPI_GELU || EPI == EPI_GELU_F32A) {
+        if (a.split_part && a.split_cnt && a.split_cap > 0 && a.red % (2 * BK) == 0) {
+            const int64_t r = nt % a.split_cap;
+            if (r > 0 && 2 * r <= a.split_cap && r <= kSplitTiles) b.split_tail = (int32_t)r;
+        }
+    }
+    const dim3 g((unsigned)(nt + b.split_tail));
     if (a.red % BK == 0)
-        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, true, QB, PB, false>), dim3((unsigned)nt), dim3(kThreads),
-                           0, s, a, tiles_p, tiles_q);
+        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, true, QB, PB, false>), g, dim3(kThreads), 0, s, b,
+                           tiles_p, tiles_q);
     else
-        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, false, QB, PB, false>), dim3((unsigned)nt),
-                           dim3(kThreads), 0, s, a, tiles_p, tiles_q);
+        hipLaunchKernelGGL((gemm_kernel<T, Q_RS, P_RS, EPI, false, QB, PB, false>), g, dim3(kThreads), 0, s, b,
+                           tiles_p, tiles_q);
     return hipGetLastError();
 }
 

@@ -106,7 +106,9 @@ class Context:
     By default the context creates its own three streams, one after another, so
     that they sit on distinct hardware queues (see zi_stream_create): products,
     host-to-device copies (confined to ``h2d_cus`` compute units if nonzero),
-    and device-to-host copies confined to ``d2h_cus`` (0: unconfined).  With ``overlap`` (the default) it also
+    and device-to-host copies confined to ``d2h_cus`` (0: unconfined).  With ``gelu_split`` (the default) the
+    workspace also holds what zi_gelu_split_bytes() asks for, so that the GeLU forward may split the
+    reduction of its last, partial round of tiles.  With ``overlap`` (the default) it also
     makes a second product stream, on which forward passes whose tiles take
     few workgroup waves run every other tile's product.  The products do not run on torch's current stream: inputs
     must be complete before a call (torch.cuda.synchronize()), and outputs are
@@ -114,8 +116,13 @@ class Context:
     """
 
     def __init__(self, plan: Plan, device: str = "cuda", workspace_bytes: Optional[int] = None,
-                 streams=None, d2h_cus: int = D2H_CUS, overlap: bool = True, h2d_cus: int = H2D_CUS):
-        nbytes = int(workspace_bytes if workspace_bytes is not None else plan.info.ring_bytes)
+                 streams=None, d2h_cus: int = D2H_CUS, overlap: bool = True, h2d_cus: int = H2D_CUS,
+                 gelu_split: bool = True):
+        if workspace_bytes is None:
+            # the ring, then (gelu_split) the GeLU forward's split workspace
+            ring = int(plan.info.ring_bytes)
+            workspace_bytes = (ring + 255) // 256 * 256 + zi.zi_gelu_split_bytes() if gelu_split else ring
+        nbytes = int(workspace_bytes)
         self.handle = None
         self._own_streams = []
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)

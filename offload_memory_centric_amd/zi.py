@@ -163,6 +163,7 @@ _sigs = {
                             ctypes.c_double, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(zi_choice),
                             ctypes.POINTER(zi_choice), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     "zi_ctx_create": (_S, [_P, _P, ctypes.c_uint64, _P, _P, _P, ctypes.POINTER(_P)]),
+    "zi_gelu_split_bytes": (ctypes.c_uint64, []),
     "zi_ctx_destroy": (_S, [_P]),
     "zi_tiled_linear_fwd": (_S, [_P, _P, _P, _P]),
     "zi_tiled_linear_fwd_gelu": (_S, [_P, _P, _P, _P, _P]),
@@ -337,6 +338,10 @@ def zi_gelu_bwd(ctx, dtype: int, dH, A, dA, count: int) -> None:
 
 def zi_gelu_bwd_f32(ctx, dtype: int, dH, A, dA, count: int) -> None:
     _check(_lib.zi_gelu_bwd_f32(ctx, int(dtype), _ptr(dH), _ptr(A), _ptr(dA), int(count)))
+
+
+def zi_gelu_split_bytes() -> int:
+    return int(_lib.zi_gelu_split_bytes())
 
 
 def zi_stream_create() -> int:

@@ -273,3 +273,44 @@ def test_gelu_epilogue_every_16bit_input(dtype):
     assert inf_pos.size and np.all(np.isposinf(oracle.decode(h_bits[inf_pos], dtype)))
     ctx.close()
     plan.close()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,K,M,N", [(4096, 512, 1024, 1), (8192, 512, 4608, 2)])
+def test_split_gelu_forward_bit_exact(dtype, T, K, M, N):
+    # The GeLU forward with the split workspace: 16 x 4 = 64 tiles, all taken
+    # as two half-reductions (K = 256 each), and 32 x 9 = 288 tiles per weight
+    # tile, one full round of 256 and 32 split.  Small integers make every sum
+    # exact, so A and H equal the unsplit launch's bit for bit and A is the
+    # oracle's product rounded once; two calls in a row check that each
+    # launch leaves its arrival counters cleared for the next.  With two
+    # weight tiles and the second product stream the tiles alternate between
+    # the two streams' split workspaces.
+    say("case split GeLU forward", dtype, T, K, M, N)
+    tiling = lib()
+    tdt = inputs.torch_dtype(dtype)
+    from zi_testlib import make_linear_inputs
+    X, Wt, _ = make_linear_inputs(T, K, M, dtype, "small_int", seed=41)
+    outs = []
+    for split, overlap in ((True, False), (False, False), (True, True)):
+        plan = tiling.Plan(T, K, M, N, 2, dtype, Wt)
+        ctx = tiling.Context(plan, gelu_split=split, overlap=overlap)
+        got = []
+        for _ in range(2):
+            A = torch.empty((T, M), dtype=tdt, device="cuda")
+            H = torch.empty_like(A)
+            torch.cuda.synchronize()
+            ctx.fwd_gelu(plan, X, A, H)
+            ctx.sync()
+            got.append((host_bits(A), host_bits(H)))
+        outs.append(got)
+        ctx.close()
+        plan.close()
+    (a0, h0), (a1, h1) = outs[0]
+    assert np.array_equal(a0, a1) and np.array_equal(h0, h1), "second split launch differs from the first"
+    assert np.array_equal(a0, outs[1][0][0]), "split A differs from the unsplit launch"
+    assert np.array_equal(h0, outs[1][0][1]), "split H differs from the unsplit launch"
+    for k in range(2):
+        assert np.array_equal(a0, outs[2][k][0]) and np.array_equal(h0, outs[2][k][1]), "two product streams"
+    ref = oracle.linear_fwd(host_bits(X), host_bits(Wt), dtype)
+    assert np.array_equal(a0, oracle.encode(ref, dtype)), "A against the oracle"
