@@ -54,3 +54,17 @@ def test_split_labels_by_dispatch_order():
     assert by_key[1] == "other"
     assert [by_key[k] for k in (2, 3, 5, 7, 9, 11)] == ["k #0", "k #0", "k #1", "k #0", "k #0", "k #1"]
     assert bench.split_labels(keys, labels, {}) == labels
+
+
+def test_comparison_switches_parse(monkeypatch):
+    # the switches that select the other form of a kernel for an alternated
+    # comparison parse, and default to the built form
+    sys.path.insert(0, ROOT)
+    import bench
+
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    a = bench.parse()
+    assert not a.no_gelu_split and not a.dx_per_tile
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--no-gelu-split", "--dx-per-tile"])
+    a = bench.parse()
+    assert a.no_gelu_split and a.dx_per_tile
