@@ -644,8 +644,8 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     int w = blockIdx.x;  // workgroup index of the current output tile
     int64_t p0, q0;      // its first output row and column
     // GeLU forward: the last split_tail tiles of the launch are each taken by
-    // two workgroups (indices from the tile count on), one half of the
-    // reduction each; half < 0 for a whole tile.
+    // two workgroups, one half of the reduction each (workgroups from index
+    // tiles - split_tail on, two per tile); half < 0 for a whole tile.
     constexpr bool GELU = EPI == EPI_GELU || EPI == EPI_GELU_F32A;
     int half = -1, sj = 0;
     if constexpr (GELU) {
@@ -701,8 +701,8 @@ void gemm_kernel(GemmArgs a, int tiles_p, int tiles_q) {
     // 2s + 1.  Copies and fragment reads are spread evenly between the
     // MFMAs, so that no wave stalls on a burst of copies while its matrix
     // unit idles.
-    // below 2^30 (the host checks); a split half (an even number of whole
-    // steps, which the host checks) runs half of it
+    // below 2^30 (the host checks); a split half runs half of it, a whole
+    // number of steps (the host checks)
     const int32_t red = (int32_t)(half >= 0 ? a.red >> 1 : a.red);
     const int64_t ksteps = (red + BK - 1) / BK;
     // slot of unit u (used for the first five units; the ring below rotates
