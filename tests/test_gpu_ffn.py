@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from offload_memory_centric_amd import inputs
-from zi_testlib import TOL, assert_close, host_bits, lib, say, stored_tol, values
+from zi_testlib import TOL, assert_close, host_bits, lib, make_linear_inputs, say, stored_tol, values
 
 pytestmark = pytest.mark.gpu
 
@@ -289,7 +289,6 @@ def test_split_gelu_forward_bit_exact(dtype, T, K, M, N):
     say("case split GeLU forward", dtype, T, K, M, N)
     tiling = lib()
     tdt = inputs.torch_dtype(dtype)
-    from zi_testlib import make_linear_inputs
     X, Wt, _ = make_linear_inputs(T, K, M, dtype, "small_int", seed=41)
     outs = []
     for split, overlap in ((True, False), (False, False), (True, True)):
